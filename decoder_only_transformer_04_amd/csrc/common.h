@@ -1,0 +1,141 @@
+// Internal declarations shared by the host plan and the HIP kernels of the
+// GPT-2 training-step library (gfx950 only).
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+#include <string>
+#include <vector>
+
+#include "../../include/gpt2.h"
+
+#ifdef __HIPCC__
+#include <hip/hip_runtime.h>
+#endif
+
+namespace g2 {
+
+typedef uint16_t bf16_t;  // bf16 bit pattern in memory
+
+// --------------------------------------------------------------- layout of the flat buffers
+static const int64_t kParamAlign = 256;  // every tensor starts on a 256-element boundary
+static const int64_t kVocabPad = 128;    // wte rows reserved up to a multiple of this
+
+struct TensorDesc {
+    std::string name;
+    int layer;
+    int decay;
+    int64_t offset, rows, cols, reserved;
+};
+
+struct LayerW {
+    int64_t ln1_g, ln1_b, w_qkv, b_qkv, w_proj, b_proj, ln2_g, ln2_b, w_fc, b_fc, w_fc2, b_fc2;  // -1: absent
+};
+
+struct ParamLayout {
+    int64_t wte, wpe, lnf_g, lnf_b;
+    std::vector<LayerW> layer;
+    std::vector<TensorDesc> tensors;
+    int64_t n_flat;   // total elements incl. padding (multiple of kParamAlign)
+    int64_t n_real;   // exact parameter count
+    int64_t vocab_pad;
+};
+
+int validate_config(const gpt2_config* c);
+ParamLayout make_param_layout(const gpt2_config& c);
+
+// --------------------------------------------------------------- arena plan
+struct Region {
+    size_t off = 0, bytes = 0;
+};
+
+struct ArenaPlan {
+    int M, B, T, mode;
+    size_t act_bytes;  // 2 (bf16) or 4 (f32)
+    Region scalars;    // status word, clip coefficient, loss
+    Region wlp;        // low-precision weights (bf16 mode)
+    Region decay_tab;  // one byte per kParamAlign chunk of the flat buffers
+    Region norm_part;  // grad-norm partial sums (double)
+    // forward activations, per layer (eval mode: one slot reused)
+    std::vector<Region> x, xmid, ln1, m1, r1, qkv, att, lse, ln2, m2, r2, fch, fcg;
+    Region xL, xf, mf, rf, logits, loss_rows;
+    // backward scratch
+    Region dres, dres_act, dtmp, dF, dqkv, datt, attD, ln_part, bias_part;
+    Region enc_count, enc_start, enc_rank, enc_order, enc_distinct;
+    size_t total = 0;
+    int ln_part_rows = 0;    // partial rows of the LayerNorm parameter-gradient reduction
+    int bias_part_rows = 0;  // partial rows of the bias-gradient reduction
+    int norm_blocks = 0;
+};
+
+ArenaPlan make_arena_plan(const gpt2_config& c, const ParamLayout& pl, int B, int T, int mode);
+
+// --------------------------------------------------------------- scalars region (int32/float slots)
+enum ScalarSlot {
+    SLOT_STATUS = 0,   // uint32 sticky status bits
+    SLOT_COEF = 1,     // float clip coefficient for AdamW
+    SLOT_NORM = 2,     // float gradient norm
+    SLOT_LOSS = 3,     // float mean loss (when the caller passes no loss pointer)
+    SLOT_NDISTINCT = 4 // int32 number of distinct tokens (embedding backward)
+};
+
+// --------------------------------------------------------------- GEMM
+enum Epilogue {
+    EPI_STORE = 0,      // C(act) = alpha*acc + bias
+    EPI_GELU = 1,       // C(act) = u = acc + bias; C2(act) = gelu_tanh(u)
+    EPI_RESID = 2,      // C(f32) = R(f32) + acc + bias      (C may alias R)
+    EPI_F32 = 3,        // C(f32) = alpha*acc (+ C if accumulate)
+    EPI_GELU_BWD = 4    // C(act) = acc * gelu_tanh'(R(act))
+};
+
+struct GemmArgs {
+    int64_t M;
+    int N, K;
+    const void* A; int64_t lda; bool a_kc;  // a_kc: A(m,k) = A[m*lda+k], else A[k*lda+m]
+    const void* B; int64_t ldb; bool b_kc;  // b_kc: B(k,n) = B[n*ldb+k], else B[k*ldb+n]
+    int epi;
+    float alpha;
+    const float* bias;
+    void* C; int64_t ldc;
+    void* C2; int64_t ldc2;
+    const void* R; int64_t ldr;
+    int accumulate;
+    void* split_buf; size_t split_bytes;  // fp32 scratch for split-K partials (nullable)
+};
+
+#ifdef __HIPCC__
+// launchers (return hipError_t of the launch)
+hipError_t gemm(int dtype, const GemmArgs& a, hipStream_t s);
+
+hipError_t encoder_fwd(int dtype, const int32_t* idx, const float* wte32, const bf16_t* wte16,
+                       const float* wpe32, const bf16_t* wpe16, float* x, int M, int T, int C, int V,
+                       uint32_t* status, hipStream_t s);
+hipError_t layernorm_fwd(int dtype, const float* x, const float* g, const float* b, float eps, void* y,
+                         float* mean, float* rstd, int64_t rows, int C, hipStream_t s);
+hipError_t layernorm_bwd(int dtype, const float* dy, const float* x, const float* mean, const float* rstd,
+                         const float* g, float* dres, void* dres_act, float* part, int part_rows, int64_t rows,
+                         int C, int add, hipStream_t s);
+hipError_t colsum_finish2(const float* part, int part_rows, int ld, float* out_a, int na, float* out_b, int nb,
+                          int accumulate, hipStream_t s);
+hipError_t bias_grad(int dtype, const void* dY, int64_t rows, int N, float* part, int part_rows, float* db,
+                     int accumulate, hipStream_t s);
+hipError_t attention_fwd(int dtype, int B, int T, int C, int H, const void* qkv, void* out, float* lse,
+                         hipStream_t s);
+hipError_t attention_bwd(int dtype, int B, int T, int C, int H, const void* qkv, const void* out,
+                         const float* lse, const void* dout, void* dqkv, float* Dbuf, hipStream_t s);
+hipError_t cross_entropy(int dtype, void* logits, int64_t rows, int V, int ld, const int32_t* targets,
+                         float* loss_rows, int32_t* argmax, int write_grad, uint32_t* status, hipStream_t s);
+hipError_t mean_loss(const float* loss_rows, int64_t rows, float* out, uint32_t* status, hipStream_t s);
+hipError_t encoder_bwd(const int32_t* idx, const float* dres, float* dwte, float* dwpe, int M, int T, int C,
+                       int V, int32_t* count, int32_t* start, int32_t* rank, int32_t* order,
+                       int32_t* distinct, int32_t* ndistinct, int accumulate_wpe, hipStream_t s);
+hipError_t cast_f32_bf16(const float* src, bf16_t* dst, int64_t n, hipStream_t s);
+hipError_t fill_zero(void* p, size_t bytes, hipStream_t s);
+hipError_t grad_norm(const float* g, int64_t n, double* part, int nblocks, float clip, float* norm_out,
+                     float* coef_out, float* user_norm, uint32_t* status, hipStream_t s);
+hipError_t adamw(float* p, const float* g, float* m, float* v, bf16_t* p16, int64_t n, float lr, float b1,
+                 float b2, float eps, float decay_mul, float bc1, float bc2, const uint8_t* decay_tab,
+                 const float* coef, hipStream_t s);
+#endif
+
+}  // namespace g2

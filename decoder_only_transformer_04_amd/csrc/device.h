@@ -1,0 +1,78 @@
+// Device helpers shared by the HIP kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <cstdint>
+
+#include "common.h"
+
+namespace g2 {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+#define G2_LDS __attribute__((address_space(3)))
+
+// fp32 -> bf16 with round-to-nearest-even (NaN stays NaN)
+__device__ __forceinline__ bf16_t f2bf(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (bf16_t)((u >> 16) | 0x40u);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (bf16_t)(u >> 16);
+}
+__device__ __forceinline__ float bf2f(bf16_t h) { return __uint_as_float((uint32_t)h << 16); }
+
+// activation element access for the two storage types
+template <class T> struct Act;
+template <> struct Act<float> {
+    __device__ static float ld(const float* p, int64_t i) { return p[i]; }
+    __device__ static void st(float* p, int64_t i, float v) { p[i] = v; }
+};
+template <> struct Act<bf16_t> {
+    __device__ static float ld(const bf16_t* p, int64_t i) { return bf2f(p[i]); }
+    __device__ static void st(bf16_t* p, int64_t i, float v) { p[i] = f2bf(v); }
+};
+
+// tanh approximation of GELU and its derivative (constants sqrt(2/pi), 0.044715)
+__device__ __forceinline__ float gelu_tanh(float u) {
+    const float k0 = 0.7978845608028654f, k1 = 0.044715f;
+    float t = tanhf(k0 * (u + k1 * u * u * u));
+    return 0.5f * u * (1.0f + t);
+}
+__device__ __forceinline__ float gelu_tanh_grad(float u) {
+    const float k0 = 0.7978845608028654f, k1 = 0.044715f;
+    float t = tanhf(k0 * (u + k1 * u * u * u));
+    return 0.5f * (1.0f + t) + 0.5f * u * (1.0f - t * t) * k0 * (1.0f + 3.0f * k1 * u * u);
+}
+
+// Two gfx950 LDS transpose loads (ds_read_b64_tr_b16) 'gap' bytes apart, packed
+// into one 8 x bf16 MFMA operand. In each 16-lane group, lane j addresses row
+// j/4 and 4 consecutive 16-bit columns 4(j%4)..; lane i of the group receives
+// column i of the 4 rows. p points into LDS.
+__device__ __forceinline__ bf16x8 lds_tr_pair(const char* p, int gap) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((G2_LDS s16x4*)p);
+    s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((G2_LDS s16x4*)(p + gap));
+    typedef short s16x8 __attribute__((ext_vector_type(8)));
+    s16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    return __builtin_bit_cast(bf16x8, v);
+#else
+    (void)p; (void)gap;
+    return bf16x8{};
+#endif
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+    return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+    return v;
+}
+
+}  // namespace g2

@@ -1,0 +1,375 @@
+// Dense contractions of the training step: every Linear forward (X . W^T),
+// its input gradient (dY . W) and its weight gradient (dY^T . X).
+//
+// bf16 path: v_mfma_f32_32x32x16_bf16 on LDS-staged 64-deep K tiles, fp32
+// accumulation, 4 waves per workgroup in a 2 x 2 arrangement. Operands whose
+// contraction index is contiguous in memory ("KC") are staged as [row][64 k]
+// with a 16-byte XOR swizzle and read with 128-bit LDS loads; operands whose
+// contraction index is strided (dgrad's W, wgrad's dY and X) are staged in
+// their natural [k][row] orientation (rows padded by 32 elements) and read
+// with the gfx950 LDS transpose load ds_read_b64_tr_b16, so no operand is
+// ever transposed in memory. Fused epilogues: bias, tanh-GELU (writing both
+// pre- and post-activation), residual add into the fp32 stream, GELU
+// derivative, fp32 (accumulating) stores and split-K partials.
+//
+// fp32 path: a plain LDS-tiled FMA kernel with the same epilogues, used by the
+// fp32 mode.
+#include <algorithm>
+
+#include "device.h"
+
+namespace g2 {
+
+struct GP {
+    const void* A;
+    const void* B;
+    int64_t lda, ldb;
+    int64_t M;
+    int N, K;
+    int k_per_split;
+    float alpha;
+    const float* bias;
+    void* C;
+    int64_t ldc;
+    int64_t c_split_stride;
+    void* C2;
+    int64_t ldc2;
+    const void* R;
+    int64_t ldr;
+    int accumulate;
+};
+
+// ------------------------------------------------------------------ epilogue
+template <int EPI, class T>
+__device__ __forceinline__ void epi_apply(const GP& p, int64_t m, int n, float v) {
+    const float bias = p.bias ? p.bias[n] : 0.0f;
+    if constexpr (EPI == EPI_STORE) {
+        Act<T>::st((T*)p.C, m * p.ldc + n, p.alpha * v + bias);
+    } else if constexpr (EPI == EPI_GELU) {
+        float u = v + bias;
+        Act<T>::st((T*)p.C, m * p.ldc + n, u);
+        Act<T>::st((T*)p.C2, m * p.ldc2 + n, gelu_tanh(u));
+    } else if constexpr (EPI == EPI_RESID) {
+        float r = ((const float*)p.R)[m * p.ldr + n];
+        ((float*)p.C)[m * p.ldc + n] = r + v + bias;
+    } else if constexpr (EPI == EPI_F32) {
+        float* c = (float*)p.C + (int64_t)blockIdx.z * p.c_split_stride + m * p.ldc + n;
+        float o = p.alpha * v;
+        if (p.accumulate) o += *c;
+        *c = o;
+    } else if constexpr (EPI == EPI_GELU_BWD) {
+        float u = Act<T>::ld((const T*)p.R, m * p.ldr + n);
+        Act<T>::st((T*)p.C, m * p.ldc + n, v * gelu_tanh_grad(u));
+    }
+}
+
+// ------------------------------------------------------------------ bf16 MFMA kernel
+template <int R, bool KC>
+struct TileCfg {
+    static constexpr int BYTES = KC ? R * 128 : 64 * (R + 32) * 2;
+    static constexpr int CHUNKS = R / 32;  // 16-byte chunks per thread per 64-deep stage
+    static constexpr int PITCH = (R + 32) * 2;  // bytes per k row, transposed staging
+};
+
+// Global -> registers for one 64-deep stage. KC: tile rows r0.. (< rmax), k in
+// [k0, kmax); not KC: k rows k0.. (< kmax), contiguous rows r0.. (< rmax).
+// kmax (KC) and rmax (not KC) are multiples of 8, so a 16-byte chunk is either
+// wholly in bounds or wholly zero-filled.
+template <int R, bool KC>
+__device__ __forceinline__ void tile_gload(uint4 (&regs)[R / 32], const bf16_t* base, int64_t ld,
+                                           int64_t r0, int64_t rmax, int k0, int kmax, int tid) {
+#pragma unroll
+    for (int i = 0; i < TileCfg<R, KC>::CHUNKS; ++i) {
+        const int c = tid + 256 * i;
+        uint4 v = make_uint4(0, 0, 0, 0);
+        if constexpr (KC) {
+            const int row = c >> 3;
+            const int k = k0 + (c & 7) * 8;
+            const int64_t gr = r0 + row;
+            if (gr < rmax && k < kmax) v = *(const uint4*)(base + gr * ld + k);
+        } else {
+            constexpr int CPR = R / 8;
+            const int k = k0 + c / CPR;
+            const int64_t gr = r0 + (c % CPR) * 8;
+            if (k < kmax && gr < rmax) v = *(const uint4*)(base + (int64_t)k * ld + gr);
+        }
+        regs[i] = v;
+    }
+}
+
+template <int R, bool KC>
+__device__ __forceinline__ void tile_sstore(char* lds, const uint4 (&regs)[R / 32], int tid) {
+#pragma unroll
+    for (int i = 0; i < TileCfg<R, KC>::CHUNKS; ++i) {
+        const int c = tid + 256 * i;
+        int off;
+        if constexpr (KC) {
+            const int row = c >> 3, ch = c & 7;
+            off = row * 128 + ((ch ^ ((row >> 1) & 7)) << 4);
+        } else {
+            constexpr int CPR = R / 8;
+            off = (c / CPR) * TileCfg<R, KC>::PITCH + (c % CPR) * 16;
+        }
+        *(uint4*)(lds + off) = regs[i];
+    }
+}
+
+// MFMA operand fragment: lane l holds rows rb + (l & 31), k = 16 kk + 8 (l >> 5) + 0..7.
+template <int R, bool KC>
+__device__ __forceinline__ bf16x8 tile_frag(const char* lds, int rb, int kk, int lane) {
+    if constexpr (KC) {
+        const int row = rb + (lane & 31);
+        const int ch = kk * 2 + (lane >> 5);
+        return *(const bf16x8*)(lds + row * 128 + ((ch ^ ((row >> 1) & 7)) << 4));
+    } else {
+        // each 16-lane group reads a 4 (k) x 16 (rows) block; lane i of the group
+        // receives the 4 k-values of row i
+        const int g = lane >> 4, j = lane & 15;
+        const int k = kk * 16 + 8 * (g >> 1) + (j >> 2);
+        const int r = rb + 16 * (g & 1) + 4 * (j & 3);
+        const char* p0 = lds + k * TileCfg<R, KC>::PITCH + r * 2;
+        return lds_tr_pair(p0, 4 * TileCfg<R, KC>::PITCH);
+    }
+}
+
+template <int BM, int BN, bool AKC, bool BKC, int EPI>
+__global__ __launch_bounds__(256) void gemm_bf16_kernel(GP p) {
+    constexpr int ABYTES = TileCfg<BM, AKC>::BYTES;
+    constexpr int BBYTES = TileCfg<BN, BKC>::BYTES;
+    constexpr int STAGE = ABYTES + BBYTES;
+    constexpr int WM = BM / 2, WN = BN / 2, FM = WM / 32, FN = WN / 32;
+    __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int64_t m0 = (int64_t)blockIdx.y * BM;
+    const int n0 = blockIdx.x * BN;
+    const int kbeg = blockIdx.z * p.k_per_split;
+    const int kend = min(p.K, kbeg + p.k_per_split);
+    const int nk = (kend - kbeg + 63) / 64;
+    const bf16_t* A = (const bf16_t*)p.A;
+    const bf16_t* B = (const bf16_t*)p.B;
+
+    f32x16 acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+    uint4 ra[TileCfg<BM, AKC>::CHUNKS], rb[TileCfg<BN, BKC>::CHUNKS];
+    if (nk > 0) {
+        tile_gload<BM, AKC>(ra, A, p.lda, m0, p.M, kbeg, kend, tid);
+        tile_gload<BN, BKC>(rb, B, p.ldb, n0, p.N, kbeg, kend, tid);
+        tile_sstore<BM, AKC>(smem, ra, tid);
+        tile_sstore<BN, BKC>(smem + ABYTES, rb, tid);
+    }
+    __syncthreads();
+    for (int kt = 0; kt < nk; ++kt) {
+        char* cur = smem + (kt & 1) * STAGE;
+        const bool more = kt + 1 < nk;
+        if (more) {
+            const int kn = kbeg + (kt + 1) * 64;
+            tile_gload<BM, AKC>(ra, A, p.lda, m0, p.M, kn, kend, tid);
+            tile_gload<BN, BKC>(rb, B, p.ldb, n0, p.N, kn, kend, tid);
+        }
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            bf16x8 af[FM], bv[FN];
+#pragma unroll
+            for (int i = 0; i < FM; ++i) af[i] = tile_frag<BM, AKC>(cur, wm * WM + i * 32, kk, lane);
+#pragma unroll
+            for (int j = 0; j < FN; ++j) bv[j] = tile_frag<BN, BKC>(cur + ABYTES, wn * WN + j * 32, kk, lane);
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bv[j], acc[i][j], 0, 0, 0);
+        }
+        if (more) {
+            char* nxt = smem + ((kt + 1) & 1) * STAGE;
+            tile_sstore<BM, AKC>(nxt, ra, tid);
+            tile_sstore<BN, BKC>(nxt + ABYTES, rb, tid);
+        }
+        __syncthreads();
+    }
+    // accumulator (i, j, r) of lane l sits at row 8 (r/4) + 4 (l/32) + r%4, column l%32
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int64_t m = m0 + wm * WM + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+                const int n = n0 + wn * WN + j * 32 + (lane & 31);
+                if (m < p.M && n < p.N) epi_apply<EPI, bf16_t>(p, m, n, acc[i][j][r]);
+            }
+}
+
+// ------------------------------------------------------------------ fp32 kernel
+template <bool AKC, bool BKC, int EPI>
+__global__ __launch_bounds__(256) void gemm_f32_kernel(GP p) {
+    __shared__ float As[16][64 + 4];
+    __shared__ float Bs[16][64 + 4];
+    const int tid = threadIdx.x;
+    const int tx = tid & 15, ty = tid >> 4;
+    const int64_t m0 = (int64_t)blockIdx.y * 64;
+    const int n0 = blockIdx.x * 64;
+    const int kbeg = blockIdx.z * p.k_per_split;
+    const int kend = min(p.K, kbeg + p.k_per_split);
+    const float* A = (const float*)p.A;
+    const float* B = (const float*)p.B;
+    float acc[4][4] = {};
+    for (int k0 = kbeg; k0 < kend; k0 += 16) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int e = tid + 256 * i;
+            int mm, kk;
+            if (AKC) { mm = e >> 4; kk = e & 15; } else { kk = e >> 6; mm = e & 63; }
+            const int64_t gm = m0 + mm;
+            const int gk = k0 + kk;
+            float v = 0.0f;
+            if (gm < p.M && gk < kend) v = AKC ? A[gm * p.lda + gk] : A[(int64_t)gk * p.lda + gm];
+            As[kk][mm] = v;
+            int nn;
+            if (BKC) { nn = e >> 4; kk = e & 15; } else { kk = e >> 6; nn = e & 63; }
+            const int gn = n0 + nn;
+            const int gk2 = k0 + kk;
+            float w = 0.0f;
+            if (gn < p.N && gk2 < kend) w = BKC ? B[(int64_t)gn * p.ldb + gk2] : B[(int64_t)gk2 * p.ldb + gn];
+            Bs[kk][nn] = w;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int kk = 0; kk < 16; ++kk) {
+            float a[4], b[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) a[i] = As[kk][ty * 4 + i];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) b[j] = Bs[kk][tx * 4 + j];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(a[i], b[j], acc[i][j]);
+        }
+        __syncthreads();
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int64_t m = m0 + ty * 4 + i;
+            const int n = n0 + tx * 4 + j;
+            if (m < p.M && n < p.N) epi_apply<EPI, float>(p, m, n, acc[i][j]);
+        }
+}
+
+// ------------------------------------------------------------------ split-K reduction
+// out[i] = sum_s part[s][i] (in s order) (+ out[i] if accumulate)
+__global__ void splitk_reduce_kernel(const float* part, int splits, int64_t n, float* out, int64_t rows,
+                                     int cols, int64_t ldo, int accumulate) {
+    int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= n) return;
+    float s = 0.0f;
+    for (int k = 0; k < splits; ++k) s += part[(int64_t)k * n + i];
+    const int64_t r = i / cols;
+    const int c = (int)(i % cols);
+    float* o = out + r * ldo + c;
+    *o = accumulate ? *o + s : s;
+    (void)rows;
+}
+
+// ------------------------------------------------------------------ launchers
+template <int BM, int BN, bool AKC, bool BKC, int EPI>
+static hipError_t launch_bf16(const GP& p, int splits, hipStream_t s) {
+    dim3 grid((p.N + BN - 1) / BN, (unsigned)((p.M + BM - 1) / BM), splits);
+    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, AKC, BKC, EPI>), grid, dim3(256), 0, s, p);
+    return hipGetLastError();
+}
+
+template <bool AKC, bool BKC, int EPI>
+static hipError_t pick_tile_bf16(const GP& p, int splits, hipStream_t s) {
+    // estimated time ~ rounds of 256 workgroups x tile area / relative efficiency
+    const int64_t t256 = ((p.M + 255) / 256) * ((p.N + 255) / 256) * splits;
+    const int64_t t25612 = ((p.M + 255) / 256) * ((p.N + 127) / 128) * splits;
+    const int64_t t128 = ((p.M + 127) / 128) * ((p.N + 127) / 128) * splits;
+    const double c256 = (double)((t256 + 255) / 256) * 65536 / 1.0;
+    const double c25612 = (double)((t25612 + 255) / 256) * 32768 / 0.85;
+    const double c128 = (double)((t128 + 255) / 256) * 16384 / 0.7;
+    if (c256 <= c25612 && c256 <= c128) return launch_bf16<256, 256, AKC, BKC, EPI>(p, splits, s);
+    if (c25612 <= c128) return launch_bf16<256, 128, AKC, BKC, EPI>(p, splits, s);
+    return launch_bf16<128, 128, AKC, BKC, EPI>(p, splits, s);
+}
+
+template <bool AKC, bool BKC, int EPI>
+static hipError_t launch_f32(const GP& p, int splits, hipStream_t s) {
+    dim3 grid((p.N + 63) / 64, (unsigned)((p.M + 63) / 64), splits);
+    hipLaunchKernelGGL((gemm_f32_kernel<AKC, BKC, EPI>), grid, dim3(256), 0, s, p);
+    return hipGetLastError();
+}
+
+template <bool AKC, bool BKC, int EPI>
+static hipError_t dispatch(int dtype, const GP& p, int splits, hipStream_t s) {
+    if (dtype == GPT2_DTYPE_BF16) return pick_tile_bf16<AKC, BKC, EPI>(p, splits, s);
+    return launch_f32<AKC, BKC, EPI>(p, splits, s);
+}
+
+hipError_t gemm(int dtype, const GemmArgs& a, hipStream_t s) {
+    GP p;
+    p.A = a.A; p.B = a.B; p.lda = a.lda; p.ldb = a.ldb;
+    p.M = a.M; p.N = a.N; p.K = a.K;
+    p.k_per_split = a.K;
+    p.alpha = a.alpha; p.bias = a.bias;
+    p.C = a.C; p.ldc = a.ldc; p.c_split_stride = 0;
+    p.C2 = a.C2; p.ldc2 = a.ldc2; p.R = a.R; p.ldr = a.ldr;
+    p.accumulate = a.accumulate;
+    if (a.M <= 0 || a.N <= 0) return hipSuccess;
+    if (a.K <= 0) {
+        // empty contraction: the product is zero
+        if (a.epi != EPI_F32) return hipErrorInvalidValue;
+        p.K = 0;
+    }
+    const bool kc11 = a.a_kc && a.b_kc, kc10 = a.a_kc && !a.b_kc, kc00 = !a.a_kc && !a.b_kc;
+    if (kc11) {
+        switch (a.epi) {
+            case EPI_STORE: return dispatch<true, true, EPI_STORE>(dtype, p, 1, s);
+            case EPI_GELU: return dispatch<true, true, EPI_GELU>(dtype, p, 1, s);
+            case EPI_RESID: return dispatch<true, true, EPI_RESID>(dtype, p, 1, s);
+            case EPI_F32: return dispatch<true, true, EPI_F32>(dtype, p, 1, s);
+        }
+    } else if (kc10) {
+        switch (a.epi) {
+            case EPI_STORE: return dispatch<true, false, EPI_STORE>(dtype, p, 1, s);
+            case EPI_F32: return dispatch<true, false, EPI_F32>(dtype, p, 1, s);
+            case EPI_GELU_BWD: return dispatch<true, false, EPI_GELU_BWD>(dtype, p, 1, s);
+        }
+    } else if (kc00 && a.epi == EPI_F32) {
+        // weight gradients: contraction over all tokens; split K when the output
+        // alone would not fill the GPU, reducing the partials in fixed order
+        int splits = 1;
+        const int64_t tiles = (int64_t)((a.M + 127) / 128) * ((a.N + 127) / 128);
+        if (dtype == GPT2_DTYPE_BF16 && a.split_buf && tiles < 256 && a.K >= 1024) {
+            splits = (int)std::min<int64_t>(std::max<int64_t>(1, 512 / tiles), a.K / 512);
+            while (splits > 1 && (size_t)splits * a.M * a.N * 4 > a.split_bytes) --splits;
+        }
+        if (splits <= 1) return dispatch<false, false, EPI_F32>(dtype, p, 1, s);
+        int kps = (int)(((a.K + splits - 1) / splits + 63) / 64 * 64);
+        splits = (a.K + kps - 1) / kps;
+        GP q = p;
+        q.k_per_split = kps;
+        q.C = a.split_buf;
+        q.ldc = a.N;
+        q.c_split_stride = (int64_t)a.M * a.N;
+        q.accumulate = 0;
+        hipError_t e = dispatch<false, false, EPI_F32>(dtype, q, splits, s);
+        if (e != hipSuccess) return e;
+        const int64_t n = (int64_t)a.M * a.N;
+        hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
+                           (const float*)a.split_buf, splits, n, (float*)a.C, a.M, a.N, a.ldc, a.accumulate);
+        return hipGetLastError();
+    }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace g2

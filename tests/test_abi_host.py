@@ -1,0 +1,137 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports every
+symbol include/gpt2.h declares, and its host-only calls (sizes, layout, errors,
+LR schedule) behave as documented."""
+import ctypes as ct
+import math
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+import synthetic as syn
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def b():
+    from decoder_only_transformer_04_amd import binding
+    if not os.path.exists(binding.LIB_PATH):
+        from decoder_only_transformer_04_amd import build
+        build.build()
+    binding.lib()
+    return binding
+
+
+def cfg_of(b, m: syn.Model, dtype):
+    return b.make_config(m.vocab, m.block_size, m.n_embd, m.n_head, m.n_layer, m.mlp_hidden, m.bias,
+                         b.DTYPE_F32 if dtype == "f32" else b.DTYPE_BF16, m.ln_eps)
+
+
+def header_functions():
+    text = open(os.path.join(ROOT, "include", "gpt2.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gpt2_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_library_exports_every_header_symbol(b):
+    names = header_functions()
+    assert len(names) >= 20
+    out = subprocess.run(["nm", "-D", "--defined-only", b.LIB_PATH], capture_output=True, text=True, check=True).stdout
+    exported = set(l.split()[-1] for l in out.splitlines() if " T " in l)
+    missing = [n for n in names if n not in exported]
+    assert not missing, missing
+    assert sorted(b.EXPORTS) == names
+    for n in names:
+        assert hasattr(b.lib(), n)
+
+
+@pytest.mark.parametrize("wname", ["tiny_f32", "char_bf16", "gpt2_124m"])
+def test_param_table_matches_model_shapes(b, wname):
+    w = syn.WORKLOADS[wname]
+    cfg = cfg_of(b, w.model, w.dtype)
+    table = b.param_table(cfg)
+    assert [(d["name"], d["shape"]) for d in table] == syn.tensor_shapes(w.model)
+    assert b.num_params(cfg) == syn.n_params_exact(w.model)
+    n_flat, arena = b.query_sizes(cfg, w.batch, w.seq, b.MODE_TRAIN)
+    assert n_flat % 256 == 0 and arena > 0
+    end = 0
+    for d in table:
+        assert d["offset"] % 256 == 0
+        assert d["offset"] >= end
+        n = int(np.prod(d["shape"]))
+        assert d["reserved"] >= n
+        end = d["offset"] + d["reserved"]
+        assert d["decay"] == (1 if len(d["shape"]) == 2 else 0)
+    assert end == n_flat
+    # the embedding table reserves rows up to a multiple of 128 for the tied head
+    wte = table[0]
+    assert wte["reserved"] >= ((w.model.vocab + 127) // 128 * 128) * w.model.n_embd
+
+
+def test_exact_124m_count(b):
+    cfg = cfg_of(b, syn.GPT2_124M, "bf16")
+    assert b.num_params(cfg) == 124439808
+
+
+def test_eval_arena_is_smaller(b):
+    w = syn.WORKLOADS["gpt2_124m"]
+    cfg = cfg_of(b, w.model, "bf16")
+    _, tr = b.query_sizes(cfg, 12, 1024, b.MODE_TRAIN)
+    _, ev = b.query_sizes(cfg, 12, 1024, b.MODE_EVAL)
+    assert ev < tr / 2
+
+
+def test_invalid_configs_rejected(b):
+    base = syn.WORKLOADS["tiny_f32"].model
+    ok = cfg_of(b, base, "f32")
+    assert b.lib().gpt2_query_sizes(ct.byref(ok), 4, 64, 0, None, None) == 0
+    bad_heads = b.make_config(65, 64, 130, 4, 4, 512, 0, b.DTYPE_F32)          # C % H != 0
+    assert b.lib().gpt2_query_sizes(ct.byref(bad_heads), 4, 64, 0, None, None) == b.GPT2_EINVAL
+    assert b.lib().gpt2_num_params(ct.byref(bad_heads)) == b.GPT2_EINVAL
+    assert b.lib().gpt2_query_sizes(ct.byref(ok), 4, 65, 0, None, None) == b.GPT2_EINVAL   # T > block_size
+    assert b.lib().gpt2_query_sizes(ct.byref(ok), 0, 64, 0, None, None) == b.GPT2_EINVAL   # B < 1
+    assert b.lib().gpt2_query_sizes(ct.byref(ok), 4, 0, 0, None, None) == b.GPT2_EINVAL    # T < 1
+    assert b.lib().gpt2_query_sizes(ct.byref(ok), 4, 64, 7, None, None) == b.GPT2_EINVAL   # mode
+    bf_odd = b.make_config(65, 64, 132, 4, 4, 512, 0, b.DTYPE_BF16)           # bf16 needs C % 8 == 0
+    assert b.lib().gpt2_query_sizes(ct.byref(bf_odd), 4, 64, 0, None, None) == b.GPT2_EINVAL
+    big_head = b.make_config(65, 64, 512, 2, 1, 512, 0, b.DTYPE_F32)          # head size 256 > 128
+    assert b.lib().gpt2_query_sizes(ct.byref(big_head), 1, 64, 0, None, None) == b.GPT2_EINVAL
+    neg_eps = b.make_config(65, 64, 128, 4, 4, 512, 0, b.DTYPE_F32, -1.0)
+    assert b.lib().gpt2_query_sizes(ct.byref(neg_eps), 1, 64, 0, None, None) == b.GPT2_EINVAL
+    # shorter sequences than block_size are valid
+    assert b.lib().gpt2_query_sizes(ct.byref(ok), 3, 37, 0, None, None) == 0
+
+
+def test_init_rejects_null_and_small_arena(b):
+    cfg = cfg_of(b, syn.WORKLOADS["tiny_f32"].model, "f32")
+    ctx = ct.c_void_p()
+    assert b.lib().gpt2_init(ct.byref(ctx), ct.byref(cfg), None, 4, 64, 0, None) == b.GPT2_EINVAL
+    n_flat, need = b.query_sizes(cfg, 4, 64, b.MODE_TRAIN)
+    # host memory stands in for device pointers: init must refuse before touching them
+    bufs = b.Buffers(1 << 20, 1 << 20, 1 << 20, 1 << 20, 1 << 20, need - 1)
+    assert b.lib().gpt2_init(ct.byref(ctx), ct.byref(cfg), ct.byref(bufs), 4, 64, 0, None) == b.GPT2_ENOSPC
+    bufs = b.Buffers(1 << 20, None, 1 << 20, 1 << 20, 1 << 20, need)
+    assert b.lib().gpt2_init(ct.byref(ctx), ct.byref(cfg), ct.byref(bufs), 4, 64, 0, None) == b.GPT2_EINVAL
+    assert b.lib().gpt2_forward(None, None, None, None, None) == b.GPT2_EINVAL
+    assert b.lib().gpt2_backward(None, 1.0, 1) == b.GPT2_EINVAL
+
+
+def test_strerror(b):
+    for c in (0, -1, -2, -3, -4, -5):
+        assert len(b.strerror(c)) >= 2
+    assert "unknown" in b.strerror(-99)
+
+
+def test_lr_schedule_values(b):
+    # closed-form values of warmup 2000 then cosine from 6e-4 to 6e-5 over 600k iterations
+    assert b.lr_cosine(0) == pytest.approx(3e-7, rel=1e-12)
+    assert b.lr_cosine(1999) == pytest.approx(6e-4, rel=1e-12)
+    assert b.lr_cosine(2000) == pytest.approx(6e-4, rel=1e-12)
+    assert b.lr_cosine(301000) == pytest.approx(3.3e-4, rel=1e-12)
+    assert b.lr_cosine(600000) == pytest.approx(6e-5, rel=1e-12)
+    assert b.lr_cosine(700000) == pytest.approx(6e-5, rel=1e-12)
+    mid = 2000 + 598000 // 4  # a quarter of the way through the decay: cos(pi/4)
+    assert b.lr_cosine(mid) == pytest.approx(6e-5 + 0.5 * (1 + math.cos(math.pi / 4)) * 5.4e-4, rel=1e-12)
