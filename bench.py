@@ -1,0 +1,228 @@
+#!/usr/bin/env python3
+"""Benchmark of one GPT-2 training step on one MI355X.
+
+A step is the whole hot path: forward, backward and AdamW over one micro-batch
+of the 124M model (12 x 1024 tokens, bf16 operands, fp32 master weights and
+optimizer state), inputs resident in HBM before the timed region. Prints one
+JSON line with training tokens/s, MFU against the bf16 dense MFMA peak, the
+roofline of the step's dominant kernel (timed live with HIP events over the
+timed region) and the CPU oracle timed on the host cores as a baseline.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import synthetic as syn  # noqa: E402
+
+METRIC = "GPT-2 124M train tokens/sec (fwd+bwd+AdamW, T=1024) + bf16 MFU % on 1 GPU"
+PEAK_BF16 = 2.5e15     # MI355X dense bf16 MFMA, FLOP/s
+PEAK_HBM = 8.0e12      # MI355X HBM3E, bytes/s
+
+
+def flops_per_token(m: syn.Model, T: int) -> int:
+    """6 N per trained token plus causal attention (6 L C (T+1)): the score and
+    value products, forward and backward, over the j <= i half of each row."""
+    return 6 * syn.n_params_exact(m) + 6 * m.n_layer * m.n_embd * (T + 1)
+
+
+def kernel_work(label: str, w: syn.Workload):
+    """(bound, algorithmic work per step for this label, unit) for the roofline."""
+    m = w.model
+    M, C, F, V, L, H = w.batch * w.seq, m.n_embd, m.mlp_hidden, m.vocab, m.n_layer, m.n_head
+    T, B = w.seq, w.batch
+    gemm = {"qkv": 2 * M * 3 * C * C, "proj": 2 * M * C * C, "fc": 2 * M * F * C, "fc2": 2 * M * C * F,
+            "head": 2 * M * V * C}
+    if label.startswith("gemm."):
+        _, kind, which = label.split(".")
+        per = gemm[which]
+        return "mfma", per * (1 if which == "head" else L), "TFLOP/s"
+    causal = B * H * (T * (T + 1) // 2) * (C // H) * 2   # one causal T x T x d product
+    if label == "attn.fwd":
+        return "mfma", 2 * causal * L, "TFLOP/s"
+    if label == "attn.bwd":
+        return "mfma", 4 * causal * L, "TFLOP/s"
+    Vp = (V + 127) // 128 * 128
+    n = syn.n_params_exact(m)
+    bytes_ = {
+        "ce": M * Vp * 2 * 2 + M * 8,                 # read logits, write dlogits (bf16)
+        "adamw": n * (4 * 4 + 3 * 4 + 2),             # read p, g, m, v; write p, m, v, bf16 p
+        "gradnorm": n * 4,
+        "ln.fwd": (2 * L + 1) * M * C * (4 + 2),      # fp32 in, bf16 out
+        "ln.bwd": (2 * L + 1) * M * C * (4 * 4 + 2),  # dy, x, dres in/out (fp32), bf16 copy
+        "embed.fwd": M * C * 4 * 3,
+        "embed.bwd": M * C * 4 * 2,
+    }
+    if label in bytes_:
+        return "hbm", bytes_[label], "GB/s"
+    return None, None, None
+
+
+LABELS = ["gemm.fwd.qkv", "gemm.fwd.proj", "gemm.fwd.fc", "gemm.fwd.fc2", "gemm.fwd.head",
+          "gemm.dgrad.head", "gemm.wgrad.head", "gemm.dgrad.fc2", "gemm.wgrad.fc2", "gemm.dgrad.fc",
+          "gemm.wgrad.fc", "gemm.dgrad.proj", "gemm.wgrad.proj", "gemm.dgrad.qkv", "gemm.wgrad.qkv",
+          "attn.fwd", "attn.bwd", "ln.fwd", "ln.bwd", "ce", "loss", "colsum", "bias", "embed.fwd", "embed.bwd",
+          "gradnorm", "adamw"]
+
+
+def cpu_baseline(w: syn.Workload, named: dict, seq: int):
+    """The oracle (fp32 instantiation, as it stands) on one sequence of `seq`
+    tokens, forward + backward, plus one AdamW pass over every parameter;
+    extrapolated to the full batch (B*T/seq sequences) to give tokens/s."""
+    import numpy as np
+    import oracle as o
+    if not os.path.exists(o.LIB_PATH):
+        from oracle import build
+        build.build()
+    m = w.model
+    cfg = o.make_cfg(m.vocab, m.block_size, m.n_embd, m.n_head, m.n_layer, m.mlp_hidden, m.bias, m.ln_eps)
+    p = o.pack(cfg, named, np.float32)
+    g = np.zeros_like(p)
+    x, y = syn.batch(w, step=0, B=1, T=seq)
+    t0 = time.perf_counter()
+    o.step(cfg, 1, seq, p, x, y, g)
+    t1 = time.perf_counter()
+    mm = np.zeros_like(p)
+    vv = np.zeros_like(p)
+    o.adamw(p, g, mm, vv, w.lr, w.beta1, w.beta2, w.eps, w.weight_decay, 1)
+    t2 = time.perf_counter()
+    per_step = (t1 - t0) * (w.batch * w.seq / seq) + (t2 - t1)
+    return {"value": round(w.batch * w.seq / per_step, 3), "unit": "tokens/s", "cores": o.max_threads(),
+            "kind": "oracle",
+            "sample": f"fp32 oracle, 1 sequence x {seq} tokens fwd+bwd ({t1 - t0:.2f} s) extrapolated x"
+                      f"{w.batch * w.seq // seq} to the {w.batch}x{w.seq} batch, plus one AdamW pass over all "
+                      f"{syn.n_params_exact(m)} parameters ({t2 - t1:.2f} s)"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="gpt2_124m", choices=["gpt2_124m"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seq", type=int, default=1024, help="tokens in the oracle's timed sample")
+    ap.add_argument("--no-breakdown", action="store_true", help="skip the per-kernel-class timing pass")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
+              "this build has no multi-GPU path", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from decoder_only_transformer_04_amd import binding as b
+
+    w = syn.WORKLOADS[args.workload]
+    m = w.model
+    cfg = b.make_config(m.vocab, m.block_size, m.n_embd, m.n_head, m.n_layer, m.mlp_hidden, m.bias, b.DTYPE_BF16,
+                        m.ln_eps)
+    named = syn.init_params(m)
+    g = b.Model(cfg, w.batch, w.seq, b.MODE_TRAIN)
+    g.load_named(named)
+    g.init()
+    nb = args.warmup + args.steps + len(LABELS)
+    xs, ys = [], []
+    for k in range(nb):
+        x, y = syn.batch(w, step=k)
+        xs.append(torch.from_numpy(x.reshape(-1)).cuda())
+        ys.append(torch.from_numpy(y.reshape(-1)).cuda())
+    torch.cuda.synchronize()
+    t = 0
+
+    def step(k):
+        nonlocal t
+        t += 1
+        g.forward(xs[k], ys[k])
+        g.backward(1.0, True)
+        g.adamw_step(w.lr, w.beta1, w.beta2, w.eps, w.weight_decay, t)
+
+    for k in range(args.warmup):
+        step(k)
+    torch.cuda.synchronize()
+
+    # per-kernel-class time of one step each (untimed), to name the dominant kernel
+    breakdown = {}
+    if not args.no_breakdown:
+        for i, lab in enumerate(LABELS):
+            g.timing_begin(lab)
+            step(args.warmup + i)
+            ms, n = g.timing_end()
+            breakdown[lab] = round(ms, 4)
+    dominant = max((l for l in breakdown if kernel_work(l, w)[0]), key=lambda l: breakdown[l]) \
+        if breakdown else "gemm.fwd.head"
+
+    # timed region: exactly K steps, the dominant kernel's launches bracketed by events
+    base = args.warmup + len(LABELS)
+    torch.cuda.synchronize()
+    g.timing_begin(dominant)
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record()
+    for k in range(args.steps):
+        step(base + k)
+    ev1.record()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    dom_ms, dom_n = g.timing_end()
+    status = g.sync_status()
+    loss = float(g.loss.item())
+    elapsed = max(ev0.elapsed_time(ev1) / 1e3, 1e-9)
+    wall = t1 - t0
+    tokens = w.batch * w.seq * args.steps
+    value = tokens / elapsed
+    fpt = flops_per_token(m, w.seq)
+    mfu = value * fpt / PEAK_BF16
+    bound, work, unit = kernel_work(dominant, w)
+    launches_per_step = max(1, dom_n // max(args.steps, 1))
+    avg_launch_s = dom_ms / 1e3 / max(dom_n, 1)
+    per_launch = work / launches_per_step
+    if bound == "mfma":
+        achieved = per_launch / avg_launch_s / 1e12
+        peak = PEAK_BF16 / 1e12
+    else:
+        achieved = per_launch / avg_launch_s / 1e9
+        peak = PEAK_HBM / 1e9
+    roofline = {"bound": bound, "kernel": dominant, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
+                "frac": round(achieved / peak, 4), "traffic": None,
+                "avg_launch_ms": round(avg_launch_s * 1e3, 4), "launches_timed": dom_n,
+                "work_per_launch": per_launch}
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(elapsed * 1e3 / args.steps, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (Zipf s=1.05 token ids, N(0,0.02) init, seeds 1234/5678)",
+        "config": {"workload": "gpt2_124m: V50257 T1024 C768 H12 L12 F3072, biases, tied head; "
+                               "micro-batch 12 x 1024, one fwd+bwd+AdamW per step",
+                   "global_batch": w.batch, "seq_len": w.seq, "parallelism": "none (1 GPU)"},
+        "mfu": round(mfu, 4),
+        "flops_per_token": fpt,
+        "wall_s": round(wall, 3),
+        "final_loss": round(loss, 5),
+        "status": status,
+        "roofline": roofline,
+        "breakdown_ms_per_step": breakdown,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, named, args.cpu_seq)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

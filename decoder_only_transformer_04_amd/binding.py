@@ -24,7 +24,7 @@ EXPORTS = [
     "gpt2_refresh_weights", "gpt2_forward", "gpt2_backward", "gpt2_adamw_step", "gpt2_sync_status",
     "gpt2_clear_status", "gpt2_arena_tensor", "gpt2_destroy", "gpt2_op_linear_fwd", "gpt2_op_linear_bwd",
     "gpt2_op_layernorm_fwd", "gpt2_op_layernorm_bwd", "gpt2_op_attention_fwd", "gpt2_op_attention_bwd",
-    "gpt2_op_cross_entropy",
+    "gpt2_op_cross_entropy", "gpt2_timing_begin", "gpt2_timing_end",
 ]
 
 
@@ -78,6 +78,8 @@ def lib():
             "gpt2_arena_tensor": (ct.c_int, [P, ct.c_char_p, i32, sz, ct.POINTER(i32), ct.POINTER(i64),
                                              ct.POINTER(i64)]),
             "gpt2_destroy": (None, [P]),
+            "gpt2_timing_begin": (ct.c_int, [P, ct.c_char_p]),
+            "gpt2_timing_end": (ct.c_int, [P, ct.POINTER(f32), ct.POINTER(i32)]),
             "gpt2_op_linear_fwd": (ct.c_int, [i32, i64, i32, i32, P, P, P, P, P]),
             "gpt2_op_linear_bwd": (ct.c_int, [i32, i64, i32, i32, P, P, P, P, P, P, i32, P]),
             "gpt2_op_layernorm_fwd": (ct.c_int, [i32, i64, i32, P, P, P, f32, P, P, P, P]),
@@ -227,6 +229,16 @@ class Model:
         if rc not in (GPT2_OK, GPT2_EDEVICE):
             raise GPT2Error(rc, "gpt2_sync_status")
         return int(bits.value)
+
+    def timing_begin(self, prefix: str) -> None:
+        check(lib().gpt2_timing_begin(self.ctx, prefix.encode()), "gpt2_timing_begin")
+
+    def timing_end(self):
+        """(total milliseconds, launches) of the launches timed since timing_begin."""
+        ms = ct.c_float()
+        n = ct.c_int32()
+        check(lib().gpt2_timing_end(self.ctx, ct.byref(ms), ct.byref(n)), "gpt2_timing_end")
+        return float(ms.value), int(n.value)
 
     def clear_status(self) -> None:
         check(lib().gpt2_clear_status(self.ctx), "gpt2_clear_status")

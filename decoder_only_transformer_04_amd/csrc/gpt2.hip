@@ -8,6 +8,9 @@
 #include <cstdio>
 #include <cstring>
 #include <new>
+#include <string>
+#include <utility>
+#include <vector>
 
 #include "common.h"
 
@@ -24,6 +27,12 @@ struct gpt2_ctx {
     bool have_idx;  // token ids of the last forward saved for the embedding backward
     Region idx_save;
     Region split;   // split-K partials of the weight-gradient GEMMs
+    // optional per-launch timing (gpt2_timing_begin/end)
+    bool timing = false;
+    std::string timing_prefix;
+    std::vector<hipEvent_t> ev_pool;
+    size_t ev_used = 0;
+    std::vector<std::pair<hipEvent_t, hipEvent_t>> ev_pairs;
 };
 
 namespace {
@@ -58,6 +67,36 @@ size_t extra_bytes(const gpt2_config& c, const ArenaPlan& ap, size_t* idx_off, s
 
 template <class P>
 P* at(gpt2_ctx* x, const Region& r) { return (P*)(x->arena + r.off); }
+
+// a label is timed when it equals the prefix or extends it by a '.'-separated part
+bool timing_on(gpt2_ctx* x, const char* label) {
+    if (!x->timing) return false;
+    const size_t n = x->timing_prefix.size();
+    if (n == 0) return true;
+    return std::strncmp(label, x->timing_prefix.c_str(), n) == 0 && (label[n] == '\0' || label[n] == '.');
+}
+hipEvent_t ev_get(gpt2_ctx* x) {
+    if (x->ev_used == x->ev_pool.size()) {
+        hipEvent_t e = nullptr;
+        if (hipEventCreate(&e) != hipSuccess) return nullptr;
+        x->ev_pool.push_back(e);
+    }
+    return x->ev_pool[x->ev_used++];
+}
+
+// launch `expr` (a hipError_t expression); bracket it with events when timed
+#define G2_T(label, expr)                                                       \
+    do {                                                                        \
+        const bool t_ = timing_on(x, label);                                    \
+        hipEvent_t a_ = t_ ? ev_get(x) : nullptr;                               \
+        if (a_) G2_TRY(hipEventRecord(a_, x->stream));                          \
+        G2_TRY(expr);                                                           \
+        hipEvent_t b_ = t_ ? ev_get(x) : nullptr;                               \
+        if (a_ && b_) {                                                         \
+            G2_TRY(hipEventRecord(b_, x->stream));                              \
+            x->ev_pairs.push_back({a_, b_});                                    \
+        }                                                                       \
+    } while (0)
 
 uint32_t* status_ptr(gpt2_ctx* x) { return at<uint32_t>(x, x->ap.scalars) + SLOT_STATUS; }
 
@@ -234,7 +273,11 @@ int gpt2_refresh_weights(gpt2_ctx* x) {
     return GPT2_OK;
 }
 
-void gpt2_destroy(gpt2_ctx* x) { delete x; }
+void gpt2_destroy(gpt2_ctx* x) {
+    if (!x) return;
+    for (hipEvent_t e : x->ev_pool) (void)hipEventDestroy(e);
+    delete x;
+}
 
 int gpt2_forward(gpt2_ctx* x, const int32_t* d_idx, const int32_t* d_targets, float* d_loss, int32_t* d_argmax) {
     if (!x || !d_idx) return GPT2_EINVAL;
@@ -252,7 +295,7 @@ int gpt2_forward(gpt2_ctx* x, const int32_t* d_idx, const int32_t* d_targets, fl
         G2_TRY(hipMemcpyAsync(at<int32_t>(x, x->idx_save), d_idx, (size_t)M * 4, hipMemcpyDeviceToDevice, s));
         x->have_idx = true;
     }
-    G2_TRY(encoder_fwd(dt, d_idx, pf(x, x->pl.wte), nullptr, pf(x, x->pl.wpe), nullptr, at<float>(x, ap.x[0]), M, T, C,
+    G2_T("embed.fwd", encoder_fwd(dt, d_idx, pf(x, x->pl.wte), nullptr, pf(x, x->pl.wpe), nullptr, at<float>(x, ap.x[0]), M, T, C,
                        c.vocab, status, s));
     for (int l = 0; l < c.n_layer; ++l) {
         const LayerW& w = x->pl.layer[l];
@@ -260,33 +303,33 @@ int gpt2_forward(gpt2_ctx* x, const int32_t* d_idx, const int32_t* d_targets, fl
         float* xin = at<float>(x, ap.x[sl]);
         float* xmid = at<float>(x, ap.xmid[sl]);
         float* xout = (l == c.n_layer - 1) ? at<float>(x, ap.xL) : at<float>(x, ap.x[train ? l + 1 : 0]);
-        G2_TRY(layernorm_fwd(dt, xin, pf(x, w.ln1_g), pf(x, w.ln1_b), c.ln_eps, at<char>(x, ap.ln1[sl]),
+        G2_T("ln.fwd", layernorm_fwd(dt, xin, pf(x, w.ln1_g), pf(x, w.ln1_b), c.ln_eps, at<char>(x, ap.ln1[sl]),
                              at<float>(x, ap.m1[sl]), at<float>(x, ap.r1[sl]), M, C, s));
-        G2_TRY(linear_fwd(x, EPI_STORE, M, 3 * C, C, at<char>(x, ap.ln1[sl]), wptr(x, w.w_qkv), pf(x, w.b_qkv),
+        G2_T("gemm.fwd.qkv", linear_fwd(x, EPI_STORE, M, 3 * C, C, at<char>(x, ap.ln1[sl]), wptr(x, w.w_qkv), pf(x, w.b_qkv),
                           at<char>(x, ap.qkv[sl]), nullptr, nullptr));
-        G2_TRY(attention_fwd(dt, ap.B, T, C, H, at<char>(x, ap.qkv[sl]), at<char>(x, ap.att[sl]),
+        G2_T("attn.fwd", attention_fwd(dt, ap.B, T, C, H, at<char>(x, ap.qkv[sl]), at<char>(x, ap.att[sl]),
                              at<float>(x, ap.lse[sl]), s));
-        G2_TRY(linear_fwd(x, EPI_RESID, M, C, C, at<char>(x, ap.att[sl]), wptr(x, w.w_proj), pf(x, w.b_proj), xmid,
+        G2_T("gemm.fwd.proj", linear_fwd(x, EPI_RESID, M, C, C, at<char>(x, ap.att[sl]), wptr(x, w.w_proj), pf(x, w.b_proj), xmid,
                           nullptr, xin));
-        G2_TRY(layernorm_fwd(dt, xmid, pf(x, w.ln2_g), pf(x, w.ln2_b), c.ln_eps, at<char>(x, ap.ln2[sl]),
+        G2_T("ln.fwd", layernorm_fwd(dt, xmid, pf(x, w.ln2_g), pf(x, w.ln2_b), c.ln_eps, at<char>(x, ap.ln2[sl]),
                              at<float>(x, ap.m2[sl]), at<float>(x, ap.r2[sl]), M, C, s));
-        G2_TRY(linear_fwd(x, EPI_GELU, M, F, C, at<char>(x, ap.ln2[sl]), wptr(x, w.w_fc), pf(x, w.b_fc),
+        G2_T("gemm.fwd.fc", linear_fwd(x, EPI_GELU, M, F, C, at<char>(x, ap.ln2[sl]), wptr(x, w.w_fc), pf(x, w.b_fc),
                           at<char>(x, ap.fch[sl]), at<char>(x, ap.fcg[sl]), nullptr));
-        G2_TRY(linear_fwd(x, EPI_RESID, M, C, F, at<char>(x, ap.fcg[sl]), wptr(x, w.w_fc2), pf(x, w.b_fc2), xout,
+        G2_T("gemm.fwd.fc2", linear_fwd(x, EPI_RESID, M, C, F, at<char>(x, ap.fcg[sl]), wptr(x, w.w_fc2), pf(x, w.b_fc2), xout,
                           nullptr, xmid));
     }
-    G2_TRY(layernorm_fwd(dt, at<float>(x, ap.xL), pf(x, x->pl.lnf_g), pf(x, x->pl.lnf_b), c.ln_eps,
+    G2_T("ln.fwd", layernorm_fwd(dt, at<float>(x, ap.xL), pf(x, x->pl.lnf_g), pf(x, x->pl.lnf_b), c.ln_eps,
                          at<char>(x, ap.xf), at<float>(x, ap.mf), at<float>(x, ap.rf), M, C, s));
     // tied head over the padded vocabulary (padded rows of wte are zero)
-    G2_TRY(linear_fwd(x, EPI_STORE, M, Vp, C, at<char>(x, ap.xf), wptr(x, x->pl.wte), nullptr, at<char>(x, ap.logits),
+    G2_T("gemm.fwd.head", linear_fwd(x, EPI_STORE, M, Vp, C, at<char>(x, ap.xf), wptr(x, x->pl.wte), nullptr, at<char>(x, ap.logits),
                       nullptr, nullptr));
     if (d_targets || d_argmax) {
         const bool grad = train && d_targets;
-        G2_TRY(cross_entropy(dt, at<char>(x, ap.logits), M, c.vocab, Vp, d_targets,
+        G2_T("ce", cross_entropy(dt, at<char>(x, ap.logits), M, c.vocab, Vp, d_targets,
                              d_targets ? at<float>(x, ap.loss_rows) : nullptr, d_argmax, grad ? 1 : 0, status, s));
         if (d_targets) {
             float* lp = d_loss ? d_loss : at<float>(x, ap.scalars) + SLOT_LOSS;
-            G2_TRY(mean_loss(at<float>(x, ap.loss_rows), M, lp, status, s));
+            G2_T("loss", mean_loss(at<float>(x, ap.loss_rows), M, lp, status, s));
         }
         x->have_dz = grad;
     }
@@ -316,46 +359,46 @@ int gpt2_backward(gpt2_ctx* x, float loss_scale, int32_t zero_grads) {
     const ParamLayout& pl = x->pl;
 
     // head: dxf = alpha dz . wte ; dwte (=|+=) alpha dz^T . xf
-    G2_TRY(linear_dgrad(dt, s, EPI_F32, M, Vp, C, at<char>(x, ap.logits), Vp, wptr(x, pl.wte), dtmp, nullptr, alpha));
-    G2_TRY(linear_wgrad(dt, s, M, Vp, C, at<char>(x, ap.logits), Vp, at<char>(x, ap.xf), gf(x, pl.wte), acc, alpha, sb,
+    G2_T("gemm.dgrad.head", linear_dgrad(dt, s, EPI_F32, M, Vp, C, at<char>(x, ap.logits), Vp, wptr(x, pl.wte), dtmp, nullptr, alpha));
+    G2_T("gemm.wgrad.head", linear_wgrad(dt, s, M, Vp, C, at<char>(x, ap.logits), Vp, at<char>(x, ap.xf), gf(x, pl.wte), acc, alpha, sb,
                         sbytes));
-    G2_TRY(layernorm_bwd(dt, dtmp, at<float>(x, ap.xL), at<float>(x, ap.mf), at<float>(x, ap.rf), pf(x, pl.lnf_g),
+    G2_T("ln.bwd", layernorm_bwd(dt, dtmp, at<float>(x, ap.xL), at<float>(x, ap.mf), at<float>(x, ap.rf), pf(x, pl.lnf_g),
                          dres, bf ? dres_act : nullptr, part, ap.ln_part_rows, M, C, 0, s));
-    G2_TRY(colsum_finish2(part, (M + 63) / 64, 2 * C, gf(x, pl.lnf_g), C, gf(x, pl.lnf_b), C, acc, s));
+    G2_T("colsum", colsum_finish2(part, (M + 63) / 64, 2 * C, gf(x, pl.lnf_g), C, gf(x, pl.lnf_b), C, acc, s));
     for (int l = c.n_layer - 1; l >= 0; --l) {
         const LayerW& w = pl.layer[l];
         // x_out = x_mid + fc2(gelu(fc(ln2(x_mid))))
-        G2_TRY(linear_dgrad(dt, s, EPI_GELU_BWD, M, C, F, dres_act, C, wptr(x, w.w_fc2), at<char>(x, ap.dF),
+        G2_T("gemm.dgrad.fc2", linear_dgrad(dt, s, EPI_GELU_BWD, M, C, F, dres_act, C, wptr(x, w.w_fc2), at<char>(x, ap.dF),
                             at<char>(x, ap.fch[l]), 1.0f));
-        G2_TRY(linear_wgrad(dt, s, M, C, F, dres_act, C, at<char>(x, ap.fcg[l]), gf(x, w.w_fc2), acc, 1.0f, sb, sbytes));
-        if (w.b_fc2 >= 0) G2_TRY(bias_grad(dt, dres_act, M, C, bpart, ap.bias_part_rows, gf(x, w.b_fc2), acc, s));
-        G2_TRY(linear_dgrad(dt, s, EPI_F32, M, F, C, at<char>(x, ap.dF), F, wptr(x, w.w_fc), dtmp, nullptr, 1.0f));
-        G2_TRY(linear_wgrad(dt, s, M, F, C, at<char>(x, ap.dF), F, at<char>(x, ap.ln2[l]), gf(x, w.w_fc), acc, 1.0f, sb,
+        G2_T("gemm.wgrad.fc2", linear_wgrad(dt, s, M, C, F, dres_act, C, at<char>(x, ap.fcg[l]), gf(x, w.w_fc2), acc, 1.0f, sb, sbytes));
+        if (w.b_fc2 >= 0) G2_T("bias", bias_grad(dt, dres_act, M, C, bpart, ap.bias_part_rows, gf(x, w.b_fc2), acc, s));
+        G2_T("gemm.dgrad.fc", linear_dgrad(dt, s, EPI_F32, M, F, C, at<char>(x, ap.dF), F, wptr(x, w.w_fc), dtmp, nullptr, 1.0f));
+        G2_T("gemm.wgrad.fc", linear_wgrad(dt, s, M, F, C, at<char>(x, ap.dF), F, at<char>(x, ap.ln2[l]), gf(x, w.w_fc), acc, 1.0f, sb,
                             sbytes));
-        if (w.b_fc >= 0) G2_TRY(bias_grad(dt, at<char>(x, ap.dF), M, F, bpart, ap.bias_part_rows, gf(x, w.b_fc), acc, s));
-        G2_TRY(layernorm_bwd(dt, dtmp, at<float>(x, ap.xmid[l]), at<float>(x, ap.m2[l]), at<float>(x, ap.r2[l]),
+        if (w.b_fc >= 0) G2_T("bias", bias_grad(dt, at<char>(x, ap.dF), M, F, bpart, ap.bias_part_rows, gf(x, w.b_fc), acc, s));
+        G2_T("ln.bwd", layernorm_bwd(dt, dtmp, at<float>(x, ap.xmid[l]), at<float>(x, ap.m2[l]), at<float>(x, ap.r2[l]),
                              pf(x, w.ln2_g), dres, bf ? dres_act : nullptr, part, ap.ln_part_rows, M, C, 1, s));
-        G2_TRY(colsum_finish2(part, (M + 63) / 64, 2 * C, gf(x, w.ln2_g), C, gf(x, w.ln2_b), C, acc, s));
+        G2_T("colsum", colsum_finish2(part, (M + 63) / 64, 2 * C, gf(x, w.ln2_g), C, gf(x, w.ln2_b), C, acc, s));
         // x_mid = x_in + proj(attn(ln1(x_in)))
-        G2_TRY(linear_dgrad(dt, s, EPI_STORE, M, C, C, dres_act, C, wptr(x, w.w_proj), at<char>(x, ap.datt), nullptr,
+        G2_T("gemm.dgrad.proj", linear_dgrad(dt, s, EPI_STORE, M, C, C, dres_act, C, wptr(x, w.w_proj), at<char>(x, ap.datt), nullptr,
                             1.0f));
-        G2_TRY(linear_wgrad(dt, s, M, C, C, dres_act, C, at<char>(x, ap.att[l]), gf(x, w.w_proj), acc, 1.0f, sb,
+        G2_T("gemm.wgrad.proj", linear_wgrad(dt, s, M, C, C, dres_act, C, at<char>(x, ap.att[l]), gf(x, w.w_proj), acc, 1.0f, sb,
                             sbytes));
-        if (w.b_proj >= 0) G2_TRY(bias_grad(dt, dres_act, M, C, bpart, ap.bias_part_rows, gf(x, w.b_proj), acc, s));
-        G2_TRY(attention_bwd(dt, ap.B, T, C, H, at<char>(x, ap.qkv[l]), at<char>(x, ap.att[l]), at<float>(x, ap.lse[l]),
+        if (w.b_proj >= 0) G2_T("bias", bias_grad(dt, dres_act, M, C, bpart, ap.bias_part_rows, gf(x, w.b_proj), acc, s));
+        G2_T("attn.bwd", attention_bwd(dt, ap.B, T, C, H, at<char>(x, ap.qkv[l]), at<char>(x, ap.att[l]), at<float>(x, ap.lse[l]),
                              at<char>(x, ap.datt), at<char>(x, ap.dqkv), at<float>(x, ap.attD), s));
-        G2_TRY(linear_dgrad(dt, s, EPI_F32, M, 3 * C, C, at<char>(x, ap.dqkv), 3 * C, wptr(x, w.w_qkv), dtmp, nullptr,
+        G2_T("gemm.dgrad.qkv", linear_dgrad(dt, s, EPI_F32, M, 3 * C, C, at<char>(x, ap.dqkv), 3 * C, wptr(x, w.w_qkv), dtmp, nullptr,
                             1.0f));
-        G2_TRY(linear_wgrad(dt, s, M, 3 * C, C, at<char>(x, ap.dqkv), 3 * C, at<char>(x, ap.ln1[l]), gf(x, w.w_qkv), acc,
+        G2_T("gemm.wgrad.qkv", linear_wgrad(dt, s, M, 3 * C, C, at<char>(x, ap.dqkv), 3 * C, at<char>(x, ap.ln1[l]), gf(x, w.w_qkv), acc,
                             1.0f, sb, sbytes));
         if (w.b_qkv >= 0)
-            G2_TRY(bias_grad(dt, at<char>(x, ap.dqkv), M, 3 * C, bpart, ap.bias_part_rows, gf(x, w.b_qkv), acc, s));
-        G2_TRY(layernorm_bwd(dt, dtmp, at<float>(x, ap.x[l]), at<float>(x, ap.m1[l]), at<float>(x, ap.r1[l]),
+            G2_T("bias", bias_grad(dt, at<char>(x, ap.dqkv), M, 3 * C, bpart, ap.bias_part_rows, gf(x, w.b_qkv), acc, s));
+        G2_T("ln.bwd", layernorm_bwd(dt, dtmp, at<float>(x, ap.x[l]), at<float>(x, ap.m1[l]), at<float>(x, ap.r1[l]),
                              pf(x, w.ln1_g), dres, bf ? dres_act : nullptr, part, ap.ln_part_rows, M, C, 1, s));
-        G2_TRY(colsum_finish2(part, (M + 63) / 64, 2 * C, gf(x, w.ln1_g), C, gf(x, w.ln1_b), C, acc, s));
+        G2_T("colsum", colsum_finish2(part, (M + 63) / 64, 2 * C, gf(x, w.ln1_g), C, gf(x, w.ln1_b), C, acc, s));
     }
     // embedding: dwte[idx[m]] += dres[m] (after the head's contribution), dwpe[t] (=|+=) sum_b dres[b,t]
-    G2_TRY(encoder_bwd(at<int32_t>(x, x->idx_save), dres, gf(x, pl.wte), gf(x, pl.wpe), M, T, C, c.vocab,
+    G2_T("embed.bwd", encoder_bwd(at<int32_t>(x, x->idx_save), dres, gf(x, pl.wte), gf(x, pl.wpe), M, T, C, c.vocab,
                        at<int32_t>(x, ap.enc_count), at<int32_t>(x, ap.enc_start), at<int32_t>(x, ap.enc_rank),
                        at<int32_t>(x, ap.enc_order), at<int32_t>(x, ap.enc_distinct),
                        at<int32_t>(x, ap.scalars) + SLOT_NDISTINCT, acc, s));
@@ -375,7 +418,7 @@ int gpt2_adamw_step(gpt2_ctx* x, float lr, float beta1, float beta2, float eps, 
     float* sc = at<float>(x, ap.scalars);
     uint32_t* status = status_ptr(x);
     if (clip > 0.0f || d_grad_norm) {
-        G2_TRY(grad_norm(x->bufs.grads, x->pl.n_flat, at<double>(x, ap.norm_part), ap.norm_blocks, clip, sc + SLOT_NORM,
+        G2_T("gradnorm", grad_norm(x->bufs.grads, x->pl.n_flat, at<double>(x, ap.norm_part), ap.norm_blocks, clip, sc + SLOT_NORM,
                          sc + SLOT_COEF, d_grad_norm, status, s));
     } else {
         // coefficient 1: written by the norm kernel's finisher on an empty range
@@ -387,7 +430,7 @@ int gpt2_adamw_step(gpt2_ctx* x, float lr, float beta1, float beta2, float eps, 
     const float decay_mul = (float)(1.0 - (double)lr * (double)weight_decay);
     bf16_t* p16 = x->cfg.dtype == GPT2_DTYPE_BF16 ? at<bf16_t>(x, ap.wlp) : nullptr;
     const uint8_t* tab = decay_mode == GPT2_DECAY_MATRICES ? at<uint8_t>(x, ap.decay_tab) : nullptr;
-    G2_TRY(adamw(x->bufs.params, x->bufs.grads, x->bufs.adam_m, x->bufs.adam_v, p16, x->pl.n_flat, lr, beta1, beta2, eps,
+    G2_T("adamw", adamw(x->bufs.params, x->bufs.grads, x->bufs.adam_m, x->bufs.adam_v, p16, x->pl.n_flat, lr, beta1, beta2, eps,
                  decay_mul, (float)bc1, (float)bc2, tab, sc + SLOT_COEF, s));
     return GPT2_OK;
 }
@@ -404,6 +447,32 @@ int gpt2_sync_status(gpt2_ctx* x, uint32_t* bits) {
 int gpt2_clear_status(gpt2_ctx* x) {
     if (!x) return GPT2_EINVAL;
     G2_TRY(fill_zero(status_ptr(x), 4, x->stream));
+    return GPT2_OK;
+}
+
+int gpt2_timing_begin(gpt2_ctx* x, const char* prefix) {
+    if (!x || !prefix) return GPT2_EINVAL;
+    x->timing = true;
+    x->timing_prefix = prefix;
+    x->ev_pairs.clear();
+    x->ev_used = 0;
+    return GPT2_OK;
+}
+
+int gpt2_timing_end(gpt2_ctx* x, float* total_ms, int32_t* launches) {
+    if (!x) return GPT2_EINVAL;
+    if (hipStreamSynchronize(x->stream) != hipSuccess) return GPT2_EHIP;
+    double tot = 0.0;
+    for (auto& pr : x->ev_pairs) {
+        float ms = 0.0f;
+        if (hipEventElapsedTime(&ms, pr.first, pr.second) != hipSuccess) return GPT2_EHIP;
+        tot += ms;
+    }
+    if (total_ms) *total_ms = (float)tot;
+    if (launches) *launches = (int32_t)x->ev_pairs.size();
+    x->timing = false;
+    x->ev_pairs.clear();
+    x->ev_used = 0;
     return GPT2_OK;
 }
 
@@ -468,7 +537,7 @@ int gpt2_op_linear_bwd(int32_t dtype, int64_t M, int32_t N, int32_t K, const voi
         float* tmp = nullptr;
         if (hipMallocAsync((void**)&tmp, (size_t)std::max(pr, 1) * N * 4, s) != hipSuccess) return GPT2_EHIP;
         hipError_t e = bias_grad(dtype, d_dY, M, N, tmp, std::max(pr, 1), d_db, accumulate ? 1 : 0, s);
-        hipFreeAsync(tmp, s);
+        (void)hipFreeAsync(tmp, s);
         if (e != hipSuccess) return GPT2_EHIP;
     }
     return GPT2_OK;
@@ -494,7 +563,7 @@ int gpt2_op_layernorm_bwd(int64_t rows, int32_t C, const float* d_dy, const floa
     if (hipMallocAsync((void**)&tmp, (size_t)pr * 2 * C * 4, s) != hipSuccess) return GPT2_EHIP;
     hipError_t e = layernorm_bwd(GPT2_DTYPE_F32, d_dy, d_x, d_mean, d_rstd, d_g, d_dx, nullptr, tmp, pr, rows, C, 1, s);
     if (e == hipSuccess) e = colsum_finish2(tmp, (int)((rows + 63) / 64), 2 * C, d_dg, C, d_db, C, 0, s);
-    hipFreeAsync(tmp, s);
+    (void)hipFreeAsync(tmp, s);
     return e == hipSuccess ? GPT2_OK : GPT2_EHIP;
 }
 
@@ -516,7 +585,7 @@ int gpt2_op_attention_bwd(int32_t dtype, int32_t B, int32_t T, int32_t C, int32_
     const size_t n = (size_t)std::max<int64_t>(1, (int64_t)B * H * T);
     if (hipMallocAsync((void**)&Dbuf, n * 4, s) != hipSuccess) return GPT2_EHIP;
     hipError_t e = attention_bwd(dtype, B, T, C, H, d_qkv, d_out, d_lse, d_dout, d_dqkv, Dbuf, s);
-    hipFreeAsync(Dbuf, s);
+    (void)hipFreeAsync(Dbuf, s);
     return e == hipSuccess ? GPT2_OK : GPT2_EHIP;
 }
 
@@ -531,7 +600,7 @@ int gpt2_op_cross_entropy(int32_t dtype, int64_t rows, int32_t V, int32_t ld, vo
     hipError_t e = fill_zero(st, 4, s);
     if (e == hipSuccess)
         e = cross_entropy(dtype, d_logits, rows, V, ld, d_targets, d_loss_rows, d_argmax, write_grad ? 1 : 0, st, s);
-    hipFreeAsync(st, s);
+    (void)hipFreeAsync(st, s);
     return e == hipSuccess ? GPT2_OK : GPT2_EHIP;
 }
 

@@ -160,6 +160,17 @@ int gpt2_adamw_step(gpt2_ctx* ctx, float lr, float beta1, float beta2, float eps
 int gpt2_sync_status(gpt2_ctx* ctx, uint32_t* bits);
 int gpt2_clear_status(gpt2_ctx* ctx);
 
+/* Per-launch timing for profiling. After gpt2_timing_begin(ctx, prefix), every
+ * kernel launch of the step whose label starts with `prefix` is bracketed by HIP
+ * events recorded on the step's stream. gpt2_timing_end synchronises the stream,
+ * returns the summed event-measured duration (ms) and the number of launches
+ * timed, and stops timing. Labels: "embed.fwd", "ln.fwd", "gemm.fwd.{qkv,proj,
+ * fc,fc2,head}", "attn.fwd", "ce", "loss", "gemm.dgrad.{head,fc2,fc,proj,qkv}",
+ * "gemm.wgrad.{head,fc2,fc,proj,qkv}", "ln.bwd", "colsum", "bias", "attn.bwd",
+ * "embed.bwd", "gradnorm", "adamw". An empty prefix times every launch. */
+int gpt2_timing_begin(gpt2_ctx* ctx, const char* prefix);
+int gpt2_timing_end(gpt2_ctx* ctx, float* total_ms, int32_t* launches);
+
 /* Byte offset inside the arena of an activation, for inspection by tests:
  * name in {"x", "xmid", "ln1", "ln2", "qkv", "att", "lse", "fch", "fcg", "xf",
  * "logits", "loss_rows"}; layer ignored for the last three. *elem_bytes receives
