@@ -1,0 +1,469 @@
+// Causal flash attention for head size 64 on bf16 MFMA (v_mfma_f32_32x32x16_bf16).
+//
+// Forward (one workgroup = 128 queries of one (batch, head), 4 waves x 32
+// queries; K/V tiles of 64 keys double-buffered in LDS): the scores are formed
+// transposed, S^T = K Q^T, so each lane owns one query row and 16 of its key
+// columns; the online softmax (running max and sum, base-2 exponent with the
+// 1/sqrt(d) scale folded in) needs one cross-lane exchange per tile. The
+// probabilities go straight from the accumulators into the next MFMA as the
+// B operand of O^T += V^T P^T; the key order inside each 16-key step is the
+// accumulator's row order, matched on the V side by the gfx950 LDS transpose
+// load (ds_read_b64_tr_b16). Saves lse = max + log(sum) per query.
+//
+// Backward (P recomputed from lse): D_i = dO_i . O_i; a dQ kernel with the
+// forward's structure (S^T, dP^T = V dO^T, dS^T = P^T (dP^T - D), dQ^T +=
+// K^T dS^T) and a dK/dV kernel owning 128 keys per workgroup that walks query
+// tiles of 64 (S = Q K^T, dP = dO V^T, dV += P^T dO, dK += dS^T Q). No atomics:
+// every output element is written by exactly one lane, so results are
+// deterministic.
+//
+// LDS tiles are [rows][64] bf16 (128 B per row) with the 16-byte chunk index
+// XOR-ed by a bit-reversal of (row / 2) mod 8: conflict-free both for 128-bit
+// row reads (MFMA operands with the contraction index along the row) and for
+// transpose reads (contraction index down the rows).
+#include <cmath>
+
+#include "device.h"
+
+namespace g2 {
+
+hipError_t attention_fwd_simple(int dtype, int B, int Tn, int C, int H, const void* qkv, void* out, float* lse,
+                                hipStream_t s);
+hipError_t attention_bwd_simple(int dtype, int B, int Tn, int C, int H, const void* qkv, const void* out,
+                                const float* lse, const void* dout, void* dqkv, float* Dbuf, hipStream_t s);
+
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr int kTileBytes = 64 * 128;  // 64 rows x 64 bf16
+
+__device__ __forceinline__ int swz(int row) {
+    const int x = (row >> 1) & 7;
+    return ((x & 1) << 2) | (x & 2) | ((x >> 2) & 1);
+}
+__device__ __forceinline__ int toff(int row, int col) {
+    return row * 128 + ((((col >> 3) ^ swz(row))) << 4) + ((col & 7) << 1);
+}
+
+// 64 rows (r0.., < rmax zero-filled) x 64 columns of a row-major bf16 matrix,
+// two 16-byte chunks per thread (256 threads)
+struct TileRegs {
+    uint4 v[2];
+};
+__device__ __forceinline__ void tile_load(TileRegs& t, const bf16_t* g, int64_t ld, int r0, int rmax, int tid) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int c = tid + 256 * i;
+        const int row = c >> 3, ch = c & 7;
+        uint4 v = make_uint4(0, 0, 0, 0);
+        if (r0 + row < rmax) v = *(const uint4*)(g + (int64_t)(r0 + row) * ld + ch * 8);
+        t.v[i] = v;
+    }
+}
+__device__ __forceinline__ void tile_store(char* lds, const TileRegs& t, int tid) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int c = tid + 256 * i;
+        const int row = c >> 3, ch = c & 7;
+        *(uint4*)(lds + row * 128 + ((ch ^ swz(row)) << 4)) = t.v[i];
+    }
+}
+
+// operand with the contraction index along the tile row: lane l holds row
+// rbase + (l & 31), columns 16 kk + 8 (l >> 5) + 0..7
+__device__ __forceinline__ bf16x8 frag_row(const char* lds, int rbase, int kk, int lane) {
+    const int row = rbase + (lane & 31);
+    const int ch = kk * 2 + (lane >> 5);
+    return *(const bf16x8*)(lds + row * 128 + ((ch ^ swz(row)) << 4));
+}
+
+// operand with the contraction index down the tile rows: lane l holds column
+// cbase + (l & 31), rows kbase + 4 (l >> 5) + {0..3} and kbase + 8 + 4 (l >> 5) + {0..3}
+__device__ __forceinline__ bf16x8 frag_col(const char* lds, int kbase, int cbase, int lane) {
+    const int G = lane >> 4, j = lane & 15;
+    const int row = kbase + 4 * (G >> 1) + (j >> 2);
+    const int col = cbase + 16 * (G & 1) + 4 * (j & 3);
+    return lds_tr2(lds + toff(row, col), lds + toff(row + 8, col));
+}
+
+__device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x16 zero16() {
+    f32x16 z;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) z[r] = 0.0f;
+    return z;
+}
+
+__device__ __forceinline__ bf16x8 load8(const bf16_t* p, bool ok) {
+    if (!ok) {
+        bf16x8 z;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) z[e] = (__bf16)0.0f;
+        return z;
+    }
+    return *(const bf16x8*)p;
+}
+
+// accumulator register r of lane l sits at row 8 (r/4) + 4 (l/32) + r%4
+__device__ __forceinline__ int acc_row(int r, int g) { return 8 * (r >> 2) + 4 * g + (r & 3); }
+
+}  // namespace
+
+// ------------------------------------------------------------------ forward
+__global__ __launch_bounds__(256) void attn_fwd_d64(const bf16_t* qkv, bf16_t* out, float* lse, int T, int C, int H,
+                                                    float sl2) {
+    __shared__ __attribute__((aligned(16))) char smem[2][2][kTileBytes];
+    const int nqb = (T + 127) / 128;
+    const int qb = nqb - 1 - (int)blockIdx.x;  // longest rows first
+    const int h = blockIdx.y, b = blockIdx.z;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 5;
+    const int64_t rs = 3 * (int64_t)C;
+    const bf16_t* base = qkv + (int64_t)b * T * rs;
+    const bf16_t* Qg = base + h * 64;
+    const bf16_t* Kg = base + C + h * 64;
+    const bf16_t* Vg = base + 2 * C + h * 64;
+    const int q0 = qb * 128 + w * 32;
+    const int qi = q0 + (lane & 31);
+    bf16x8 qf[4];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) qf[kk] = load8(Qg + (int64_t)qi * rs + 16 * kk + 8 * g, qi < T);
+    f32x16 o[2] = {zero16(), zero16()};
+    float m = -INFINITY, l = 0.0f;
+    const int kend = min(T, qb * 128 + 128);
+    const int nkt = (kend + 63) / 64;
+    TileRegs rk, rv;
+    tile_load(rk, Kg, rs, 0, T, tid);
+    tile_load(rv, Vg, rs, 0, T, tid);
+    tile_store(smem[0][0], rk, tid);
+    tile_store(smem[0][1], rv, tid);
+    __syncthreads();
+    for (int kt = 0; kt < nkt; ++kt) {
+        const int k0 = kt * 64;
+        const bool more = kt + 1 < nkt;
+        if (more) {
+            tile_load(rk, Kg, rs, k0 + 64, T, tid);
+            tile_load(rv, Vg, rs, k0 + 64, T, tid);
+        }
+        const char* Ks = smem[kt & 1][0];
+        const char* Vs = smem[kt & 1][1];
+        if (k0 <= q0 + 31) {
+            f32x16 s[2];
+#pragma unroll
+            for (int kh = 0; kh < 2; ++kh) {
+                s[kh] = zero16();
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk) s[kh] = mfma(frag_row(Ks, 32 * kh, kk, lane), qf[kk], s[kh]);
+            }
+            const bool diag = k0 + 63 > q0;
+            float mx = -INFINITY;
+#pragma unroll
+            for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    float v = s[kh][r] * sl2;
+                    if (diag && k0 + 32 * kh + acc_row(r, g) > qi) v = -INFINITY;
+                    s[kh][r] = v;
+                    mx = fmaxf(mx, v);
+                }
+            mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+            const float mn = fmaxf(m, mx);
+            const float corr = exp2f(m - mn);
+            l *= corr;
+#pragma unroll
+            for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) o[dt][r] *= corr;
+            float ls = 0.0f;
+            bf16x8 pk[4];
+#pragma unroll
+            for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const float p = exp2f(s[kh][r] - mn);
+                    ls += p;
+                    pk[2 * kh + (r >> 3)][r & 7] = (__bf16)p;
+                }
+            l += ls + __shfl_xor(ls, 32, 64);
+            m = mn;
+#pragma unroll
+            for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+                for (int u = 0; u < 4; ++u) o[dt] = mfma(frag_col(Vs, 16 * u, 32 * dt, lane), pk[u], o[dt]);
+        }
+        if (more) {
+            tile_store(smem[(kt + 1) & 1][0], rk, tid);
+            tile_store(smem[(kt + 1) & 1][1], rv, tid);
+        }
+        __syncthreads();
+    }
+    if (qi < T) {
+        const float inv = 1.0f / l;
+        bf16_t* orow = out + ((int64_t)b * T + qi) * C + h * 64;
+#pragma unroll
+        for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+            for (int rq = 0; rq < 4; ++rq) {
+                const int d = 32 * dt + 8 * rq + 4 * g;
+                uint2 pk2;
+                pk2.x = (uint32_t)f2bf(o[dt][4 * rq + 0] * inv) | ((uint32_t)f2bf(o[dt][4 * rq + 1] * inv) << 16);
+                pk2.y = (uint32_t)f2bf(o[dt][4 * rq + 2] * inv) | ((uint32_t)f2bf(o[dt][4 * rq + 3] * inv) << 16);
+                *(uint2*)(orow + d) = pk2;
+            }
+        if (g == 0) lse[((int64_t)b * H + h) * T + qi] = (m + log2f(l)) * kLn2;
+    }
+}
+
+// ------------------------------------------------------------------ backward: D = rowsum(dO * O)
+__global__ void attn_bwd_pre_d64(const bf16_t* out, const bf16_t* dout, float* Dbuf, int B, int T, int C, int H) {
+    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (t >= (int64_t)B * H * T) return;
+    const int i = (int)(t % T);
+    const int h = (int)((t / T) % H);
+    const int b = (int)(t / ((int64_t)T * H));
+    const int64_t off = ((int64_t)b * T + i) * C + h * 64;
+    float s = 0.0f;
+#pragma unroll
+    for (int c = 0; c < 64; c += 8) {
+        const uint4 a = *(const uint4*)(out + off + c);
+        const uint4 d = *(const uint4*)(dout + off + c);
+        const uint32_t av[4] = {a.x, a.y, a.z, a.w}, dv[4] = {d.x, d.y, d.z, d.w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            s += bf2f((bf16_t)(av[k] & 0xffff)) * bf2f((bf16_t)(dv[k] & 0xffff));
+            s += bf2f((bf16_t)(av[k] >> 16)) * bf2f((bf16_t)(dv[k] >> 16));
+        }
+    }
+    Dbuf[t] = s;
+}
+
+// ------------------------------------------------------------------ backward: dQ
+__global__ __launch_bounds__(256) void attn_bwd_dq_d64(const bf16_t* qkv, const bf16_t* dout, const float* lse,
+                                                       const float* Dbuf, bf16_t* dqkv, int T, int C, int H,
+                                                       float sl2, float scale) {
+    __shared__ __attribute__((aligned(16))) char smem[2][2][kTileBytes];
+    const int nqb = (T + 127) / 128;
+    const int qb = nqb - 1 - (int)blockIdx.x;
+    const int h = blockIdx.y, b = blockIdx.z;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 5;
+    const int64_t rs = 3 * (int64_t)C;
+    const bf16_t* base = qkv + (int64_t)b * T * rs;
+    const bf16_t* Qg = base + h * 64;
+    const bf16_t* Kg = base + C + h * 64;
+    const bf16_t* Vg = base + 2 * C + h * 64;
+    const bf16_t* dOg = dout + (int64_t)b * T * C + h * 64;
+    const int q0 = qb * 128 + w * 32;
+    const int qi = q0 + (lane & 31);
+    const bool qok = qi < T;
+    bf16x8 qf[4], df[4];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+        qf[kk] = load8(Qg + (int64_t)qi * rs + 16 * kk + 8 * g, qok);
+        df[kk] = load8(dOg + (int64_t)qi * C + 16 * kk + 8 * g, qok);
+    }
+    const int64_t lb = ((int64_t)b * H + h) * T;
+    const float lse2 = qok ? lse[lb + qi] * kLog2e : 0.0f;
+    const float Dq = qok ? Dbuf[lb + qi] : 0.0f;
+    f32x16 dq[2] = {zero16(), zero16()};
+    const int kend = min(T, qb * 128 + 128);
+    const int nkt = (kend + 63) / 64;
+    TileRegs rk, rv;
+    tile_load(rk, Kg, rs, 0, T, tid);
+    tile_load(rv, Vg, rs, 0, T, tid);
+    tile_store(smem[0][0], rk, tid);
+    tile_store(smem[0][1], rv, tid);
+    __syncthreads();
+    for (int kt = 0; kt < nkt; ++kt) {
+        const int k0 = kt * 64;
+        const bool more = kt + 1 < nkt;
+        if (more) {
+            tile_load(rk, Kg, rs, k0 + 64, T, tid);
+            tile_load(rv, Vg, rs, k0 + 64, T, tid);
+        }
+        const char* Ks = smem[kt & 1][0];
+        const char* Vs = smem[kt & 1][1];
+        if (k0 <= q0 + 31) {
+            f32x16 s[2], dp[2];
+#pragma unroll
+            for (int kh = 0; kh < 2; ++kh) {
+                s[kh] = zero16();
+                dp[kh] = zero16();
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk) {
+                    s[kh] = mfma(frag_row(Ks, 32 * kh, kk, lane), qf[kk], s[kh]);
+                    dp[kh] = mfma(frag_row(Vs, 32 * kh, kk, lane), df[kk], dp[kh]);
+                }
+            }
+            bf16x8 dsk[4];
+#pragma unroll
+            for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int key = k0 + 32 * kh + acc_row(r, g);
+                    const float p = (key <= qi && key < T) ? exp2f(s[kh][r] * sl2 - lse2) : 0.0f;
+                    dsk[2 * kh + (r >> 3)][r & 7] = (__bf16)(p * (dp[kh][r] - Dq));
+                }
+#pragma unroll
+            for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+                for (int u = 0; u < 4; ++u) dq[dt] = mfma(frag_col(Ks, 16 * u, 32 * dt, lane), dsk[u], dq[dt]);
+        }
+        if (more) {
+            tile_store(smem[(kt + 1) & 1][0], rk, tid);
+            tile_store(smem[(kt + 1) & 1][1], rv, tid);
+        }
+        __syncthreads();
+    }
+    if (qok) {
+        bf16_t* drow = dqkv + ((int64_t)b * T + qi) * rs + h * 64;
+#pragma unroll
+        for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+            for (int rq = 0; rq < 4; ++rq) {
+                const int d = 32 * dt + 8 * rq + 4 * g;
+                uint2 pk2;
+                pk2.x = (uint32_t)f2bf(dq[dt][4 * rq + 0] * scale) | ((uint32_t)f2bf(dq[dt][4 * rq + 1] * scale) << 16);
+                pk2.y = (uint32_t)f2bf(dq[dt][4 * rq + 2] * scale) | ((uint32_t)f2bf(dq[dt][4 * rq + 3] * scale) << 16);
+                *(uint2*)(drow + d) = pk2;
+            }
+    }
+}
+
+// ------------------------------------------------------------------ backward: dK, dV
+__global__ __launch_bounds__(256) void attn_bwd_dkdv_d64(const bf16_t* qkv, const bf16_t* dout, const float* lse,
+                                                         const float* Dbuf, bf16_t* dqkv, int T, int C, int H,
+                                                         float sl2, float scale) {
+    __shared__ __attribute__((aligned(16))) char smem[2][2][kTileBytes];
+    __shared__ float sL[2][64], sD[2][64];
+    const int kb = blockIdx.x;  // earliest keys (most query tiles) first
+    const int h = blockIdx.y, b = blockIdx.z;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 5;
+    const int64_t rs = 3 * (int64_t)C;
+    const bf16_t* base = qkv + (int64_t)b * T * rs;
+    const bf16_t* Qg = base + h * 64;
+    const bf16_t* Kg = base + C + h * 64;
+    const bf16_t* Vg = base + 2 * C + h * 64;
+    const bf16_t* dOg = dout + (int64_t)b * T * C + h * 64;
+    const int64_t lb = ((int64_t)b * H + h) * T;
+    const int k0w = kb * 128 + w * 32;
+    const int kj = k0w + (lane & 31);
+    bf16x8 kf[4], vf[4];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+        kf[kk] = load8(Kg + (int64_t)kj * rs + 16 * kk + 8 * g, kj < T);
+        vf[kk] = load8(Vg + (int64_t)kj * rs + 16 * kk + 8 * g, kj < T);
+    }
+    f32x16 dk[2] = {zero16(), zero16()}, dv[2] = {zero16(), zero16()};
+    const int qt0 = (kb * 128) / 64;
+    const int nqt = (T + 63) / 64;
+    TileRegs rq, rd;
+    float pl = 0.0f, pd = 0.0f;
+    auto fetch = [&](int qt) {
+        tile_load(rq, Qg, rs, qt * 64, T, tid);
+        tile_load(rd, dOg, C, qt * 64, T, tid);
+        if (tid < 64) {
+            const int q = qt * 64 + tid;
+            pl = q < T ? lse[lb + q] * kLog2e : 0.0f;
+            pd = q < T ? Dbuf[lb + q] : 0.0f;
+        }
+    };
+    auto put = [&](int buf) {
+        tile_store(smem[buf][0], rq, tid);
+        tile_store(smem[buf][1], rd, tid);
+        if (tid < 64) {
+            sL[buf][tid] = pl;
+            sD[buf][tid] = pd;
+        }
+    };
+    if (qt0 < nqt) {
+        fetch(qt0);
+        put(0);
+    }
+    __syncthreads();
+    for (int qt = qt0; qt < nqt; ++qt) {
+        const int buf = (qt - qt0) & 1;
+        const bool more = qt + 1 < nqt;
+        if (more) fetch(qt + 1);
+        const int q0t = qt * 64;
+        const char* Qs = smem[buf][0];
+        const char* dOs = smem[buf][1];
+        if (q0t + 63 >= k0w) {
+            bf16x8 pt[4], dst[4];
+#pragma unroll
+            for (int qh = 0; qh < 2; ++qh) {
+                f32x16 s = zero16(), dp = zero16();
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk) {
+                    s = mfma(frag_row(Qs, 32 * qh, kk, lane), kf[kk], s);
+                    dp = mfma(frag_row(dOs, 32 * qh, kk, lane), vf[kk], dp);
+                }
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int ql = 32 * qh + acc_row(r, g);
+                    const int q = q0t + ql;
+                    const float p = (q >= kj && q < T) ? exp2f(s[r] * sl2 - sL[buf][ql]) : 0.0f;
+                    pt[2 * qh + (r >> 3)][r & 7] = (__bf16)p;
+                    dst[2 * qh + (r >> 3)][r & 7] = (__bf16)(p * (dp[r] - sD[buf][ql]));
+                }
+            }
+#pragma unroll
+            for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    dv[dt] = mfma(pt[u], frag_col(dOs, 16 * u, 32 * dt, lane), dv[dt]);
+                    dk[dt] = mfma(dst[u], frag_col(Qs, 16 * u, 32 * dt, lane), dk[dt]);
+                }
+        }
+        if (more) put(buf ^ 1);
+        __syncthreads();
+    }
+    // lane l holds column d = 32 dt + (l & 31), keys k0w + acc_row(r, g)
+#pragma unroll
+    for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int key = k0w + acc_row(r, g);
+            if (key < T) {
+                bf16_t* drow = dqkv + ((int64_t)b * T + key) * rs + h * 64 + 32 * dt + (lane & 31);
+                drow[C] = f2bf(dk[dt][r] * scale);
+                drow[2 * C] = f2bf(dv[dt][r]);
+            }
+        }
+}
+
+// ------------------------------------------------------------------ dispatch
+hipError_t attention_fwd(int dtype, int B, int Tn, int C, int H, const void* qkv, void* out, float* lse,
+                         hipStream_t s) {
+    if (B == 0 || Tn == 0) return hipSuccess;
+    if (dtype == GPT2_DTYPE_BF16 && C / H == 64) {
+        const float sl2 = kLog2e / 8.0f;  // 1/sqrt(64) in base 2
+        dim3 grid((Tn + 127) / 128, H, B);
+        hipLaunchKernelGGL(attn_fwd_d64, grid, dim3(256), 0, s, (const bf16_t*)qkv, (bf16_t*)out, lse, Tn, C, H, sl2);
+        return hipGetLastError();
+    }
+    return attention_fwd_simple(dtype, B, Tn, C, H, qkv, out, lse, s);
+}
+
+hipError_t attention_bwd(int dtype, int B, int Tn, int C, int H, const void* qkv, const void* out, const float* lse,
+                         const void* dout, void* dqkv, float* Dbuf, hipStream_t s) {
+    if (B == 0 || Tn == 0) return hipSuccess;
+    if (dtype == GPT2_DTYPE_BF16 && C / H == 64) {
+        const float sl2 = kLog2e / 8.0f;
+        const float scale = 0.125f;
+        const int64_t n = (int64_t)B * H * Tn;
+        hipLaunchKernelGGL(attn_bwd_pre_d64, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, (const bf16_t*)out,
+                           (const bf16_t*)dout, Dbuf, B, Tn, C, H);
+        dim3 grid((Tn + 127) / 128, H, B);
+        hipLaunchKernelGGL(attn_bwd_dq_d64, grid, dim3(256), 0, s, (const bf16_t*)qkv, (const bf16_t*)dout, lse,
+                           (const float*)Dbuf, (bf16_t*)dqkv, Tn, C, H, sl2, scale);
+        hipLaunchKernelGGL(attn_bwd_dkdv_d64, grid, dim3(256), 0, s, (const bf16_t*)qkv, (const bf16_t*)dout, lse,
+                           (const float*)Dbuf, (bf16_t*)dqkv, Tn, C, H, sl2, scale);
+        return hipGetLastError();
+    }
+    return attention_bwd_simple(dtype, B, Tn, C, H, qkv, out, lse, dout, dqkv, Dbuf, s);
+}
+
+}  // namespace g2

@@ -269,16 +269,4 @@ hipError_t attention_bwd_simple(int dtype, int B, int Tn, int C, int H, const vo
     return bwd_simple<float, 128>(B, Tn, C, H, qkv, out, lse, dout, dqkv, Dbuf, s);
 }
 
-// dispatch: the scalar kernels for now
-hipError_t attention_fwd(int dtype, int B, int Tn, int C, int H, const void* qkv, void* out, float* lse,
-                         hipStream_t s) {
-    if (B == 0 || Tn == 0) return hipSuccess;
-    return attention_fwd_simple(dtype, B, Tn, C, H, qkv, out, lse, s);
-}
-hipError_t attention_bwd(int dtype, int B, int Tn, int C, int H, const void* qkv, const void* out, const float* lse,
-                         const void* dout, void* dqkv, float* Dbuf, hipStream_t s) {
-    if (B == 0 || Tn == 0) return hipSuccess;
-    return attention_bwd_simple(dtype, B, Tn, C, H, qkv, out, lse, dout, dqkv, Dbuf, s);
-}
-
 }  // namespace g2

@@ -64,6 +64,20 @@ __device__ __forceinline__ bf16x8 lds_tr_pair(const char* p, int gap) {
 #endif
 }
 
+// Two gfx950 LDS transpose loads from independent addresses, packed as above.
+__device__ __forceinline__ bf16x8 lds_tr2(const char* p0, const char* p1) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((G2_LDS s16x4*)p0);
+    s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((G2_LDS s16x4*)p1);
+    typedef short s16x8 __attribute__((ext_vector_type(8)));
+    s16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    return __builtin_bit_cast(bf16x8, v);
+#else
+    (void)p0; (void)p1;
+    return bf16x8{};
+#endif
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);

@@ -115,7 +115,8 @@ def test_layernorm_fwd_bwd(b, oracle, dtype, rows, C):
     assert max_rel(to_host(dg), rdg) <= 1e-5 and max_rel(to_host(dbb), rdb) <= 1e-5
 
 
-ATT = [(2, 100, 128, 2), (1, 64, 128, 4), (3, 37, 96, 3), (1, 256, 384, 6), (2, 1, 64, 1)]
+ATT = [(2, 100, 128, 2), (1, 64, 128, 4), (3, 37, 96, 3), (1, 256, 384, 6), (2, 1, 64, 1), (2, 300, 768, 12),
+       (1, 1024, 256, 4), (1, 129, 64, 1)]
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
