@@ -61,7 +61,7 @@ struct ArenaPlan {
     Region xL, xf, mf, rf, logits, loss_rows;
     // backward scratch
     Region dres, dres_act, dtmp, dF, dqkv, datt, attD, ln_part, bias_part;
-    Region enc_count, enc_start, enc_rank, enc_order, enc_distinct;
+    Region enc_count, enc_start, enc_segstart, enc_order, enc_segtok;
     size_t total = 0;
     int ln_part_rows = 0;    // partial rows of the LayerNorm parameter-gradient reduction
     int bias_part_rows = 0;  // partial rows of the bias-gradient reduction
@@ -76,7 +76,7 @@ enum ScalarSlot {
     SLOT_COEF = 1,     // float clip coefficient for AdamW
     SLOT_NORM = 2,     // float gradient norm
     SLOT_LOSS = 3,     // float mean loss (when the caller passes no loss pointer)
-    SLOT_NDISTINCT = 4 // int32 number of distinct tokens (embedding backward)
+    SLOT_NSEG = 4      // int32 number of token segments (embedding backward)
 };
 
 // --------------------------------------------------------------- GEMM
@@ -115,6 +115,7 @@ hipError_t layernorm_fwd(int dtype, const float* x, const float* g, const float*
 hipError_t layernorm_bwd(int dtype, const float* dy, const float* x, const float* mean, const float* rstd,
                          const float* g, float* dres, void* dres_act, float* part, int part_rows, int64_t rows,
                          int C, int add, hipStream_t s);
+int ln_bwd_partial_rows(int64_t rows);  // partial rows layernorm_bwd writes
 hipError_t colsum_finish2(const float* part, int part_rows, int ld, float* out_a, int na, float* out_b, int nb,
                           int accumulate, hipStream_t s);
 hipError_t bias_grad(int dtype, const void* dY, int64_t rows, int N, float* part, int part_rows, float* db,
@@ -127,8 +128,8 @@ hipError_t cross_entropy(int dtype, void* logits, int64_t rows, int V, int ld, c
                          float* loss_rows, int32_t* argmax, int write_grad, uint32_t* status, hipStream_t s);
 hipError_t mean_loss(const float* loss_rows, int64_t rows, float* out, uint32_t* status, hipStream_t s);
 hipError_t encoder_bwd(const int32_t* idx, const float* dres, float* dwte, float* dwpe, int M, int T, int C,
-                       int V, int32_t* count, int32_t* start, int32_t* rank, int32_t* order,
-                       int32_t* distinct, int32_t* ndistinct, int accumulate_wpe, hipStream_t s);
+                       int V, int32_t* count, int32_t* start, int32_t* seg_start, int32_t* order, int32_t* seg_tok,
+                       int32_t* nseg_total, float* seg_part, int accumulate_wpe, hipStream_t s);
 hipError_t cast_f32_bf16(const float* src, bf16_t* dst, int64_t n, hipStream_t s);
 hipError_t fill_zero(void* p, size_t bytes, hipStream_t s);
 hipError_t grad_norm(const float* g, int64_t n, double* part, int nblocks, float clip, float* norm_out,

@@ -24,6 +24,15 @@ __device__ __forceinline__ bf16_t f2bf(float f) {
 }
 __device__ __forceinline__ float bf2f(bf16_t h) { return __uint_as_float((uint32_t)h << 16); }
 
+__device__ __forceinline__ void unpack8f(uint4 u, float (&o)[8]) {
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        o[2 * k] = __uint_as_float(w[k] << 16);
+        o[2 * k + 1] = __uint_as_float(w[k] & 0xffff0000u);
+    }
+}
+
 // activation element access for the two storage types
 template <class T> struct Act;
 template <> struct Act<float> {
@@ -35,16 +44,19 @@ template <> struct Act<bf16_t> {
     __device__ static void st(bf16_t* p, int64_t i, float v) { p[i] = f2bf(v); }
 };
 
-// tanh approximation of GELU and its derivative (constants sqrt(2/pi), 0.044715)
-__device__ __forceinline__ float gelu_tanh(float u) {
-    const float k0 = 0.7978845608028654f, k1 = 0.044715f;
-    float t = tanhf(k0 * (u + k1 * u * u * u));
-    return 0.5f * u * (1.0f + t);
+// tanh approximation of GELU, 0.5 u (1 + tanh z) with z = sqrt(2/pi) (u + 0.044715 u^3),
+// evaluated through the identity 0.5 (1 + tanh z) = 1 / (1 + exp(-2 z)): one exp and
+// one reciprocal, no cancellation near zero. Its derivative uses
+// 1 - tanh(z)^2 = 4 s (1 - s) with s = 1 / (1 + exp(-2 z)).
+__device__ __forceinline__ float gelu_sig(float u) {
+    const float k0x2 = 1.5957691216057308f, k1 = 0.044715f;  // 2 sqrt(2/pi)
+    return __builtin_amdgcn_rcpf(1.0f + __expf(-k0x2 * (u + k1 * u * u * u)));
 }
+__device__ __forceinline__ float gelu_tanh(float u) { return u * gelu_sig(u); }
 __device__ __forceinline__ float gelu_tanh_grad(float u) {
     const float k0 = 0.7978845608028654f, k1 = 0.044715f;
-    float t = tanhf(k0 * (u + k1 * u * u * u));
-    return 0.5f * (1.0f + t) + 0.5f * u * (1.0f - t * t) * k0 * (1.0f + 3.0f * k1 * u * u);
+    const float sg = gelu_sig(u);
+    return sg + 2.0f * u * sg * (1.0f - sg) * k0 * (1.0f + 3.0f * k1 * u * u);
 }
 
 // Two gfx950 LDS transpose loads (ds_read_b64_tr_b16) 'gap' bytes apart, packed

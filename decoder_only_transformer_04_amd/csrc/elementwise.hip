@@ -65,8 +65,12 @@ hipError_t encoder_fwd(int dtype, const int32_t* idx, const float* wte32, const 
 
 // Backward of the gather, deterministic: positions are grouped by token with a
 // stable counting sort (count, exclusive scan, rank = number of earlier
-// positions holding the same id), then each token's rows are summed in
-// position order and added to its dwte row. dwpe[t] = sum over the batch.
+// positions holding the same id). Each token's position list is cut into
+// segments of at most 32 positions; segment sums (in position order) are
+// computed in parallel, then each token adds its segments, in order, to its
+// dwte row. dwpe[t] = sum over the batch.
+constexpr int kEncSeg = 32;
+
 __global__ void enc_count_kernel(const int32_t* idx, int M, int V, int32_t* count) {
     int m = blockIdx.x * blockDim.x + threadIdx.x;
     if (m < M) {
@@ -75,31 +79,40 @@ __global__ void enc_count_kernel(const int32_t* idx, int M, int V, int32_t* coun
     }
 }
 
-// one block: exclusive scan of count[0..V) into start
-__global__ void enc_scan_kernel(const int32_t* count, int32_t* start, int V) {
-    __shared__ int32_t sums[1024];
+// one block: exclusive scans of count[] (row starts) and of the segment counts
+__global__ void enc_scan_kernel(const int32_t* count, int32_t* start, int32_t* seg_start, int32_t* nseg_total, int V) {
+    __shared__ int32_t sums[1024], segs[1024];
     const int tid = threadIdx.x;
     const int per = (V + 1023) / 1024;
     const int b = tid * per, e = min(V, b + per);
-    int32_t s = 0;
-    for (int i = b; i < e; ++i) s += count[i];
+    int32_t s = 0, sg = 0;
+    for (int i = b; i < e; ++i) {
+        s += count[i];
+        sg += (count[i] + kEncSeg - 1) / kEncSeg;
+    }
     sums[tid] = s;
+    segs[tid] = sg;
     __syncthreads();
     for (int o = 1; o < 1024; o <<= 1) {
-        int32_t v = tid >= o ? sums[tid - o] : 0;
+        const int32_t v = tid >= o ? sums[tid - o] : 0;
+        const int32_t w = tid >= o ? segs[tid - o] : 0;
         __syncthreads();
         sums[tid] += v;
+        segs[tid] += w;
         __syncthreads();
     }
     int32_t run = tid > 0 ? sums[tid - 1] : 0;
+    int32_t srun = tid > 0 ? segs[tid - 1] : 0;
     for (int i = b; i < e; ++i) {
         start[i] = run;
+        seg_start[i] = srun;
         run += count[i];
+        srun += (count[i] + kEncSeg - 1) / kEncSeg;
     }
+    if (tid == 1023) *nseg_total = segs[1023];
 }
 
-__global__ void enc_rank_kernel(const int32_t* idx, int M, int V, const int32_t* start, int32_t* order,
-                                int32_t* distinct, int32_t* ndistinct) {
+__global__ void enc_rank_kernel(const int32_t* idx, int M, int V, const int32_t* start, int32_t* order) {
     __shared__ int32_t tile[256];
     const int m = blockIdx.x * 256 + threadIdx.x;
     const int mine = m < M ? idx[m] : -1;
@@ -113,22 +126,42 @@ __global__ void enc_rank_kernel(const int32_t* idx, int M, int V, const int32_t*
         for (int t = 0; t < lim; ++t) rank += tile[t] == mine;
         __syncthreads();
     }
-    if (m < M && mine >= 0 && mine < V) {
-        order[start[mine] + rank] = m;
-        if (rank == 0) distinct[atomicAdd(ndistinct, 1)] = mine;
+    if (m < M && mine >= 0 && mine < V) order[start[mine] + rank] = m;
+}
+
+__global__ void enc_segfill_kernel(const int32_t* count, const int32_t* seg_start, int32_t* seg_tok, int V) {
+    const int v = blockIdx.x * blockDim.x + threadIdx.x;
+    if (v >= V) return;
+    const int n = (count[v] + kEncSeg - 1) / kEncSeg;
+    for (int k = 0; k < n; ++k) seg_tok[seg_start[v] + k] = v;
+}
+
+__global__ void enc_segsum_kernel(const float* dres, int C, const int32_t* count, const int32_t* start,
+                                  const int32_t* seg_start, const int32_t* order, const int32_t* seg_tok,
+                                  const int32_t* nseg_total, float* seg_part) {
+    const int seg = blockIdx.x;
+    if (seg >= *nseg_total) return;
+    const int v = seg_tok[seg];
+    const int r0 = start[v] + kEncSeg * (seg - seg_start[v]);
+    const int r1 = min(start[v] + count[v], r0 + kEncSeg);
+    for (int c = threadIdx.x; c < C; c += blockDim.x) {
+        float s = 0.0f;
+        for (int r = r0; r < r1; ++r) s += dres[(int64_t)order[r] * C + c];
+        seg_part[(int64_t)seg * C + c] = s;
     }
 }
 
-__global__ void enc_accum_kernel(const float* dres, float* dwte, int C, const int32_t* count, const int32_t* start,
-                                 const int32_t* order, const int32_t* distinct, const int32_t* ndistinct) {
-    const int j = blockIdx.x;
-    if (j >= *ndistinct) return;
-    const int tok = distinct[j];
-    const int b = start[tok], n = count[tok];
+__global__ void enc_tokadd_kernel(float* dwte, int C, const int32_t* count, const int32_t* seg_start,
+                                  const int32_t* seg_tok, const int32_t* nseg_total, const float* seg_part) {
+    const int seg = blockIdx.x;
+    if (seg >= *nseg_total) return;
+    const int v = seg_tok[seg];
+    if (seg != seg_start[v]) return;  // the token's first segment adds all of them
+    const int n = (count[v] + kEncSeg - 1) / kEncSeg;
     for (int c = threadIdx.x; c < C; c += blockDim.x) {
-        float s = 0.0f;
-        for (int r = 0; r < n; ++r) s += dres[(int64_t)order[b + r] * C + c];
-        dwte[(int64_t)tok * C + c] += s;
+        float t = 0.0f;
+        for (int k = 0; k < n; ++k) t += seg_part[(int64_t)(seg + k) * C + c];
+        dwte[(int64_t)v * C + c] += t;
     }
 }
 
@@ -142,20 +175,20 @@ __global__ void enc_wpe_kernel(const float* dres, float* dwpe, int B, int T, int
 }
 
 hipError_t encoder_bwd(const int32_t* idx, const float* dres, float* dwte, float* dwpe, int M, int T, int C, int V,
-                       int32_t* count, int32_t* start, int32_t* rank_unused, int32_t* order, int32_t* distinct,
-                       int32_t* ndistinct, int accumulate_wpe, hipStream_t s) {
-    (void)rank_unused;
+                       int32_t* count, int32_t* start, int32_t* seg_start, int32_t* order, int32_t* seg_tok,
+                       int32_t* nseg_total, float* seg_part, int accumulate_wpe, hipStream_t s) {
     if (M == 0) return hipSuccess;
     hipError_t e = fill_zero(count, (size_t)V * 4, s);
     if (e != hipSuccess) return e;
-    e = fill_zero(ndistinct, 4, s);
-    if (e != hipSuccess) return e;
     hipLaunchKernelGGL(enc_count_kernel, dim3(nblk(M, 256)), dim3(256), 0, s, idx, M, V, count);
-    hipLaunchKernelGGL(enc_scan_kernel, dim3(1), dim3(1024), 0, s, count, start, V);
-    hipLaunchKernelGGL(enc_rank_kernel, dim3(nblk(M, 256)), dim3(256), 0, s, idx, M, V, start, order, distinct,
-                       ndistinct);
-    hipLaunchKernelGGL(enc_accum_kernel, dim3(M), dim3(256), 0, s, dres, dwte, C, count, start, order, distinct,
-                       ndistinct);
+    hipLaunchKernelGGL(enc_scan_kernel, dim3(1), dim3(1024), 0, s, count, start, seg_start, nseg_total, V);
+    hipLaunchKernelGGL(enc_rank_kernel, dim3(nblk(M, 256)), dim3(256), 0, s, idx, M, V, start, order);
+    hipLaunchKernelGGL(enc_segfill_kernel, dim3(nblk(V, 256)), dim3(256), 0, s, count, seg_start, seg_tok, V);
+    // at most M segments (each holds at least one position)
+    hipLaunchKernelGGL(enc_segsum_kernel, dim3(M), dim3(256), 0, s, dres, C, count, start, seg_start, order, seg_tok,
+                       nseg_total, seg_part);
+    hipLaunchKernelGGL(enc_tokadd_kernel, dim3(M), dim3(256), 0, s, dwte, C, count, seg_start, seg_tok, nseg_total,
+                       seg_part);
     const int B = M / T;
     hipLaunchKernelGGL(enc_wpe_kernel, dim3(nblk((int64_t)T * C, 256)), dim3(256), 0, s, dres, dwpe, B, T, C,
                        accumulate_wpe);
@@ -163,8 +196,66 @@ hipError_t encoder_bwd(const int32_t* idx, const float* dres, float* dwte, float
 }
 
 // ------------------------------------------------------------------ LayerNorm
-// One wave per row; lane holds columns lane + 64 j (j < NJ) in registers.
+// One wave per row. The vector kernels (C % 4 == 0) give lane l the float4
+// columns 4 (l + 64 j); the scalar kernels (any C) give it columns l + 64 j.
 // y = (x - mean) * rstd * g + b, biased variance, rstd = 1 / sqrt(var + eps).
+template <class T> __device__ __forceinline__ void st4(T* p, float4 v);
+template <> __device__ __forceinline__ void st4<float>(float* p, float4 v) { *(float4*)p = v; }
+template <> __device__ __forceinline__ void st4<bf16_t>(bf16_t* p, float4 v) {
+    uint2 o;
+    o.x = (uint32_t)f2bf(v.x) | ((uint32_t)f2bf(v.y) << 16);
+    o.y = (uint32_t)f2bf(v.z) | ((uint32_t)f2bf(v.w) << 16);
+    *(uint2*)p = o;
+}
+__device__ __forceinline__ float hsum4(float4 v) { return (v.x + v.y) + (v.z + v.w); }
+
+template <int NJ4, class T>
+__global__ __launch_bounds__(256) void ln_fwd_v4(const float* x, const float* g, const float* b, float eps, T* y,
+                                                 float* mean, float* rstd, int64_t rows, int C) {
+    const int lane = threadIdx.x & 63;
+    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= rows) return;
+    const int C4 = C / 4;
+    const float4* xr = (const float4*)(x + row * C);
+    float4 v[NJ4];
+    float s = 0.0f;
+#pragma unroll
+    for (int j = 0; j < NJ4; ++j) {
+        const int c4 = lane + 64 * j;
+        v[j] = c4 < C4 ? xr[c4] : make_float4(0.f, 0.f, 0.f, 0.f);
+        s += hsum4(v[j]);
+    }
+    const float mu = wave_sum(s) / (float)C;
+    float q = 0.0f;
+#pragma unroll
+    for (int j = 0; j < NJ4; ++j) {
+        const int c4 = lane + 64 * j;
+        if (c4 < C4) {
+            const float a = v[j].x - mu, bq = v[j].y - mu, c = v[j].z - mu, d = v[j].w - mu;
+            q += (a * a + bq * bq) + (c * c + d * d);
+        }
+    }
+    const float var = wave_sum(q) / (float)C;
+    const float rs = 1.0f / sqrtf(var + eps);
+#pragma unroll
+    for (int j = 0; j < NJ4; ++j) {
+        const int c4 = lane + 64 * j;
+        if (c4 < C4) {
+            const float4 gg = ((const float4*)g)[c4], bb = ((const float4*)b)[c4];
+            float4 o;
+            o.x = (v[j].x - mu) * rs * gg.x + bb.x;
+            o.y = (v[j].y - mu) * rs * gg.y + bb.y;
+            o.z = (v[j].z - mu) * rs * gg.z + bb.z;
+            o.w = (v[j].w - mu) * rs * gg.w + bb.w;
+            st4<T>(y + row * C + 4 * c4, o);
+        }
+    }
+    if (lane == 0) {
+        mean[row] = mu;
+        rstd[row] = rs;
+    }
+}
+
 template <int NJ, class T>
 __global__ __launch_bounds__(256) void ln_fwd_kernel(const float* x, const float* g, const float* b, float eps, T* y,
                                                      float* mean, float* rstd, int64_t rows, int C) {
@@ -205,6 +296,19 @@ template <class T>
 static hipError_t ln_fwd_dispatch(const float* x, const float* g, const float* b, float eps, T* y, float* mean,
                                   float* rstd, int64_t rows, int C, hipStream_t s) {
     dim3 grid(nblk(rows, 4)), blk(256);
+    if (C % 4 == 0) {
+        const int nj4 = (C / 4 + 63) / 64;
+#define G2_LNF4(N) hipLaunchKernelGGL((ln_fwd_v4<N, T>), grid, blk, 0, s, x, g, b, eps, y, mean, rstd, rows, C)
+        if (nj4 <= 1) G2_LNF4(1);
+        else if (nj4 <= 2) G2_LNF4(2);
+        else if (nj4 <= 3) G2_LNF4(3);
+        else if (nj4 <= 4) G2_LNF4(4);
+        else if (nj4 <= 6) G2_LNF4(6);
+        else if (nj4 <= 8) G2_LNF4(8);
+        else return hipErrorInvalidValue;
+#undef G2_LNF4
+        return hipGetLastError();
+    }
     const int nj = (C + 63) / 64;
 #define G2_LNF(N) hipLaunchKernelGGL((ln_fwd_kernel<N, T>), grid, blk, 0, s, x, g, b, eps, y, mean, rstd, rows, C)
     if (nj <= 2) G2_LNF(2);
@@ -229,7 +333,83 @@ hipError_t layernorm_fwd(int dtype, const float* x, const float* g, const float*
 
 // dx = rstd (g dy - mean(g dy) - xhat mean(g dy xhat)); dres (+)= dx; the act copy
 // of dres is refreshed; per-block partial sums of dy*xhat (dg) and dy (db) go to
-// part[block][0..C) and part[block][C..2C). Each block covers 64 rows (16 per wave).
+// part[block][0..C) and part[block][C..2C). A block covers 16 rows (4 per wave).
+int ln_bwd_partial_rows(int64_t rows) { return (int)((rows + 15) / 16); }
+
+template <int NJ4, class T>
+__global__ __launch_bounds__(256) void ln_bwd_v4(const float* dy, const float* x, const float* mean, const float* rstd,
+                                                 const float* g, float* dres, T* dres_act, float* part, int64_t rows,
+                                                 int C, int add) {
+    __shared__ float red[4][2][256 * NJ4];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int C4 = C / 4;
+    float4 gg[NJ4], pg[NJ4], pb[NJ4];
+#pragma unroll
+    for (int j = 0; j < NJ4; ++j) {
+        const int c4 = lane + 64 * j;
+        gg[j] = c4 < C4 ? ((const float4*)g)[c4] : make_float4(0.f, 0.f, 0.f, 0.f);
+        pg[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+        pb[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    for (int rr = 0; rr < 4; ++rr) {
+        const int64_t row = (int64_t)blockIdx.x * 16 + wave * 4 + rr;
+        if (row >= rows) break;
+        const float mu = mean[row], rs = rstd[row];
+        const float4* xr = (const float4*)(x + row * C);
+        const float4* dr = (const float4*)(dy + row * C);
+        float4 xh[NJ4], d[NJ4];
+        float a = 0.0f, bb = 0.0f;
+#pragma unroll
+        for (int j = 0; j < NJ4; ++j) {
+            const int c4 = lane + 64 * j;
+            if (c4 < C4) {
+                const float4 xv = xr[c4];
+                d[j] = dr[c4];
+                xh[j] = make_float4((xv.x - mu) * rs, (xv.y - mu) * rs, (xv.z - mu) * rs, (xv.w - mu) * rs);
+            } else {
+                d[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+                xh[j] = d[j];
+            }
+            const float4 gd = make_float4(gg[j].x * d[j].x, gg[j].y * d[j].y, gg[j].z * d[j].z, gg[j].w * d[j].w);
+            a += hsum4(gd);
+            bb += (gd.x * xh[j].x + gd.y * xh[j].y) + (gd.z * xh[j].z + gd.w * xh[j].w);
+            pg[j].x += d[j].x * xh[j].x; pg[j].y += d[j].y * xh[j].y;
+            pg[j].z += d[j].z * xh[j].z; pg[j].w += d[j].w * xh[j].w;
+            pb[j].x += d[j].x; pb[j].y += d[j].y; pb[j].z += d[j].z; pb[j].w += d[j].w;
+        }
+        a = wave_sum(a) / (float)C;
+        bb = wave_sum(bb) / (float)C;
+#pragma unroll
+        for (int j = 0; j < NJ4; ++j) {
+            const int c4 = lane + 64 * j;
+            if (c4 < C4) {
+                float4 o = make_float4(rs * (gg[j].x * d[j].x - a - xh[j].x * bb),
+                                       rs * (gg[j].y * d[j].y - a - xh[j].y * bb),
+                                       rs * (gg[j].z * d[j].z - a - xh[j].z * bb),
+                                       rs * (gg[j].w * d[j].w - a - xh[j].w * bb));
+                float4* dp = (float4*)(dres + row * C) + c4;
+                if (add) {
+                    const float4 old = *dp;
+                    o.x += old.x; o.y += old.y; o.z += old.z; o.w += old.w;
+                }
+                *dp = o;
+                if (dres_act) st4<T>(dres_act + row * C + 4 * c4, o);
+            }
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < NJ4; ++j) {
+        const int c = 4 * (lane + 64 * j);
+        red[wave][0][c] = pg[j].x; red[wave][0][c + 1] = pg[j].y; red[wave][0][c + 2] = pg[j].z; red[wave][0][c + 3] = pg[j].w;
+        red[wave][1][c] = pb[j].x; red[wave][1][c + 1] = pb[j].y; red[wave][1][c + 2] = pb[j].z; red[wave][1][c + 3] = pb[j].w;
+    }
+    __syncthreads();
+    for (int c = threadIdx.x; c < C; c += 256) {
+        part[(int64_t)blockIdx.x * 2 * C + c] = ((red[0][0][c] + red[1][0][c]) + red[2][0][c]) + red[3][0][c];
+        part[(int64_t)blockIdx.x * 2 * C + C + c] = ((red[0][1][c] + red[1][1][c]) + red[2][1][c]) + red[3][1][c];
+    }
+}
+
 template <int NJ, class T>
 __global__ __launch_bounds__(256) void ln_bwd_kernel(const float* dy, const float* x, const float* mean,
                                                      const float* rstd, const float* g, float* dres, T* dres_act,
@@ -244,8 +424,8 @@ __global__ __launch_bounds__(256) void ln_bwd_kernel(const float* dy, const floa
         pb[j] = 0.0f;
         gg[j] = c < C ? g[c] : 0.0f;
     }
-    for (int rr = 0; rr < 16; ++rr) {
-        const int64_t row = (int64_t)blockIdx.x * 64 + wave * 16 + rr;
+    for (int rr = 0; rr < 4; ++rr) {
+        const int64_t row = (int64_t)blockIdx.x * 16 + wave * 4 + rr;
         if (row >= rows) break;
         const float mu = mean[row], rs = rstd[row];
         float xh[NJ], d[NJ];
@@ -290,7 +470,22 @@ template <class T>
 static hipError_t ln_bwd_dispatch(const float* dy, const float* x, const float* mean, const float* rstd,
                                   const float* g, float* dres, T* dres_act, float* part, int64_t rows, int C, int add,
                                   hipStream_t s) {
-    dim3 grid(nblk(rows, 64)), blk(256);
+    dim3 grid(nblk(rows, 16)), blk(256);
+    if (C % 4 == 0) {
+        const int nj4 = (C / 4 + 63) / 64;
+#define G2_LNB4(N)                                                                                              \
+    hipLaunchKernelGGL((ln_bwd_v4<N, T>), grid, blk, 0, s, dy, x, mean, rstd, g, dres, dres_act, part, rows, C, \
+                       add)
+        if (nj4 <= 1) G2_LNB4(1);
+        else if (nj4 <= 2) G2_LNB4(2);
+        else if (nj4 <= 3) G2_LNB4(3);
+        else if (nj4 <= 4) G2_LNB4(4);
+        else if (nj4 <= 6) G2_LNB4(6);
+        else if (nj4 <= 8) G2_LNB4(8);
+        else return hipErrorInvalidValue;
+#undef G2_LNB4
+        return hipGetLastError();
+    }
     const int nj = (C + 63) / 64;
 #define G2_LNB(N)                                                                                                  \
     hipLaunchKernelGGL((ln_bwd_kernel<N, T>), grid, blk, 0, s, dy, x, mean, rstd, g, dres, dres_act, part, rows, C, \
@@ -310,32 +505,88 @@ hipError_t layernorm_bwd(int dtype, const float* dy, const float* x, const float
                          const float* g, float* dres, void* dres_act, float* part, int part_rows, int64_t rows, int C,
                          int add, hipStream_t s) {
     if (rows == 0) return hipSuccess;
-    if ((int64_t)part_rows < (rows + 63) / 64) return hipErrorInvalidValue;
+    if (part_rows < ln_bwd_partial_rows(rows)) return hipErrorInvalidValue;
     if (dtype == GPT2_DTYPE_BF16)
         return ln_bwd_dispatch<bf16_t>(dy, x, mean, rstd, g, dres, (bf16_t*)dres_act, part, rows, C, add, s);
     return ln_bwd_dispatch<float>(dy, x, mean, rstd, g, dres, (float*)dres_act, part, rows, C, add, s);
 }
 
-// out_a[c] (+)= sum_p part[p][c] for c < na; out_b[c] (+)= sum_p part[p][na + c] for c < nb,
-// partial rows summed in index order
-__global__ void colsum_kernel(const float* part, int prows, int ld, float* out_a, int na, float* out_b, int nb,
-                              int accumulate) {
-    const int c = blockIdx.x * blockDim.x + threadIdx.x;
-    if (c >= na + nb) return;
+// out_a[c] (+)= sum_p part[p][c] for c < na; out_b[c] (+)= sum_p part[p][na + c] for c < nb.
+// 64 columns per block, 16 row slices summed in a fixed order.
+__global__ __launch_bounds__(1024) void colsum_kernel(const float* part, int prows, int ld, float* out_a, int na,
+                                                      float* out_b, int nb, int accumulate) {
+    __shared__ float red[16][65];
+    const int cl = threadIdx.x & 63, sl = threadIdx.x >> 6;
+    const int c = blockIdx.x * 64 + cl;
     float s = 0.0f;
-    for (int p = 0; p < prows; ++p) s += part[(int64_t)p * ld + c];
-    float* o = c < na ? out_a + c : out_b + (c - na);
-    *o = accumulate ? *o + s : s;
+    if (c < na + nb)
+        for (int p = sl; p < prows; p += 16) s += part[(int64_t)p * ld + c];
+    red[sl][cl] = s;
+    __syncthreads();
+    if (sl == 0 && c < na + nb) {
+        float t = red[0][cl];
+#pragma unroll
+        for (int k = 1; k < 16; ++k) t += red[k][cl];
+        float* o = c < na ? out_a + c : out_b + (c - na);
+        *o = accumulate ? *o + t : t;
+    }
 }
 hipError_t colsum_finish2(const float* part, int part_rows, int ld, float* out_a, int na, float* out_b, int nb,
                           int accumulate, hipStream_t s) {
     if (na + nb == 0) return hipSuccess;
-    hipLaunchKernelGGL(colsum_kernel, dim3(nblk(na + nb, 256)), dim3(256), 0, s, part, part_rows, ld, out_a, na,
+    hipLaunchKernelGGL(colsum_kernel, dim3(nblk(na + nb, 64)), dim3(1024), 0, s, part, part_rows, ld, out_a, na,
                        out_b, nb, accumulate);
     return hipGetLastError();
 }
 
-// bias gradient: column sums of dY [rows, N] (act) over 64-row slabs, then finish
+// bias gradient: column sums of dY [rows, N] (act). Vector path (N % 8 == 0):
+// 64 columns x 256 rows per block, 8-column chunks per thread, 32 row lanes
+// combined in a fixed order; then the partial rows are summed in order.
+__device__ __forceinline__ void ld8act(const bf16_t* p, float (&o)[8]) {
+    const uint4 u = *(const uint4*)p;
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        o[2 * k] = bf2f((bf16_t)(w[k] & 0xffffu));
+        o[2 * k + 1] = bf2f((bf16_t)(w[k] >> 16));
+    }
+}
+__device__ __forceinline__ void ld8act(const float* p, float (&o)[8]) {
+    const float4 a = *(const float4*)p, b = *(const float4*)(p + 4);
+    o[0] = a.x; o[1] = a.y; o[2] = a.z; o[3] = a.w; o[4] = b.x; o[5] = b.y; o[6] = b.z; o[7] = b.w;
+}
+
+template <class T>
+__global__ __launch_bounds__(256) void colpart8_kernel(const T* dY, int64_t rows, int N, int rps, float* part) {
+    __shared__ float red[32][65];
+    const int t = threadIdx.x, ch = t & 7, rl = t >> 3;
+    const int col = blockIdx.x * 64 + ch * 8;
+    const int64_t r0 = (int64_t)blockIdx.y * rps;
+    const int64_t r1 = min(rows, r0 + rps);
+    float acc[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) acc[k] = 0.0f;
+    if (col < N) {
+        for (int64_t r = r0 + rl; r < r1; r += 32) {
+            float v[8];
+            ld8act(dY + r * N + col, v);
+#pragma unroll
+            for (int k = 0; k < 8; ++k) acc[k] += v[k];
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) red[rl][ch * 8 + k] = acc[k];
+    __syncthreads();
+    if (t < 64) {
+        const int c = blockIdx.x * 64 + t;
+        if (c < N) {
+            float s = red[0][t];
+            for (int k = 1; k < 32; ++k) s += red[k][t];
+            part[(int64_t)blockIdx.y * N + c] = s;
+        }
+    }
+}
+
 template <class T>
 __global__ void colpart_kernel(const T* dY, int64_t rows, int N, float* part) {
     const int c = blockIdx.x * blockDim.x + threadIdx.x;
@@ -349,9 +600,22 @@ __global__ void colpart_kernel(const T* dY, int64_t rows, int N, float* part) {
 hipError_t bias_grad(int dtype, const void* dY, int64_t rows, int N, float* part, int part_rows, float* db,
                      int accumulate, hipStream_t s) {
     if (N == 0) return hipSuccess;
+    if (rows == 0) return colsum_finish2(part, 0, N, db, N, nullptr, 0, accumulate, s);
+    if (N % 8 == 0) {
+        const int rps = 256;
+        const int pr = (int)((rows + rps - 1) / rps);
+        if (pr > part_rows) return hipErrorInvalidValue;
+        dim3 grid(nblk(N, 64), pr);
+        if (dtype == GPT2_DTYPE_BF16)
+            hipLaunchKernelGGL(colpart8_kernel<bf16_t>, grid, dim3(256), 0, s, (const bf16_t*)dY, rows, N, rps, part);
+        else
+            hipLaunchKernelGGL(colpart8_kernel<float>, grid, dim3(256), 0, s, (const float*)dY, rows, N, rps, part);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        return colsum_finish2(part, pr, N, db, N, nullptr, 0, accumulate, s);
+    }
     const int pr = (int)((rows + 63) / 64);
     if (pr > part_rows) return hipErrorInvalidValue;
-    if (pr == 0) return colsum_finish2(part, 0, N, db, N, nullptr, 0, accumulate, s);
     dim3 grid(nblk(N, 256), pr);
     if (dtype == GPT2_DTYPE_BF16)
         hipLaunchKernelGGL(colpart_kernel<bf16_t>, grid, dim3(256), 0, s, (const bf16_t*)dY, rows, N, part);
@@ -428,9 +692,135 @@ __global__ __launch_bounds__(256) void ce_kernel(T* logits, int64_t rows, int V,
     }
 }
 
+// Single HBM pass for bf16 logits: a 512-thread block holds its whole row in
+// registers (KC 16-byte chunks per thread), reduces max/argmax, then sum of
+// exp(z - max), and overwrites the row with softmax - onehot from registers.
+template <int KC>
+__global__ __launch_bounds__(512) void ce_reg_kernel(bf16_t* logits, int64_t rows, int V, int ld,
+                                                     const int32_t* targets, float* loss_rows, int32_t* argmax,
+                                                     int write_grad, uint32_t* status) {
+    __shared__ float sv[8], ss[8];
+    __shared__ int si[8];
+    const int64_t row = blockIdx.x;
+    bf16_t* z = logits + row * ld;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int nch = ld / 8;
+    uint4 r[KC];
+#pragma unroll
+    for (int k = 0; k < KC; ++k) {
+        const int c = tid + 512 * k;
+        r[k] = c < nch ? ((const uint4*)z)[c] : make_uint4(0, 0, 0, 0);
+    }
+    // max and argmax (lowest column among equal maxima)
+    float bv = -INFINITY;
+    int bi = 0x7fffffff;
+#pragma unroll
+    for (int k = 0; k < KC; ++k) {
+        const int c = tid + 512 * k;
+        if (c < nch) {
+            float v[8];
+            unpack8f(r[k], v);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int col = 8 * c + e;
+                if (col < V && v[e] > bv) { bv = v[e]; bi = col; }
+            }
+        }
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        const float v2 = __shfl_xor(bv, o, 64);
+        const int i2 = __shfl_xor(bi, o, 64);
+        if (v2 > bv || (v2 == bv && i2 < bi)) { bv = v2; bi = i2; }
+    }
+    if (lane == 0) { sv[wave] = bv; si[wave] = bi; }
+    __syncthreads();
+    bv = sv[0]; bi = si[0];
+#pragma unroll
+    for (int w = 1; w < 8; ++w)
+        if (sv[w] > bv || (sv[w] == bv && si[w] < bi)) { bv = sv[w]; bi = si[w]; }
+    const float mx = bv;
+    float sum = 0.0f;
+#pragma unroll
+    for (int k = 0; k < KC; ++k) {
+        const int c = tid + 512 * k;
+        if (c < nch) {
+            float v[8];
+            unpack8f(r[k], v);
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                if (8 * c + e < V) sum += __expf(v[e] - mx);
+        }
+    }
+    sum = wave_sum(sum);
+    if (lane == 0) ss[wave] = sum;
+    __syncthreads();
+    sum = ((ss[0] + ss[1]) + (ss[2] + ss[3])) + ((ss[4] + ss[5]) + (ss[6] + ss[7]));
+    const float lse = mx + logf(sum);
+    int tgt = targets ? targets[row] : -1;
+    if (targets && (tgt < 0 || tgt >= V)) {
+        if (tid == 0) atomicOr(status, (uint32_t)GPT2_STATUS_TOKEN_RANGE);
+        tgt = -1;
+    }
+    if (tid == 0) {
+        if (argmax) argmax[row] = bi;
+        if (loss_rows && tgt < 0) loss_rows[row] = 0.0f;
+    }
+    if (tgt >= 0 && loss_rows) {
+        // the thread holding the target column reports the loss
+        const int c = tgt / 8;
+        if (c % 512 == tid) {
+#pragma unroll
+            for (int k = 0; k < KC; ++k)
+                if (k == c / 512) {  // constant register index after unrolling
+                    float v[8];
+                    unpack8f(r[k], v);
+                    float zt = v[0];
+#pragma unroll
+                    for (int e = 1; e < 8; ++e)
+                        if (e == tgt % 8) zt = v[e];
+                    loss_rows[row] = lse - zt;
+                }
+        }
+    }
+    if (!write_grad) return;
+#pragma unroll
+    for (int k = 0; k < KC; ++k) {
+        const int c = tid + 512 * k;
+        if (c < nch) {
+            float v[8], o[8];
+            unpack8f(r[k], v);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int col = 8 * c + e;
+                o[e] = col < V ? __expf(v[e] - lse) - (col == tgt ? 1.0f : 0.0f) : 0.0f;
+            }
+            uint4 u;
+            u.x = (uint32_t)f2bf(o[0]) | ((uint32_t)f2bf(o[1]) << 16);
+            u.y = (uint32_t)f2bf(o[2]) | ((uint32_t)f2bf(o[3]) << 16);
+            u.z = (uint32_t)f2bf(o[4]) | ((uint32_t)f2bf(o[5]) << 16);
+            u.w = (uint32_t)f2bf(o[6]) | ((uint32_t)f2bf(o[7]) << 16);
+            ((uint4*)z)[c] = u;
+        }
+    }
+}
+
 hipError_t cross_entropy(int dtype, void* logits, int64_t rows, int V, int ld, const int32_t* targets,
                          float* loss_rows, int32_t* argmax, int write_grad, uint32_t* status, hipStream_t s) {
     if (rows == 0) return hipSuccess;
+    if (dtype == GPT2_DTYPE_BF16 && ld % 8 == 0) {
+        const int kc = (ld / 8 + 511) / 512;
+#define G2_CE(K)                                                                                             \
+    hipLaunchKernelGGL(ce_reg_kernel<K>, dim3((unsigned)rows), dim3(512), 0, s, (bf16_t*)logits, rows, V, ld, \
+                       targets, loss_rows, argmax, write_grad, status)
+        if (kc <= 1) { G2_CE(1); return hipGetLastError(); }
+        if (kc <= 2) { G2_CE(2); return hipGetLastError(); }
+        if (kc <= 4) { G2_CE(4); return hipGetLastError(); }
+        if (kc <= 8) { G2_CE(8); return hipGetLastError(); }
+        if (kc <= 13) { G2_CE(13); return hipGetLastError(); }
+        if (kc <= 16) { G2_CE(16); return hipGetLastError(); }
+#undef G2_CE
+    }
     if (dtype == GPT2_DTYPE_BF16)
         hipLaunchKernelGGL(ce_kernel<bf16_t>, dim3((unsigned)rows), dim3(256), 0, s, (bf16_t*)logits, rows, V, ld,
                            targets, loss_rows, argmax, write_grad, status);

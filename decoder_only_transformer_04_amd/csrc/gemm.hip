@@ -18,6 +18,13 @@
 
 #include "device.h"
 
+#ifndef G2_GEMM_PIPE
+#define G2_GEMM_PIPE 1
+#endif
+#ifndef G2_GEMM_IGLP
+#define G2_GEMM_IGLP -1
+#endif
+
 namespace g2 {
 
 struct GP {
@@ -60,6 +67,77 @@ __device__ __forceinline__ void epi_apply(const GP& p, int64_t m, int n, float v
     } else if constexpr (EPI == EPI_GELU_BWD) {
         float u = Act<T>::ld((const T*)p.R, m * p.ldr + n);
         Act<T>::st((T*)p.C, m * p.ldc + n, v * gelu_tanh_grad(u));
+    }
+}
+
+// Eight consecutive columns n..n+7 of row m (n % 8 == 0, N % 8 == 0): vector
+// loads of bias / residual / pre-activation and 16- or 32-byte stores.
+__device__ __forceinline__ uint4 pack8(const float (&o)[8]) {
+    uint4 r;
+    r.x = (uint32_t)f2bf(o[0]) | ((uint32_t)f2bf(o[1]) << 16);
+    r.y = (uint32_t)f2bf(o[2]) | ((uint32_t)f2bf(o[3]) << 16);
+    r.z = (uint32_t)f2bf(o[4]) | ((uint32_t)f2bf(o[5]) << 16);
+    r.w = (uint32_t)f2bf(o[6]) | ((uint32_t)f2bf(o[7]) << 16);
+    return r;
+}
+__device__ __forceinline__ void unpack8(uint4 u, float (&o)[8]) {
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        o[2 * k] = bf2f((bf16_t)(w[k] & 0xffffu));
+        o[2 * k + 1] = bf2f((bf16_t)(w[k] >> 16));
+    }
+}
+__device__ __forceinline__ void ld8f(const float* p, float (&o)[8]) {
+    const float4 a = *(const float4*)p, b = *(const float4*)(p + 4);
+    o[0] = a.x; o[1] = a.y; o[2] = a.z; o[3] = a.w; o[4] = b.x; o[5] = b.y; o[6] = b.z; o[7] = b.w;
+}
+__device__ __forceinline__ void st8f(float* p, const float (&o)[8]) {
+    *(float4*)p = make_float4(o[0], o[1], o[2], o[3]);
+    *(float4*)(p + 4) = make_float4(o[4], o[5], o[6], o[7]);
+}
+
+template <int EPI>
+__device__ __forceinline__ void epi_apply8(const GP& p, int64_t m, int n, const float (&v)[8]) {
+    float bv[8];
+    if (p.bias) ld8f(p.bias + n, bv);
+    else {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) bv[k] = 0.0f;
+    }
+    float o[8];
+    if constexpr (EPI == EPI_STORE) {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) o[k] = p.alpha * v[k] + bv[k];
+        *(uint4*)((bf16_t*)p.C + m * p.ldc + n) = pack8(o);
+    } else if constexpr (EPI == EPI_GELU) {
+        float gl[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            o[k] = v[k] + bv[k];
+            gl[k] = gelu_tanh(o[k]);
+        }
+        *(uint4*)((bf16_t*)p.C + m * p.ldc + n) = pack8(o);
+        *(uint4*)((bf16_t*)p.C2 + m * p.ldc2 + n) = pack8(gl);
+    } else if constexpr (EPI == EPI_RESID) {
+        float r[8];
+        ld8f((const float*)p.R + m * p.ldr + n, r);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) o[k] = r[k] + v[k] + bv[k];
+        st8f((float*)p.C + m * p.ldc + n, o);
+    } else if constexpr (EPI == EPI_F32) {
+        float* c = (float*)p.C + (int64_t)blockIdx.z * p.c_split_stride + m * p.ldc + n;
+        float prev[8];
+        if (p.accumulate) ld8f(c, prev);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) o[k] = p.alpha * v[k] + (p.accumulate ? prev[k] : 0.0f);
+        st8f(c, o);
+    } else if constexpr (EPI == EPI_GELU_BWD) {
+        float u[8];
+        unpack8(*(const uint4*)((const bf16_t*)p.R + m * p.ldr + n), u);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) o[k] = v[k] * gelu_tanh_grad(u[k]);
+        *(uint4*)((bf16_t*)p.C + m * p.ldc + n) = pack8(o);
     }
 }
 
@@ -174,6 +252,33 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GP p) {
             tile_gload<BM, AKC>(ra, A, p.lda, m0, p.M, kn, kend, tid);
             tile_gload<BN, BKC>(rb, B, p.ldb, n0, p.N, kn, kend, tid);
         }
+#if G2_GEMM_IGLP >= 0
+        __builtin_amdgcn_iglp_opt(G2_GEMM_IGLP);
+#endif
+#if G2_GEMM_PIPE
+        // fragments of step kk+1 are read from LDS while step kk's MFMAs run
+        bf16x8 af[2][FM], bv[2][FN];
+#pragma unroll
+        for (int i = 0; i < FM; ++i) af[0][i] = tile_frag<BM, AKC>(cur, wm * WM + i * 32, 0, lane);
+#pragma unroll
+        for (int j = 0; j < FN; ++j) bv[0][j] = tile_frag<BN, BKC>(cur + ABYTES, wn * WN + j * 32, 0, lane);
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            const int c = kk & 1;
+            if (kk < 3) {
+#pragma unroll
+                for (int i = 0; i < FM; ++i) af[c ^ 1][i] = tile_frag<BM, AKC>(cur, wm * WM + i * 32, kk + 1, lane);
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
+                    bv[c ^ 1][j] = tile_frag<BN, BKC>(cur + ABYTES, wn * WN + j * 32, kk + 1, lane);
+            }
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[c][i], bv[c][j], acc[i][j], 0, 0, 0);
+        }
+#else
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
             bf16x8 af[FM], bv[FN];
@@ -187,6 +292,7 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GP p) {
                 for (int j = 0; j < FN; ++j)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bv[j], acc[i][j], 0, 0, 0);
         }
+#endif
         if (more) {
             char* nxt = smem + ((kt + 1) & 1) * STAGE;
             tile_sstore<BM, AKC>(nxt, ra, tid);
@@ -194,17 +300,35 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GP p) {
         }
         __syncthreads();
     }
-    // accumulator (i, j, r) of lane l sits at row 8 (r/4) + 4 (l/32) + r%4, column l%32
+    // Epilogue: each wave stages one 32-row strip of its tile at a time through
+    // LDS (reusing the main-loop buffers) so that lanes then own 8 consecutive
+    // columns of a row. Accumulator (i, j, r) of lane l sits at row
+    // 8 (r/4) + 4 (l/32) + r%4 and column l%32 of fragment (i, j).
+    constexpr int SP = WN + 4;          // staged floats per row (padding spreads banks)
+    constexpr int LPR = WN / 8;         // lanes per staged row
+    constexpr int RPP = 64 / LPR;       // rows per pass
+    static_assert(4 * 32 * SP * 4 <= 2 * STAGE, "epilogue staging exceeds the LDS buffers");
+    float* st = (float*)smem + wave * 32 * SP;
 #pragma unroll
-    for (int i = 0; i < FM; ++i)
+    for (int i = 0; i < FM; ++i) {
 #pragma unroll
         for (int j = 0; j < FN; ++j)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int64_t m = m0 + wm * WM + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-                const int n = n0 + wn * WN + j * 32 + (lane & 31);
-                if (m < p.M && n < p.N) epi_apply<EPI, bf16_t>(p, m, n, acc[i][j][r]);
-            }
+            for (int r = 0; r < 16; ++r)
+                st[(8 * (r >> 2) + 4 * (lane >> 5) + (r & 3)) * SP + j * 32 + (lane & 31)] = acc[i][j][r];
+        __syncthreads();
+#pragma unroll
+        for (int pass = 0; pass < 32 / RPP; ++pass) {
+            const int rr = pass * RPP + lane / LPR;
+            const int cc = (lane % LPR) * 8;
+            float v[8];
+            ld8f(st + rr * SP + cc, v);
+            const int64_t m = m0 + wm * WM + i * 32 + rr;
+            const int n = n0 + wn * WN + cc;
+            if (m < p.M && n < p.N) epi_apply8<EPI>(p, m, n, v);
+        }
+        __syncthreads();
+    }
 }
 
 // ------------------------------------------------------------------ fp32 kernel

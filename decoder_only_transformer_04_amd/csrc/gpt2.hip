@@ -364,7 +364,7 @@ int gpt2_backward(gpt2_ctx* x, float loss_scale, int32_t zero_grads) {
                         sbytes));
     G2_T("ln.bwd", layernorm_bwd(dt, dtmp, at<float>(x, ap.xL), at<float>(x, ap.mf), at<float>(x, ap.rf), pf(x, pl.lnf_g),
                          dres, bf ? dres_act : nullptr, part, ap.ln_part_rows, M, C, 0, s));
-    G2_T("colsum", colsum_finish2(part, (M + 63) / 64, 2 * C, gf(x, pl.lnf_g), C, gf(x, pl.lnf_b), C, acc, s));
+    G2_T("colsum", colsum_finish2(part, ln_bwd_partial_rows(M), 2 * C, gf(x, pl.lnf_g), C, gf(x, pl.lnf_b), C, acc, s));
     for (int l = c.n_layer - 1; l >= 0; --l) {
         const LayerW& w = pl.layer[l];
         // x_out = x_mid + fc2(gelu(fc(ln2(x_mid))))
@@ -378,7 +378,7 @@ int gpt2_backward(gpt2_ctx* x, float loss_scale, int32_t zero_grads) {
         if (w.b_fc >= 0) G2_T("bias", bias_grad(dt, at<char>(x, ap.dF), M, F, bpart, ap.bias_part_rows, gf(x, w.b_fc), acc, s));
         G2_T("ln.bwd", layernorm_bwd(dt, dtmp, at<float>(x, ap.xmid[l]), at<float>(x, ap.m2[l]), at<float>(x, ap.r2[l]),
                              pf(x, w.ln2_g), dres, bf ? dres_act : nullptr, part, ap.ln_part_rows, M, C, 1, s));
-        G2_T("colsum", colsum_finish2(part, (M + 63) / 64, 2 * C, gf(x, w.ln2_g), C, gf(x, w.ln2_b), C, acc, s));
+        G2_T("colsum", colsum_finish2(part, ln_bwd_partial_rows(M), 2 * C, gf(x, w.ln2_g), C, gf(x, w.ln2_b), C, acc, s));
         // x_mid = x_in + proj(attn(ln1(x_in)))
         G2_T("gemm.dgrad.proj", linear_dgrad(dt, s, EPI_STORE, M, C, C, dres_act, C, wptr(x, w.w_proj), at<char>(x, ap.datt), nullptr,
                             1.0f));
@@ -395,13 +395,14 @@ int gpt2_backward(gpt2_ctx* x, float loss_scale, int32_t zero_grads) {
             G2_T("bias", bias_grad(dt, at<char>(x, ap.dqkv), M, 3 * C, bpart, ap.bias_part_rows, gf(x, w.b_qkv), acc, s));
         G2_T("ln.bwd", layernorm_bwd(dt, dtmp, at<float>(x, ap.x[l]), at<float>(x, ap.m1[l]), at<float>(x, ap.r1[l]),
                              pf(x, w.ln1_g), dres, bf ? dres_act : nullptr, part, ap.ln_part_rows, M, C, 1, s));
-        G2_T("colsum", colsum_finish2(part, (M + 63) / 64, 2 * C, gf(x, w.ln1_g), C, gf(x, w.ln1_b), C, acc, s));
+        G2_T("colsum", colsum_finish2(part, ln_bwd_partial_rows(M), 2 * C, gf(x, w.ln1_g), C, gf(x, w.ln1_b), C, acc, s));
     }
     // embedding: dwte[idx[m]] += dres[m] (after the head's contribution), dwpe[t] (=|+=) sum_b dres[b,t]
     G2_T("embed.bwd", encoder_bwd(at<int32_t>(x, x->idx_save), dres, gf(x, pl.wte), gf(x, pl.wpe), M, T, C, c.vocab,
-                       at<int32_t>(x, ap.enc_count), at<int32_t>(x, ap.enc_start), at<int32_t>(x, ap.enc_rank),
-                       at<int32_t>(x, ap.enc_order), at<int32_t>(x, ap.enc_distinct),
-                       at<int32_t>(x, ap.scalars) + SLOT_NDISTINCT, acc, s));
+                                  at<int32_t>(x, ap.enc_count), at<int32_t>(x, ap.enc_start),
+                                  at<int32_t>(x, ap.enc_segstart), at<int32_t>(x, ap.enc_order),
+                                  at<int32_t>(x, ap.enc_segtok), at<int32_t>(x, ap.scalars) + SLOT_NSEG, dtmp,
+                                  acc, s));
     return GPT2_OK;
 }
 
@@ -558,11 +559,11 @@ int gpt2_op_layernorm_bwd(int64_t rows, int32_t C, const float* d_dy, const floa
     if (rows < 0 || C < 1 || C > 1024 || !d_dy || !d_x || !d_mean || !d_rstd || !d_g || !d_dx || !d_dg || !d_db)
         return GPT2_EINVAL;
     hipStream_t s = (hipStream_t)hip_stream;
-    const int pr = (int)std::max<int64_t>(1, (rows + 63) / 64);
+    const int pr = std::max(1, ln_bwd_partial_rows(rows));
     float* tmp = nullptr;
     if (hipMallocAsync((void**)&tmp, (size_t)pr * 2 * C * 4, s) != hipSuccess) return GPT2_EHIP;
     hipError_t e = layernorm_bwd(GPT2_DTYPE_F32, d_dy, d_x, d_mean, d_rstd, d_g, d_dx, nullptr, tmp, pr, rows, C, 1, s);
-    if (e == hipSuccess) e = colsum_finish2(tmp, (int)((rows + 63) / 64), 2 * C, d_dg, C, d_db, C, 0, s);
+    if (e == hipSuccess) e = colsum_finish2(tmp, ln_bwd_partial_rows(rows), 2 * C, d_dg, C, d_db, C, 0, s);
     (void)hipFreeAsync(tmp, s);
     return e == hipSuccess ? GPT2_OK : GPT2_EHIP;
 }

@@ -133,16 +133,16 @@ ArenaPlan make_arena_plan(const gpt2_config& c, const ParamLayout& pl, int B, in
         a.dqkv = take(M * 3 * C * ab);
         a.datt = take(M * C * ab);
         a.attD = take((size_t)B * H * T * 4);
-        a.ln_part_rows = (int)((M + 63) / 64);
+        a.ln_part_rows = (int)((M + 15) / 16);
         a.ln_part = take((size_t)a.ln_part_rows * 2 * C * 4);
         size_t maxN = 3 * C > F ? 3 * C : F;
         a.bias_part_rows = (int)((M + 63) / 64);
         a.bias_part = take((size_t)a.bias_part_rows * maxN * 4);
         a.enc_count = take(Vp * 4);
         a.enc_start = take(Vp * 4);
-        a.enc_rank = take(M * 4);
+        a.enc_segstart = take(Vp * 4);
         a.enc_order = take(M * 4);
-        a.enc_distinct = take(M * 4);
+        a.enc_segtok = take(M * 4);
     }
     a.total = off;
     return a;
