@@ -18,9 +18,6 @@
 
 #include "device.h"
 
-#ifndef G2_GEMM_PIPE
-#define G2_GEMM_PIPE 1
-#endif
 #ifndef G2_GEMM_IGLP
 #define G2_GEMM_IGLP -1
 #endif
@@ -142,31 +139,47 @@ __device__ __forceinline__ void epi_apply8(const GP& p, int64_t m, int n, const 
 }
 
 // ------------------------------------------------------------------ bf16 MFMA kernel
-template <int R, bool KC>
+template <int R, bool KC, int BK = 64>
 struct TileCfg {
-    static constexpr int BYTES = KC ? R * 128 : 64 * (R + 32) * 2;
-    static constexpr int CHUNKS = R / 32;  // 16-byte chunks per thread per 64-deep stage
-    static constexpr int PITCH = (R + 32) * 2;  // bytes per k row, transposed staging
+    static constexpr int BYTES = R * BK * 2;
+    static constexpr int CHUNKS = BYTES / 16 / 256;  // 16-byte chunks per thread per stage
+    static constexpr int PITCH = KC ? BK * 2 : R * 2;  // bytes per tile row
+    static constexpr int CPR = PITCH / 16;           // 16-byte chunks per tile row
 };
 
-// Global -> registers for one 64-deep stage. KC: tile rows r0.. (< rmax), k in
-// [k0, kmax); not KC: k rows k0.. (< kmax), contiguous rows r0.. (< rmax).
-// kmax (KC) and rmax (not KC) are multiples of 8, so a 16-byte chunk is either
-// wholly in bounds or wholly zero-filled.
-template <int R, bool KC>
-__device__ __forceinline__ void tile_gload(uint4 (&regs)[R / 32], const bf16_t* base, int64_t ld,
-                                           int64_t r0, int64_t rmax, int k0, int kmax, int tid) {
+// LDS placement of 16-byte chunk `ch` of tile row `row`.
+// KC tiles ([R][BK k]): the chunk index is XOR-ed with a function of the row so
+// that the 128-bit fragment reads (16 consecutive rows, one chunk) hit 16
+// distinct 16-byte bank groups. Transposed tiles ([BK k][R]): chunk ^ 4 (row mod 4)
+// keeps the transpose reads (4 consecutive rows, 4 consecutive chunks) conflict-free.
+template <int R, bool KC, int BK = 64>
+__device__ __forceinline__ int slot_of(int row, int ch) {
+    if constexpr (KC) {
+        if constexpr (BK == 64) return row * 8 + (ch ^ ((row >> 1) & 7));
+        else return row * 4 + (ch ^ ((row >> 2) & 3));
+    } else {
+        return row * (R / 8) + (ch ^ (4 * (row & 3)));
+    }
+}
+
+// Global -> registers for one BK-deep stage, zero-filling out-of-range chunks.
+// KC: tile rows r0.. (< rmax), k in [k0, kmax); not KC: k rows k0.. (< kmax),
+// contiguous rows r0.. (< rmax). kmax (KC) and rmax (not KC) are multiples of
+// 8, so a 16-byte chunk is either wholly in bounds or wholly zero-filled.
+template <int R, bool KC, int BK>
+__device__ __forceinline__ void tile_gload(uint4 (&regs)[R * BK / 2048], const bf16_t* base,
+                                           int64_t ld, int64_t r0, int64_t rmax, int k0, int kmax, int tid) {
+    constexpr int CPR = TileCfg<R, KC, BK>::CPR;
 #pragma unroll
-    for (int i = 0; i < TileCfg<R, KC>::CHUNKS; ++i) {
+    for (int i = 0; i < TileCfg<R, KC, BK>::CHUNKS; ++i) {
         const int c = tid + 256 * i;
         uint4 v = make_uint4(0, 0, 0, 0);
         if constexpr (KC) {
-            const int row = c >> 3;
-            const int k = k0 + (c & 7) * 8;
+            const int row = c / CPR;
+            const int k = k0 + (c % CPR) * 8;
             const int64_t gr = r0 + row;
             if (gr < rmax && k < kmax) v = *(const uint4*)(base + gr * ld + k);
         } else {
-            constexpr int CPR = R / 8;
             const int k = k0 + c / CPR;
             const int64_t gr = r0 + (c % CPR) * 8;
             if (k < kmax && gr < rmax) v = *(const uint4*)(base + (int64_t)k * ld + gr);
@@ -175,48 +188,117 @@ __device__ __forceinline__ void tile_gload(uint4 (&regs)[R / 32], const bf16_t* 
     }
 }
 
-template <int R, bool KC>
-__device__ __forceinline__ void tile_sstore(char* lds, const uint4 (&regs)[R / 32], int tid) {
+template <int R, bool KC, int BK>
+__device__ __forceinline__ void tile_sstore(char* lds, const uint4 (&regs)[R * BK / 2048], int tid) {
+    constexpr int CPR = TileCfg<R, KC, BK>::CPR;
 #pragma unroll
-    for (int i = 0; i < TileCfg<R, KC>::CHUNKS; ++i) {
+    for (int i = 0; i < TileCfg<R, KC, BK>::CHUNKS; ++i) {
         const int c = tid + 256 * i;
-        int off;
-        if constexpr (KC) {
-            const int row = c >> 3, ch = c & 7;
-            off = row * 128 + ((ch ^ ((row >> 1) & 7)) << 4);
-        } else {
-            constexpr int CPR = R / 8;
-            off = (c / CPR) * TileCfg<R, KC>::PITCH + (c % CPR) * 16;
-        }
-        *(uint4*)(lds + off) = regs[i];
+        *(uint4*)(lds + 16 * slot_of<R, KC, BK>(c / CPR, c % CPR)) = regs[i];
     }
 }
 
+// Direct global -> LDS for whole 64-deep stages (gfx950 global_load_lds_dwordx4):
+// each wave instruction fills 1 KB of LDS, lane i at +16 i, so every lane
+// fetches the global chunk that belongs at its slot. The per-lane source
+// pointers are computed once per tile and advanced by one stage per issue.
+// Rows past rmax are clamped to valid memory (their products land only in
+// discarded output rows or columns); a stage that would cross the end of K
+// takes the register path instead, which zero-fills the tail.
+template <int R, bool KC, int BK>
+struct DmaPlan {
+    static constexpr int NI = TileCfg<R, KC, BK>::BYTES / 4096;  // 1 KB instructions per wave
+    static constexpr int CPR = TileCfg<R, KC, BK>::CPR;
+    const bf16_t* src[NI];
+    int64_t step;
+    __device__ __forceinline__ void init(const bf16_t* base, int64_t ld, int64_t r0, int64_t rmax, int k0, int wave,
+                                         int lane) {
+        step = KC ? BK : (int64_t)BK * ld;
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+            const int slot = (wave * NI + i) * 64 + lane;
+            const int row = slot / CPR;
+            // the logical chunk whose swizzled position is this slot (XOR is an involution)
+            const int ch = slot_of<R, KC, BK>(row, slot % CPR) - row * CPR;
+            if constexpr (KC) {
+                const int64_t gr = min(r0 + row, rmax - 1);
+                src[i] = base + gr * ld + k0 + 8 * ch;
+            } else {
+                const int64_t gc = min(r0 + 8 * ch, rmax - 8);
+                src[i] = base + (int64_t)(k0 + row) * ld + gc;
+            }
+        }
+    }
+    // load the current stage into `lds` and move to the next stage
+    __device__ __forceinline__ void issue(char* lds, int wave) {
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+#if defined(__HIP_DEVICE_COMPILE__)
+            __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src[i],
+                                             (G2_LDS void*)(lds + (wave * NI + i) * 1024), 16, 0, 0);
+#endif
+            src[i] += step;
+        }
+    }
+    __device__ __forceinline__ void skip() {
+#pragma unroll
+        for (int i = 0; i < NI; ++i) src[i] += step;
+    }
+};
+
 // MFMA operand fragment: lane l holds rows rb + (l & 31), k = 16 kk + 8 (l >> 5) + 0..7.
-template <int R, bool KC>
+template <int R, bool KC, int BK>
 __device__ __forceinline__ bf16x8 tile_frag(const char* lds, int rb, int kk, int lane) {
     if constexpr (KC) {
         const int row = rb + (lane & 31);
         const int ch = kk * 2 + (lane >> 5);
-        return *(const bf16x8*)(lds + row * 128 + ((ch ^ ((row >> 1) & 7)) << 4));
+        return *(const bf16x8*)(lds + 16 * slot_of<R, KC, BK>(row, ch));
     } else {
         // each 16-lane group reads a 4 (k) x 16 (rows) block; lane i of the group
         // receives the 4 k-values of row i
         const int g = lane >> 4, j = lane & 15;
         const int k = kk * 16 + 8 * (g >> 1) + (j >> 2);
         const int r = rb + 16 * (g & 1) + 4 * (j & 3);
-        const char* p0 = lds + k * TileCfg<R, KC>::PITCH + r * 2;
-        return lds_tr_pair(p0, 4 * TileCfg<R, KC>::PITCH);
+        // rows k and k + 4 share the swizzle (it depends on k mod 4)
+        const char* p0 = lds + 16 * slot_of<R, KC, BK>(k, r >> 3) + (r & 7) * 2;
+        return lds_tr_pair(p0, 4 * TileCfg<R, KC, BK>::PITCH);
     }
 }
 
-template <int BM, int BN, bool AKC, bool BKC, int EPI>
+// One BK-deep stage from LDS: BK/16 steps of 16, every wave multiplying its
+// FM x FN grid of 32x32 fragments.
+template <int BM, int BN, bool AKC, bool BKC, int BK, int FM, int FN>
+__device__ __forceinline__ void mma_stage(const char* cur, f32x16 (&acc)[FM][FN], int wm, int wn, int lane) {
+    constexpr int ABYTES = TileCfg<BM, AKC, BK>::BYTES;
+    constexpr int WM = BM / 2, WN = BN / 2;
+#if G2_GEMM_IGLP >= 0
+    __builtin_amdgcn_iglp_opt(G2_GEMM_IGLP);
+#endif
+#pragma unroll
+    for (int kk = 0; kk < BK / 16; ++kk) {
+        bf16x8 af[FM], bv[FN];
+#pragma unroll
+        for (int i = 0; i < FM; ++i) af[i] = tile_frag<BM, AKC, BK>(cur, wm * WM + i * 32, kk, lane);
+#pragma unroll
+        for (int j = 0; j < FN; ++j) bv[j] = tile_frag<BN, BKC, BK>(cur + ABYTES, wn * WN + j * 32, kk, lane);
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bv[j], acc[i][j], 0, 0, 0);
+    }
+}
+
+template <int BM, int BN, int BK, bool AKC, bool BKC, int EPI>
 __global__ __launch_bounds__(256) void gemm_bf16_kernel(GP p) {
-    constexpr int ABYTES = TileCfg<BM, AKC>::BYTES;
-    constexpr int BBYTES = TileCfg<BN, BKC>::BYTES;
+    constexpr int ABYTES = TileCfg<BM, AKC, BK>::BYTES;
+    constexpr int BBYTES = TileCfg<BN, BKC, BK>::BYTES;
     constexpr int STAGE = ABYTES + BBYTES;
     constexpr int WM = BM / 2, WN = BN / 2, FM = WM / 32, FN = WN / 32;
-    __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
+    constexpr int SP = WN + 4;  // epilogue: staged floats per row (padding spreads banks)
+    constexpr int EPI_BYTES = 4 * 32 * SP * 4;
+    constexpr int SMEM = 2 * STAGE > EPI_BYTES ? 2 * STAGE : EPI_BYTES;
+    __shared__ __attribute__((aligned(16))) char smem[SMEM];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1;
@@ -224,7 +306,7 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GP p) {
     const int n0 = blockIdx.x * BN;
     const int kbeg = blockIdx.z * p.k_per_split;
     const int kend = min(p.K, kbeg + p.k_per_split);
-    const int nk = (kend - kbeg + 63) / 64;
+    const int nk = (kend - kbeg + BK - 1) / BK;
     const bf16_t* A = (const bf16_t*)p.A;
     const bf16_t* B = (const bf16_t*)p.B;
 
@@ -236,78 +318,44 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GP p) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-    uint4 ra[TileCfg<BM, AKC>::CHUNKS], rb[TileCfg<BN, BKC>::CHUNKS];
-    if (nk > 0) {
-        tile_gload<BM, AKC>(ra, A, p.lda, m0, p.M, kbeg, kend, tid);
-        tile_gload<BN, BKC>(rb, B, p.ldb, n0, p.N, kbeg, kend, tid);
-        tile_sstore<BM, AKC>(smem, ra, tid);
-        tile_sstore<BN, BKC>(smem + ABYTES, rb, tid);
-    }
+    // Stage t+1 streams straight into the other LDS buffer (no staging
+    // registers) while stage t is multiplied out of LDS; a stage that would
+    // cross the end of K takes the register path, which zero-fills the tail.
+    DmaPlan<BM, AKC, BK> dA;
+    DmaPlan<BN, BKC, BK> dB;
+    dA.init(A, p.lda, m0, p.M, kbeg, wave, lane);
+    dB.init(B, p.ldb, n0, p.N, kbeg, wave, lane);
+    auto issue = [&](char* buf, int kt) {
+        const int k0 = kbeg + kt * BK;
+        if (k0 + BK <= kend) {
+            dA.issue(buf, wave);
+            dB.issue(buf + ABYTES, wave);
+        } else {
+            uint4 ra[TileCfg<BM, AKC, BK>::CHUNKS], rb[TileCfg<BN, BKC, BK>::CHUNKS];
+            tile_gload<BM, AKC, BK>(ra, A, p.lda, m0, p.M, k0, kend, tid);
+            tile_gload<BN, BKC, BK>(rb, B, p.ldb, n0, p.N, k0, kend, tid);
+            tile_sstore<BM, AKC, BK>(buf, ra, tid);
+            tile_sstore<BN, BKC, BK>(buf + ABYTES, rb, tid);
+            dA.skip();
+            dB.skip();
+        }
+    };
+    if (nk > 0) issue(smem, 0);
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     for (int kt = 0; kt < nk; ++kt) {
         char* cur = smem + (kt & 1) * STAGE;
-        const bool more = kt + 1 < nk;
-        if (more) {
-            const int kn = kbeg + (kt + 1) * 64;
-            tile_gload<BM, AKC>(ra, A, p.lda, m0, p.M, kn, kend, tid);
-            tile_gload<BN, BKC>(rb, B, p.ldb, n0, p.N, kn, kend, tid);
-        }
-#if G2_GEMM_IGLP >= 0
-        __builtin_amdgcn_iglp_opt(G2_GEMM_IGLP);
-#endif
-#if G2_GEMM_PIPE
-        // fragments of step kk+1 are read from LDS while step kk's MFMAs run
-        bf16x8 af[2][FM], bv[2][FN];
-#pragma unroll
-        for (int i = 0; i < FM; ++i) af[0][i] = tile_frag<BM, AKC>(cur, wm * WM + i * 32, 0, lane);
-#pragma unroll
-        for (int j = 0; j < FN; ++j) bv[0][j] = tile_frag<BN, BKC>(cur + ABYTES, wn * WN + j * 32, 0, lane);
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-            const int c = kk & 1;
-            if (kk < 3) {
-#pragma unroll
-                for (int i = 0; i < FM; ++i) af[c ^ 1][i] = tile_frag<BM, AKC>(cur, wm * WM + i * 32, kk + 1, lane);
-#pragma unroll
-                for (int j = 0; j < FN; ++j)
-                    bv[c ^ 1][j] = tile_frag<BN, BKC>(cur + ABYTES, wn * WN + j * 32, kk + 1, lane);
-            }
-#pragma unroll
-            for (int i = 0; i < FM; ++i)
-#pragma unroll
-                for (int j = 0; j < FN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[c][i], bv[c][j], acc[i][j], 0, 0, 0);
-        }
-#else
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-            bf16x8 af[FM], bv[FN];
-#pragma unroll
-            for (int i = 0; i < FM; ++i) af[i] = tile_frag<BM, AKC>(cur, wm * WM + i * 32, kk, lane);
-#pragma unroll
-            for (int j = 0; j < FN; ++j) bv[j] = tile_frag<BN, BKC>(cur + ABYTES, wn * WN + j * 32, kk, lane);
-#pragma unroll
-            for (int i = 0; i < FM; ++i)
-#pragma unroll
-                for (int j = 0; j < FN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bv[j], acc[i][j], 0, 0, 0);
-        }
-#endif
-        if (more) {
-            char* nxt = smem + ((kt + 1) & 1) * STAGE;
-            tile_sstore<BM, AKC>(nxt, ra, tid);
-            tile_sstore<BN, BKC>(nxt + ABYTES, rb, tid);
-        }
+        if (kt + 1 < nk) issue(smem + ((kt + 1) & 1) * STAGE, kt + 1);
+        mma_stage<BM, BN, AKC, BKC, BK, FM, FN>(cur, acc, wm, wn, lane);
+        __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
     }
     // Epilogue: each wave stages one 32-row strip of its tile at a time through
     // LDS (reusing the main-loop buffers) so that lanes then own 8 consecutive
     // columns of a row. Accumulator (i, j, r) of lane l sits at row
     // 8 (r/4) + 4 (l/32) + r%4 and column l%32 of fragment (i, j).
-    constexpr int SP = WN + 4;          // staged floats per row (padding spreads banks)
     constexpr int LPR = WN / 8;         // lanes per staged row
     constexpr int RPP = 64 / LPR;       // rows per pass
-    static_assert(4 * 32 * SP * 4 <= 2 * STAGE, "epilogue staging exceeds the LDS buffers");
     float* st = (float*)smem + wave * 32 * SP;
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
@@ -405,25 +453,33 @@ __global__ void splitk_reduce_kernel(const float* part, int splits, int64_t n, f
 }
 
 // ------------------------------------------------------------------ launchers
-template <int BM, int BN, bool AKC, bool BKC, int EPI>
+template <int BM, int BN, bool AKC, bool BKC, int EPI, int BK = 64>
 static hipError_t launch_bf16(const GP& p, int splits, hipStream_t s) {
     dim3 grid((p.N + BN - 1) / BN, (unsigned)((p.M + BM - 1) / BM), splits);
-    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, AKC, BKC, EPI>), grid, dim3(256), 0, s, p);
+    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, BK, AKC, BKC, EPI>), grid, dim3(256), 0, s, p);
     return hipGetLastError();
 }
 
 template <bool AKC, bool BKC, int EPI>
 static hipError_t pick_tile_bf16(const GP& p, int splits, hipStream_t s) {
-    // estimated time ~ rounds of 256 workgroups x tile area / relative efficiency
-    const int64_t t256 = ((p.M + 255) / 256) * ((p.N + 255) / 256) * splits;
-    const int64_t t25612 = ((p.M + 255) / 256) * ((p.N + 127) / 128) * splits;
-    const int64_t t128 = ((p.M + 127) / 128) * ((p.N + 127) / 128) * splits;
-    const double c256 = (double)((t256 + 255) / 256) * 65536 / 1.0;
-    const double c25612 = (double)((t25612 + 255) / 256) * 32768 / 0.85;
-    const double c128 = (double)((t128 + 255) / 256) * 16384 / 0.7;
-    if (c256 <= c25612 && c256 <= c128) return launch_bf16<256, 256, AKC, BKC, EPI>(p, splits, s);
-    if (c25612 <= c128) return launch_bf16<256, 128, AKC, BKC, EPI>(p, splits, s);
-    return launch_bf16<128, 128, AKC, BKC, EPI>(p, splits, s);
+#ifdef G2_FORCE_TILE  // tile experiments only
+    if (G2_FORCE_TILE == 0) return launch_bf16<256, 256, AKC, BKC, EPI>(p, splits, s);
+    if (G2_FORCE_TILE == 2) return launch_bf16<128, 128, AKC, BKC, EPI>(p, splits, s);
+    if (G2_FORCE_TILE == 3) return launch_bf16<128, 128, AKC, BKC, EPI, 32>(p, splits, s);
+    if (G2_FORCE_TILE == 4) return launch_bf16<256, 128, AKC, BKC, EPI, 32>(p, splits, s);
+#endif
+    // Tile policy from measurements on the 124M model's shapes: 128 x 128 tiles
+    // let two or three workgroups share a CU, which hides LDS and global latency
+    // better than one 256 x 256 workgroup. Products with K-contiguous operands
+    // (forward) and input gradients use 32-deep stages (32 KB of LDS, three
+    // workgroups per CU); the very wide vocabulary product uses 256 x 128; the
+    // weight gradients (two transposed operands, K = tokens) keep 64-deep stages.
+    if constexpr (!AKC) {
+        return launch_bf16<128, 128, AKC, BKC, EPI, 64>(p, splits, s);
+    } else {
+        if (BKC && p.N >= 8192) return launch_bf16<256, 128, AKC, BKC, EPI, 32>(p, splits, s);
+        return launch_bf16<128, 128, AKC, BKC, EPI, 32>(p, splits, s);
+    }
 }
 
 template <bool AKC, bool BKC, int EPI>
