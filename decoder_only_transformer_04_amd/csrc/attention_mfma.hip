@@ -108,6 +108,10 @@ __device__ __forceinline__ bf16x8 load8(const bf16_t* p, bool ok) {
     return *(const bf16x8*)p;
 }
 
+// 2^x on the hardware exp unit; every argument here is <= 0 (scores minus their
+// running maximum), where flushing a denormal result to zero is harmless
+__device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
 // accumulator register r of lane l sits at row 8 (r/4) + 4 (l/32) + r%4
 __device__ __forceinline__ int acc_row(int r, int g) { return 8 * (r >> 2) + 4 * g + (r & 3); }
 
@@ -158,32 +162,39 @@ __global__ __launch_bounds__(256) void attn_fwd_d64(const bf16_t* qkv, bf16_t* o
 #pragma unroll
                 for (int kk = 0; kk < 4; ++kk) s[kh] = mfma(frag_row(Ks, 32 * kh, kk, lane), qf[kk], s[kh]);
             }
-            const bool diag = k0 + 63 > q0;
+            // causal mask only on tiles that reach past this wave's first query
+            if (k0 + 63 > q0) {
+#pragma unroll
+                for (int kh = 0; kh < 2; ++kh) {
+                    const int lim = qi - (k0 + 32 * kh + 4 * g);  // row offset allowed up to lim
+#pragma unroll
+                    for (int r = 0; r < 16; ++r)
+                        if (8 * (r >> 2) + (r & 3) > lim) s[kh][r] = -INFINITY;
+                }
+            }
             float mx = -INFINITY;
 #pragma unroll
             for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    float v = s[kh][r] * sl2;
-                    if (diag && k0 + 32 * kh + acc_row(r, g) > qi) v = -INFINITY;
-                    s[kh][r] = v;
-                    mx = fmaxf(mx, v);
-                }
+                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kh][r]);
             mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-            const float mn = fmaxf(m, mx);
-            const float corr = exp2f(m - mn);
-            l *= corr;
+            // running max in the scaled base-2 domain; raw scores scale by sl2 > 0
+            const float mn = fmaxf(m, mx * sl2);
+            if (__any(mn != m)) {
+                const float corr = fexp2(m - mn);
+                l *= corr;
 #pragma unroll
-            for (int dt = 0; dt < 2; ++dt)
+                for (int dt = 0; dt < 2; ++dt)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) o[dt][r] *= corr;
+                    for (int r = 0; r < 16; ++r) o[dt][r] *= corr;
+            }
             float ls = 0.0f;
             bf16x8 pk[4];
 #pragma unroll
             for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    const float p = exp2f(s[kh][r] - mn);
+                    const float p = fexp2(fmaf(s[kh][r], sl2, -mn));
                     ls += p;
                     pk[2 * kh + (r >> 3)][r & 7] = (__bf16)p;
                 }
@@ -298,14 +309,17 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_d64(const bf16_t* qkv, const 
                 }
             }
             bf16x8 dsk[4];
+            const bool diag = k0 + 63 > q0;
 #pragma unroll
-            for (int kh = 0; kh < 2; ++kh)
+            for (int kh = 0; kh < 2; ++kh) {
+                const int lim = qi - (k0 + 32 * kh + 4 * g);
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    const int key = k0 + 32 * kh + acc_row(r, g);
-                    const float p = (key <= qi && key < T) ? exp2f(s[kh][r] * sl2 - lse2) : 0.0f;
+                    float p = fexp2(fmaf(s[kh][r], sl2, -lse2));
+                    if (diag && 8 * (r >> 2) + (r & 3) > lim) p = 0.0f;
                     dsk[2 * kh + (r >> 3)][r & 7] = (__bf16)(p * (dp[kh][r] - Dq));
                 }
+            }
 #pragma unroll
             for (int dt = 0; dt < 2; ++dt)
 #pragma unroll
@@ -366,7 +380,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_d64(const bf16_t* qkv, cons
         tile_load(rd, dOg, C, qt * 64, T, tid);
         if (tid < 64) {
             const int q = qt * 64 + tid;
-            pl = q < T ? lse[lb + q] * kLog2e : 0.0f;
+            pl = q < T ? lse[lb + q] * kLog2e : INFINITY;  // rows past T get probability 0
             pd = q < T ? Dbuf[lb + q] : 0.0f;
         }
     };
@@ -400,11 +414,14 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_d64(const bf16_t* qkv, cons
                     s = mfma(frag_row(Qs, 32 * qh, kk, lane), kf[kk], s);
                     dp = mfma(frag_row(dOs, 32 * qh, kk, lane), vf[kk], dp);
                 }
+                // queries of this half are q0t + 32 qh + acc_row(r, g); keep q >= kj
+                const bool diag = q0t + 32 * qh < k0w + 32;
+                const int lim = kj - (q0t + 32 * qh + 4 * g);  // row offset must be >= lim
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int ql = 32 * qh + acc_row(r, g);
-                    const int q = q0t + ql;
-                    const float p = (q >= kj && q < T) ? exp2f(s[r] * sl2 - sL[buf][ql]) : 0.0f;
+                    float p = fexp2(fmaf(s[r], sl2, -sL[buf][ql]));
+                    if (diag && 8 * (r >> 2) + (r & 3) < lim) p = 0.0f;
                     pt[2 * qh + (r >> 3)][r & 7] = (__bf16)p;
                     dst[2 * qh + (r >> 3)][r & 7] = (__bf16)(p * (dp[r] - sD[buf][ql]));
                 }
