@@ -46,8 +46,15 @@ def kernel_work(label: str, w: syn.Workload):
     causal = B * H * (T * (T + 1) // 2) * (C // H) * 2   # one causal T x T x d product
     if label == "attn.fwd":
         return "mfma", 2 * causal * L, "TFLOP/s"
+    # backward: 4 causal products per layer (dV, dP, dK, dQ); the dK/dV kernel is
+    # credited with dV, dP and dK, the dQ kernel with dQ (recomputed S and dP are
+    # not counted as algorithmic work)
     if label == "attn.bwd":
         return "mfma", 4 * causal * L, "TFLOP/s"
+    if label == "attn.bwd.dkdv":
+        return "mfma", 3 * causal * L, "TFLOP/s"
+    if label == "attn.bwd.dq":
+        return "mfma", causal * L, "TFLOP/s"
     Vp = (V + 127) // 128 * 128
     n = syn.n_params_exact(m)
     bytes_ = {
@@ -58,6 +65,7 @@ def kernel_work(label: str, w: syn.Workload):
         "ln.bwd": (2 * L + 1) * M * C * (4 * 4 + 2),  # dy, x, dres in/out (fp32), bf16 copy
         "embed.fwd": M * C * 4 * 3,
         "embed.bwd": M * C * 4 * 2,
+        "attn.bwd.pre": L * (M * C * 2 * 2 + B * H * T * 4),  # read O, dO (bf16); write D (fp32)
     }
     if label in bytes_:
         return "hbm", bytes_[label], "GB/s"
@@ -67,8 +75,8 @@ def kernel_work(label: str, w: syn.Workload):
 LABELS = ["gemm.fwd.qkv", "gemm.fwd.proj", "gemm.fwd.fc", "gemm.fwd.fc2", "gemm.fwd.head",
           "gemm.dgrad.head", "gemm.wgrad.head", "gemm.dgrad.fc2", "gemm.wgrad.fc2", "gemm.dgrad.fc",
           "gemm.wgrad.fc", "gemm.dgrad.proj", "gemm.wgrad.proj", "gemm.dgrad.qkv", "gemm.wgrad.qkv",
-          "attn.fwd", "attn.bwd", "ln.fwd", "ln.bwd", "ce", "loss", "colsum", "bias", "embed.fwd", "embed.bwd",
-          "gradnorm", "adamw"]
+          "attn.fwd", "attn.bwd.pre", "attn.bwd.dq", "attn.bwd.dkdv", "ln.fwd", "ln.bwd", "ce", "loss", "colsum",
+          "bias", "embed.fwd", "embed.bwd", "gradnorm", "adamw"]
 
 
 def cpu_baseline(w: syn.Workload, named: dict, seq: int):
@@ -109,6 +117,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seq", type=int, default=1024, help="tokens in the oracle's timed sample")
     ap.add_argument("--no-breakdown", action="store_true", help="skip the per-kernel-class timing pass")
+    ap.add_argument("--roofline-kernel", default=None, help="timing label for the roofline (default: the "
+                    "label with the largest time in the breakdown pass)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -155,8 +165,14 @@ def main():
             step(args.warmup + i)
             ms, n = g.timing_end()
             breakdown[lab] = round(ms, 4)
-    dominant = max((l for l in breakdown if kernel_work(l, w)[0]), key=lambda l: breakdown[l]) \
-        if breakdown else "gemm.fwd.head"
+    if args.roofline_kernel:
+        dominant = args.roofline_kernel
+    elif breakdown:
+        dominant = max((l for l in breakdown if kernel_work(l, w)[0]), key=lambda l: breakdown[l])
+    else:
+        dominant = "gemm.fwd.head"
+    if kernel_work(dominant, w)[0] is None:
+        sys.exit(f"no roofline work defined for label {dominant!r}")
 
     # timed region: exactly K steps, the dominant kernel's launches bracketed by events
     base = args.warmup + len(LABELS)

@@ -464,22 +464,28 @@ hipError_t attention_fwd(int dtype, int B, int Tn, int C, int H, const void* qkv
     return attention_fwd_simple(dtype, B, Tn, C, H, qkv, out, lse, s);
 }
 
+bool attention_bwd_staged(int dtype, int C, int H) { return dtype == GPT2_DTYPE_BF16 && C / H == 64; }
+
 hipError_t attention_bwd(int dtype, int B, int Tn, int C, int H, const void* qkv, const void* out, const float* lse,
-                         const void* dout, void* dqkv, float* Dbuf, hipStream_t s) {
+                         const void* dout, void* dqkv, float* Dbuf, hipStream_t s, int stages) {
     if (B == 0 || Tn == 0) return hipSuccess;
-    if (dtype == GPT2_DTYPE_BF16 && C / H == 64) {
+    if (attention_bwd_staged(dtype, C, H)) {
         const float sl2 = kLog2e / 8.0f;
         const float scale = 0.125f;
         const int64_t n = (int64_t)B * H * Tn;
-        hipLaunchKernelGGL(attn_bwd_pre_d64, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, (const bf16_t*)out,
-                           (const bf16_t*)dout, Dbuf, B, Tn, C, H);
         dim3 grid((Tn + 127) / 128, H, B);
-        hipLaunchKernelGGL(attn_bwd_dq_d64, grid, dim3(256), 0, s, (const bf16_t*)qkv, (const bf16_t*)dout, lse,
-                           (const float*)Dbuf, (bf16_t*)dqkv, Tn, C, H, sl2, scale);
-        hipLaunchKernelGGL(attn_bwd_dkdv_d64, grid, dim3(256), 0, s, (const bf16_t*)qkv, (const bf16_t*)dout, lse,
-                           (const float*)Dbuf, (bf16_t*)dqkv, Tn, C, H, sl2, scale);
+        if (stages & ATT_BWD_PRE)
+            hipLaunchKernelGGL(attn_bwd_pre_d64, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
+                               (const bf16_t*)out, (const bf16_t*)dout, Dbuf, B, Tn, C, H);
+        if (stages & ATT_BWD_DQ)
+            hipLaunchKernelGGL(attn_bwd_dq_d64, grid, dim3(256), 0, s, (const bf16_t*)qkv, (const bf16_t*)dout, lse,
+                               (const float*)Dbuf, (bf16_t*)dqkv, Tn, C, H, sl2, scale);
+        if (stages & ATT_BWD_DKDV)
+            hipLaunchKernelGGL(attn_bwd_dkdv_d64, grid, dim3(256), 0, s, (const bf16_t*)qkv, (const bf16_t*)dout,
+                               lse, (const float*)Dbuf, (bf16_t*)dqkv, Tn, C, H, sl2, scale);
         return hipGetLastError();
     }
+    if (stages != ATT_BWD_ALL) return hipErrorInvalidValue;
     return attention_bwd_simple(dtype, B, Tn, C, H, qkv, out, lse, dout, dqkv, Dbuf, s);
 }
 

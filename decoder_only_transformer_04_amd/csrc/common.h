@@ -122,8 +122,13 @@ hipError_t bias_grad(int dtype, const void* dY, int64_t rows, int N, float* part
                      int accumulate, hipStream_t s);
 hipError_t attention_fwd(int dtype, int B, int T, int C, int H, const void* qkv, void* out, float* lse,
                          hipStream_t s);
+// attention backward runs as three launches (D = rowsum(dO*O), dQ, dK/dV) on the MFMA
+// path; `stages` selects which of them to enqueue (the scalar path takes all only)
+enum { ATT_BWD_PRE = 1, ATT_BWD_DQ = 2, ATT_BWD_DKDV = 4, ATT_BWD_ALL = 7 };
+bool attention_bwd_staged(int dtype, int C, int H);
 hipError_t attention_bwd(int dtype, int B, int T, int C, int H, const void* qkv, const void* out,
-                         const float* lse, const void* dout, void* dqkv, float* Dbuf, hipStream_t s);
+                         const float* lse, const void* dout, void* dqkv, float* Dbuf, hipStream_t s,
+                         int stages = ATT_BWD_ALL);
 hipError_t cross_entropy(int dtype, void* logits, int64_t rows, int V, int ld, const int32_t* targets,
                          float* loss_rows, int32_t* argmax, int write_grad, uint32_t* status, hipStream_t s);
 hipError_t mean_loss(const float* loss_rows, int64_t rows, float* out, uint32_t* status, hipStream_t s);

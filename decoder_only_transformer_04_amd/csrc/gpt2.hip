@@ -385,8 +385,22 @@ int gpt2_backward(gpt2_ctx* x, float loss_scale, int32_t zero_grads) {
         G2_T("gemm.wgrad.proj", linear_wgrad(dt, s, M, C, C, dres_act, C, at<char>(x, ap.att[l]), gf(x, w.w_proj), acc, 1.0f, sb,
                             sbytes));
         if (w.b_proj >= 0) G2_T("bias", bias_grad(dt, dres_act, M, C, bpart, ap.bias_part_rows, gf(x, w.b_proj), acc, s));
-        G2_T("attn.bwd", attention_bwd(dt, ap.B, T, C, H, at<char>(x, ap.qkv[l]), at<char>(x, ap.att[l]), at<float>(x, ap.lse[l]),
-                             at<char>(x, ap.datt), at<char>(x, ap.dqkv), at<float>(x, ap.attD), s));
+        {
+            const char* qkv_l = at<char>(x, ap.qkv[l]);
+            const char* att_l = at<char>(x, ap.att[l]);
+            const float* lse_l = at<float>(x, ap.lse[l]);
+            char* datt = at<char>(x, ap.datt);
+            char* dqkv = at<char>(x, ap.dqkv);
+            float* attD = at<float>(x, ap.attD);
+            if (attention_bwd_staged(dt, C, H)) {
+                G2_T("attn.bwd.pre", attention_bwd(dt, ap.B, T, C, H, qkv_l, att_l, lse_l, datt, dqkv, attD, s, ATT_BWD_PRE));
+                G2_T("attn.bwd.dq", attention_bwd(dt, ap.B, T, C, H, qkv_l, att_l, lse_l, datt, dqkv, attD, s, ATT_BWD_DQ));
+                G2_T("attn.bwd.dkdv",
+                     attention_bwd(dt, ap.B, T, C, H, qkv_l, att_l, lse_l, datt, dqkv, attD, s, ATT_BWD_DKDV));
+            } else {
+                G2_T("attn.bwd", attention_bwd(dt, ap.B, T, C, H, qkv_l, att_l, lse_l, datt, dqkv, attD, s));
+            }
+        }
         G2_T("gemm.dgrad.qkv", linear_dgrad(dt, s, EPI_F32, M, 3 * C, C, at<char>(x, ap.dqkv), 3 * C, wptr(x, w.w_qkv), dtmp, nullptr,
                             1.0f));
         G2_T("gemm.wgrad.qkv", linear_wgrad(dt, s, M, 3 * C, C, at<char>(x, ap.dqkv), 3 * C, at<char>(x, ap.ln1[l]), gf(x, w.w_qkv), acc,
