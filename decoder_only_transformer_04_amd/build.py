@@ -17,7 +17,11 @@ ARCH = "gfx950"
 SOURCES = ["layout.cpp", "gemm.hip", "elementwise.hip", "attention_simple.hip", "attention_mfma.hip", "gpt2.hip"]
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall", "-Wno-unused-function",
          # packed fp32 ALU ops stay off (hipcc's host pass warns that it does not know the feature)
-         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         # MFMA results in ordinary VGPRs: the attention kernels read every score
+         # accumulator with VALU code, and AGPR results cost one v_accvgpr move
+         # per element and iteration (and, in the dK/dV kernel, a second wave per SIMD)
+         "-mllvm", "-amdgpu-mfma-vgpr-form"]
 
 
 def _compile(src: str, verbose: bool) -> str:

@@ -115,15 +115,29 @@ __device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(
 // accumulator register r of lane l sits at row 8 (r/4) + 4 (l/32) + r%4
 __device__ __forceinline__ int acc_row(int r, int g) { return 8 * (r >> 2) + 4 * g + (r & 3); }
 
+// 1-D grid over (128-row block, head, batch), ordered by decreasing causal work:
+// query blocks from the last (longest rows) down, key blocks from the first
+// (most query tiles) up, so the dispatcher schedules longest jobs first. When
+// H B is a multiple of 8, all blocks of one (batch, head) share blockIdx mod 8,
+// which keeps them on one XCD and its L2.
+__device__ __forceinline__ void block_coords(int T, int H, bool late_first, int& blk, int& h, int& b) {
+    const int nblk = (T + 127) / 128;
+    const int hb_n = (int)gridDim.x / nblk;  // H * B
+    const int bid = (int)blockIdx.x;
+    const int rank = bid / hb_n, hb = bid - rank * hb_n;
+    blk = late_first ? nblk - 1 - rank : rank;
+    h = hb % H;
+    b = hb / H;
+}
+
 }  // namespace
 
 // ------------------------------------------------------------------ forward
 __global__ __launch_bounds__(256) void attn_fwd_d64(const bf16_t* qkv, bf16_t* out, float* lse, int T, int C, int H,
                                                     float sl2) {
     __shared__ __attribute__((aligned(16))) char smem[2][2][kTileBytes];
-    const int nqb = (T + 127) / 128;
-    const int qb = nqb - 1 - (int)blockIdx.x;  // longest rows first
-    const int h = blockIdx.y, b = blockIdx.z;
+    int qb, h, b;
+    block_coords(T, H, true, qb, h, b);
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 5;
     const int64_t rs = 3 * (int64_t)C;
     const bf16_t* base = qkv + (int64_t)b * T * rs;
@@ -256,9 +270,8 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_d64(const bf16_t* qkv, const 
                                                        const float* Dbuf, bf16_t* dqkv, int T, int C, int H,
                                                        float sl2, float scale) {
     __shared__ __attribute__((aligned(16))) char smem[2][2][kTileBytes];
-    const int nqb = (T + 127) / 128;
-    const int qb = nqb - 1 - (int)blockIdx.x;
-    const int h = blockIdx.y, b = blockIdx.z;
+    int qb, h, b;
+    block_coords(T, H, true, qb, h, b);
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 5;
     const int64_t rs = 3 * (int64_t)C;
     const bf16_t* base = qkv + (int64_t)b * T * rs;
@@ -352,8 +365,8 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_d64(const bf16_t* qkv, cons
                                                          float sl2, float scale) {
     __shared__ __attribute__((aligned(16))) char smem[2][2][kTileBytes];
     __shared__ float sL[2][64], sD[2][64];
-    const int kb = blockIdx.x;  // earliest keys (most query tiles) first
-    const int h = blockIdx.y, b = blockIdx.z;
+    int kb, h, b;
+    block_coords(T, H, false, kb, h, b);
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 5;
     const int64_t rs = 3 * (int64_t)C;
     const bf16_t* base = qkv + (int64_t)b * T * rs;
@@ -457,7 +470,7 @@ hipError_t attention_fwd(int dtype, int B, int Tn, int C, int H, const void* qkv
     if (B == 0 || Tn == 0) return hipSuccess;
     if (dtype == GPT2_DTYPE_BF16 && C / H == 64) {
         const float sl2 = kLog2e / 8.0f;  // 1/sqrt(64) in base 2
-        dim3 grid((Tn + 127) / 128, H, B);
+        const dim3 grid((unsigned)((Tn + 127) / 128 * H * B));
         hipLaunchKernelGGL(attn_fwd_d64, grid, dim3(256), 0, s, (const bf16_t*)qkv, (bf16_t*)out, lse, Tn, C, H, sl2);
         return hipGetLastError();
     }
@@ -473,7 +486,7 @@ hipError_t attention_bwd(int dtype, int B, int Tn, int C, int H, const void* qkv
         const float sl2 = kLog2e / 8.0f;
         const float scale = 0.125f;
         const int64_t n = (int64_t)B * H * Tn;
-        dim3 grid((Tn + 127) / 128, H, B);
+        const dim3 grid((unsigned)((Tn + 127) / 128 * H * B));
         if (stages & ATT_BWD_PRE)
             hipLaunchKernelGGL(attn_bwd_pre_d64, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
                                (const bf16_t*)out, (const bf16_t*)dout, Dbuf, B, Tn, C, H);

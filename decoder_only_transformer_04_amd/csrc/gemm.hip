@@ -289,15 +289,40 @@ __device__ __forceinline__ void mma_stage(const char* cur, f32x16 (&acc)[FM][FN]
     }
 }
 
-template <int BM, int BN, int BK, bool AKC, bool BKC, int EPI>
+// Wait until at most N vector-memory operations of this wave are outstanding
+// (vmcnt only; LDS and export counters untouched). Loads, including the LDS DMA
+// loads, retire in issue order, so this waits for all but the newest N.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Workgroup barrier for the stage ring. __syncthreads() (and any fence) makes
+// the compiler drain every outstanding vector-memory operation first (vmcnt(0)),
+// including the LDS DMA loads of later stages that must stay in flight across
+// the barrier. Here each wave has already waited (wait_vmcnt) for its own share
+// of the stage about to be read, so the barrier only needs the wave's LDS
+// operations complete (lgkmcnt(0)); the empty asm statements keep the compiler
+// from moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt not waited
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+template <int BM, int BN, int BK, bool AKC, bool BKC, int EPI, int NS>
 __global__ __launch_bounds__(256) void gemm_bf16_kernel(GP p) {
+    static_assert(NS >= 2 && NS <= 4, "pipeline depth");
     constexpr int ABYTES = TileCfg<BM, AKC, BK>::BYTES;
     constexpr int BBYTES = TileCfg<BN, BKC, BK>::BYTES;
     constexpr int STAGE = ABYTES + BBYTES;
     constexpr int WM = BM / 2, WN = BN / 2, FM = WM / 32, FN = WN / 32;
     constexpr int SP = WN + 4;  // epilogue: staged floats per row (padding spreads banks)
     constexpr int EPI_BYTES = 4 * 32 * SP * 4;
-    constexpr int SMEM = 2 * STAGE > EPI_BYTES ? 2 * STAGE : EPI_BYTES;
+    constexpr int SMEM = NS * STAGE > EPI_BYTES ? NS * STAGE : EPI_BYTES;
+    constexpr int DMA_OPS = DmaPlan<BM, AKC, BK>::NI + DmaPlan<BN, BKC, BK>::NI;  // per wave per stage
     __shared__ __attribute__((aligned(16))) char smem[SMEM];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -318,9 +343,11 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GP p) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-    // Stage t+1 streams straight into the other LDS buffer (no staging
-    // registers) while stage t is multiplied out of LDS; a stage that would
-    // cross the end of K takes the register path, which zero-fills the tail.
+    // NS-deep ring of LDS stages: while stage t is multiplied out of LDS, the
+    // next NS - 1 stages stream straight from global memory into their LDS
+    // slots (no staging registers). A stage that would cross the end of K takes
+    // the register path, which zero-fills the tail and completes before it
+    // returns, so only whole stages are ever in flight.
     DmaPlan<BM, AKC, BK> dA;
     DmaPlan<BN, BKC, BK> dB;
     dA.init(A, p.lda, m0, p.M, kbeg, wave, lane);
@@ -340,16 +367,34 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GP p) {
             dB.skip();
         }
     };
-    if (nk > 0) issue(smem, 0);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
+    // stages [0, nfull) are whole BK-deep stages loaded by DMA
+    const int nfull = (kend - kbeg) / BK;
+#pragma unroll
+    for (int t = 0; t < NS - 1; ++t)
+        if (t < nk) issue(smem + t * STAGE, t);
     for (int kt = 0; kt < nk; ++kt) {
-        char* cur = smem + (kt & 1) * STAGE;
-        if (kt + 1 < nk) issue(smem + ((kt + 1) & 1) * STAGE, kt + 1);
-        mma_stage<BM, BN, AKC, BKC, BK, FM, FN>(cur, acc, wm, wn, lane);
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
+        // stage kt must have landed: the DMA stages issued after it may stay in flight
+        const int newer = min(nk - 1, kt + NS - 2) - kt;        // stages issued after kt
+        const int newer_dma = max(0, min(nfull - 1, kt + NS - 2) - kt);
+        if (newer_dma == newer) {
+            if constexpr (NS >= 4) {
+                if (newer >= 2) wait_vmcnt<2 * DMA_OPS>();
+                else if (newer == 1) wait_vmcnt<DMA_OPS>();
+                else wait_vmcnt<0>();
+            } else if constexpr (NS == 3) {
+                if (newer >= 1) wait_vmcnt<DMA_OPS>();
+                else wait_vmcnt<0>();
+            } else {
+                wait_vmcnt<0>();
+            }
+        } else {
+            wait_vmcnt<0>();
+        }
+        lds_barrier();  // every wave's share of stage kt is in LDS; stage kt-1 is free
+        if (kt + NS - 1 < nk) issue(smem + ((kt + NS - 1) % NS) * STAGE, kt + NS - 1);
+        mma_stage<BM, BN, AKC, BKC, BK, FM, FN>(smem + (kt % NS) * STAGE, acc, wm, wn, lane);
     }
+    __syncthreads();  // the epilogue reuses the stage buffers
     // Epilogue: each wave stages one 32-row strip of its tile at a time through
     // LDS (reusing the main-loop buffers) so that lanes then own 8 consecutive
     // columns of a row. Accumulator (i, j, r) of lane l sits at row
@@ -453,20 +498,28 @@ __global__ void splitk_reduce_kernel(const float* part, int splits, int64_t n, f
 }
 
 // ------------------------------------------------------------------ launchers
-template <int BM, int BN, bool AKC, bool BKC, int EPI, int BK = 64>
+#ifndef G2_GEMM_NS
+#define G2_GEMM_NS 2
+#endif
+template <int BM, int BN, bool AKC, bool BKC, int EPI, int BK = 64, int NS = G2_GEMM_NS>
 static hipError_t launch_bf16(const GP& p, int splits, hipStream_t s) {
     dim3 grid((p.N + BN - 1) / BN, (unsigned)((p.M + BM - 1) / BM), splits);
-    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, BK, AKC, BKC, EPI>), grid, dim3(256), 0, s, p);
+    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, BK, AKC, BKC, EPI, NS>), grid, dim3(256), 0, s, p);
     return hipGetLastError();
 }
 
 template <bool AKC, bool BKC, int EPI>
 static hipError_t pick_tile_bf16(const GP& p, int splits, hipStream_t s) {
-#ifdef G2_FORCE_TILE  // tile experiments only
-    if (G2_FORCE_TILE == 0) return launch_bf16<256, 256, AKC, BKC, EPI>(p, splits, s);
-    if (G2_FORCE_TILE == 2) return launch_bf16<128, 128, AKC, BKC, EPI>(p, splits, s);
-    if (G2_FORCE_TILE == 3) return launch_bf16<128, 128, AKC, BKC, EPI, 32>(p, splits, s);
-    if (G2_FORCE_TILE == 4) return launch_bf16<256, 128, AKC, BKC, EPI, 32>(p, splits, s);
+#if defined(G2_FORCE_TILE)  // tile experiments only
+#if G2_FORCE_TILE == 0
+    return launch_bf16<256, 256, AKC, BKC, EPI>(p, splits, s);
+#elif G2_FORCE_TILE == 2
+    return launch_bf16<128, 128, AKC, BKC, EPI>(p, splits, s);
+#elif G2_FORCE_TILE == 3
+    return launch_bf16<128, 128, AKC, BKC, EPI, 32>(p, splits, s);
+#elif G2_FORCE_TILE == 4
+    return launch_bf16<256, 128, AKC, BKC, EPI, 32>(p, splits, s);
+#endif
 #endif
     // Tile policy from measurements on the 124M model's shapes: 128 x 128 tiles
     // let two or three workgroups share a CU, which hides LDS and global latency
