@@ -234,8 +234,8 @@ __global__ __launch_bounds__(256) void attn_fwd_d64(const bf16_t* qkv, bf16_t* o
             for (int rq = 0; rq < 4; ++rq) {
                 const int d = 32 * dt + 8 * rq + 4 * g;
                 uint2 pk2;
-                pk2.x = (uint32_t)f2bf(o[dt][4 * rq + 0] * inv) | ((uint32_t)f2bf(o[dt][4 * rq + 1] * inv) << 16);
-                pk2.y = (uint32_t)f2bf(o[dt][4 * rq + 2] * inv) | ((uint32_t)f2bf(o[dt][4 * rq + 3] * inv) << 16);
+                pk2.x = pack2bf(o[dt][4 * rq + 0] * inv, o[dt][4 * rq + 1] * inv);
+                pk2.y = pack2bf(o[dt][4 * rq + 2] * inv, o[dt][4 * rq + 3] * inv);
                 *(uint2*)(orow + d) = pk2;
             }
         if (g == 0) lse[((int64_t)b * H + h) * T + qi] = (m + log2f(l)) * kLn2;
@@ -360,8 +360,8 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_d64(const bf16_t* qkv, const 
             for (int rq = 0; rq < 4; ++rq) {
                 const int d = 32 * dt + 8 * rq + 4 * g;
                 uint2 pk2;
-                pk2.x = (uint32_t)f2bf(dq[dt][4 * rq + 0] * scale) | ((uint32_t)f2bf(dq[dt][4 * rq + 1] * scale) << 16);
-                pk2.y = (uint32_t)f2bf(dq[dt][4 * rq + 2] * scale) | ((uint32_t)f2bf(dq[dt][4 * rq + 3] * scale) << 16);
+                pk2.x = pack2bf(dq[dt][4 * rq + 0] * scale, dq[dt][4 * rq + 1] * scale);
+                pk2.y = pack2bf(dq[dt][4 * rq + 2] * scale, dq[dt][4 * rq + 3] * scale);
                 *(uint2*)(drow + d) = pk2;
             }
     }

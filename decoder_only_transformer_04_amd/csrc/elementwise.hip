@@ -203,8 +203,8 @@ template <class T> __device__ __forceinline__ void st4(T* p, float4 v);
 template <> __device__ __forceinline__ void st4<float>(float* p, float4 v) { *(float4*)p = v; }
 template <> __device__ __forceinline__ void st4<bf16_t>(bf16_t* p, float4 v) {
     uint2 o;
-    o.x = (uint32_t)f2bf(v.x) | ((uint32_t)f2bf(v.y) << 16);
-    o.y = (uint32_t)f2bf(v.z) | ((uint32_t)f2bf(v.w) << 16);
+    o.x = pack2bf(v.x, v.y);
+    o.y = pack2bf(v.z, v.w);
     *(uint2*)p = o;
 }
 __device__ __forceinline__ float hsum4(float4 v) { return (v.x + v.y) + (v.z + v.w); }
@@ -850,10 +850,10 @@ __global__ __launch_bounds__(512) void ce_reg_kernel(bf16_t* logits, int64_t row
                 o[e] = col < V ? __expf(v[e] - lse) - (col == tgt ? 1.0f : 0.0f) : 0.0f;
             }
             uint4 u;
-            u.x = (uint32_t)f2bf(o[0]) | ((uint32_t)f2bf(o[1]) << 16);
-            u.y = (uint32_t)f2bf(o[2]) | ((uint32_t)f2bf(o[3]) << 16);
-            u.z = (uint32_t)f2bf(o[4]) | ((uint32_t)f2bf(o[5]) << 16);
-            u.w = (uint32_t)f2bf(o[6]) | ((uint32_t)f2bf(o[7]) << 16);
+            u.x = pack2bf(o[0], o[1]);
+            u.y = pack2bf(o[2], o[3]);
+            u.z = pack2bf(o[4], o[5]);
+            u.w = pack2bf(o[6], o[7]);
             ((uint4*)z)[c] = u;
         }
     }
@@ -989,8 +989,8 @@ __global__ __launch_bounds__(256) void adamw_kernel(float* p, const float* g, fl
         ((float4*)v)[i] = vv;
         if (p16) {
             uint2 o;
-            o.x = (uint32_t)f2bf(pp.x) | ((uint32_t)f2bf(pp.y) << 16);
-            o.y = (uint32_t)f2bf(pp.z) | ((uint32_t)f2bf(pp.w) << 16);
+            o.x = pack2bf(pp.x, pp.y);
+            o.y = pack2bf(pp.z, pp.w);
             ((uint2*)p16)[i] = o;
         }
     }

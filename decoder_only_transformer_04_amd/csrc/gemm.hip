@@ -71,10 +71,10 @@ __device__ __forceinline__ void epi_apply(const GP& p, int64_t m, int n, float v
 // loads of bias / residual / pre-activation and 16- or 32-byte stores.
 __device__ __forceinline__ uint4 pack8(const float (&o)[8]) {
     uint4 r;
-    r.x = (uint32_t)f2bf(o[0]) | ((uint32_t)f2bf(o[1]) << 16);
-    r.y = (uint32_t)f2bf(o[2]) | ((uint32_t)f2bf(o[3]) << 16);
-    r.z = (uint32_t)f2bf(o[4]) | ((uint32_t)f2bf(o[5]) << 16);
-    r.w = (uint32_t)f2bf(o[6]) | ((uint32_t)f2bf(o[7]) << 16);
+    r.x = pack2bf(o[0], o[1]);
+    r.y = pack2bf(o[2], o[3]);
+    r.z = pack2bf(o[4], o[5]);
+    r.w = pack2bf(o[6], o[7]);
     return r;
 }
 __device__ __forceinline__ void unpack8(uint4 u, float (&o)[8]) {
@@ -266,26 +266,33 @@ __device__ __forceinline__ bf16x8 tile_frag(const char* lds, int rb, int kk, int
 }
 
 // One BK-deep stage from LDS: BK/16 steps of 16, every wave multiplying its
-// FM x FN grid of 32x32 fragments.
+// FM x FN grid of 32x32 fragments. The fragments of step kk+1 are read while
+// the MFMAs of step kk run (two register sets), so each step waits only for its
+// own LDS reads.
 template <int BM, int BN, bool AKC, bool BKC, int BK, int FM, int FN>
 __device__ __forceinline__ void mma_stage(const char* cur, f32x16 (&acc)[FM][FN], int wm, int wn, int lane) {
     constexpr int ABYTES = TileCfg<BM, AKC, BK>::BYTES;
     constexpr int WM = BM / 2, WN = BN / 2;
+    constexpr int KK = BK / 16;
 #if G2_GEMM_IGLP >= 0
     __builtin_amdgcn_iglp_opt(G2_GEMM_IGLP);
 #endif
+    bf16x8 af[2][FM], bv[2][FN];
+    auto load = [&](int buf, int kk) {
 #pragma unroll
-    for (int kk = 0; kk < BK / 16; ++kk) {
-        bf16x8 af[FM], bv[FN];
+        for (int i = 0; i < FM; ++i) af[buf][i] = tile_frag<BM, AKC, BK>(cur, wm * WM + i * 32, kk, lane);
 #pragma unroll
-        for (int i = 0; i < FM; ++i) af[i] = tile_frag<BM, AKC, BK>(cur, wm * WM + i * 32, kk, lane);
+        for (int j = 0; j < FN; ++j) bv[buf][j] = tile_frag<BN, BKC, BK>(cur + ABYTES, wn * WN + j * 32, kk, lane);
+    };
+    load(0, 0);
 #pragma unroll
-        for (int j = 0; j < FN; ++j) bv[j] = tile_frag<BN, BKC, BK>(cur + ABYTES, wn * WN + j * 32, kk, lane);
+    for (int kk = 0; kk < KK; ++kk) {
+        if (kk + 1 < KK) load((kk + 1) & 1, kk + 1);
 #pragma unroll
         for (int i = 0; i < FM; ++i)
 #pragma unroll
             for (int j = 0; j < FN; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bv[j], acc[i][j], 0, 0, 0);
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[kk & 1][i], bv[kk & 1][j], acc[i][j], 0, 0, 0);
     }
 }
 
@@ -430,8 +437,9 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GP p) {
     // LDS (reusing the main-loop buffers) so that lanes then own 8 consecutive
     // columns of a row. Accumulator (i, j, r) of lane l sits at row
     // 8 (r/4) + 4 (l/32) + r%4 and column l%32 of fragment (i, j).
-    constexpr int LPR = WN / 8;         // lanes per staged row
-    constexpr int RPP = 64 / LPR;       // rows per pass
+    constexpr int LPR = WN / 8;                   // lanes per staged row
+    constexpr int RPP = 64 / LPR;                 // rows per pass
+    constexpr int NPASS = (32 + RPP - 1) / RPP;   // passes per 32-row strip
     float* st = (float*)smem + wave * 32 * SP;
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
@@ -442,14 +450,16 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GP p) {
                 st[(8 * (r >> 2) + 4 * (lane >> 5) + (r & 3)) * SP + j * 32 + (lane & 31)] = acc[i][j][r];
         __syncthreads();
 #pragma unroll
-        for (int pass = 0; pass < 32 / RPP; ++pass) {
+        for (int pass = 0; pass < NPASS; ++pass) {
             const int rr = pass * RPP + lane / LPR;
             const int cc = (lane % LPR) * 8;
-            float v[8];
-            ld8f(st + rr * SP + cc, v);
-            const int64_t m = m0 + wm * WM + i * 32 + rr;
-            const int n = n0 + wn * WN + cc;
-            if (m < p.M && n < p.N) epi_apply8<EPI>(p, m, n, v);
+            if (lane < RPP * LPR && rr < 32) {  // WN = 96 leaves lanes 60..63 idle
+                float v[8];
+                ld8f(st + rr * SP + cc, v);
+                const int64_t m = m0 + wm * WM + i * 32 + rr;
+                const int n = n0 + wn * WN + cc;
+                if (m < p.M && n < p.N) epi_apply8<EPI>(p, m, n, v);
+            }
         }
         __syncthreads();
     }
@@ -572,6 +582,13 @@ static hipError_t pick_tile_bf16(const GP& p, int splits, hipStream_t s) {
     return launch_bf16<128, 128, AKC, BKC, EPI, 32>(p, splits, s);
 #elif G2_FORCE_TILE == 4
     return launch_bf16<256, 128, AKC, BKC, EPI, 32>(p, splits, s);
+#elif G2_FORCE_TILE == 5
+    if constexpr (AKC && BKC) return launch_bf16<192, 192, AKC, BKC, EPI, 32>(p, splits, s);
+#elif G2_FORCE_TILE == 6
+    if constexpr (AKC && BKC) return launch_bf16<192, 192, AKC, BKC, EPI, 64>(p, splits, s);
+#elif G2_FORCE_TILE == 7
+    if constexpr (AKC && BKC) return launch_bf16<192, 192, AKC, BKC, EPI, 64, 3>(p, splits, s);
+    if constexpr (!(AKC && BKC)) return launch_bf16<128, 128, AKC, BKC, EPI, AKC ? 32 : 64, 2>(p, splits, s);
 #endif
 #endif
     // Tile policy from measurements on the 124M model's shapes: 128 x 128 tiles
