@@ -139,10 +139,10 @@ __device__ __forceinline__ void epi_apply8(const GP& p, int64_t m, int n, const 
 }
 
 // ------------------------------------------------------------------ bf16 MFMA kernel
-template <int R, bool KC, int BK = 64>
+template <int R, bool KC, int BK = 64, int NT = 256>
 struct TileCfg {
     static constexpr int BYTES = R * BK * 2;
-    static constexpr int CHUNKS = BYTES / 16 / 256;  // 16-byte chunks per thread per stage
+    static constexpr int CHUNKS = BYTES / 16 / NT;   // 16-byte chunks per thread per stage (NT threads)
     static constexpr int PITCH = KC ? BK * 2 : R * 2;  // bytes per tile row
     static constexpr int CPR = PITCH / 16;           // 16-byte chunks per tile row
 };
@@ -150,15 +150,22 @@ struct TileCfg {
 // LDS placement of 16-byte chunk `ch` of tile row `row`.
 // KC tiles ([R][BK k]): the chunk index is XOR-ed with a function of the row so
 // that the 128-bit fragment reads (16 consecutive rows, one chunk) hit 16
-// distinct 16-byte bank groups. Transposed tiles ([BK k][R]): chunk ^ 4 (row mod 4)
-// keeps the transpose reads (4 consecutive rows, 4 consecutive chunks) conflict-free.
+// distinct 16-byte bank groups. Transposed tiles ([BK k][R]) are read four
+// consecutive rows by four consecutive chunks at a time. With 256- or 512-byte
+// rows (R = 128, 256) every row starts on bank 0 and chunk ^ 4 (row mod 4)
+// spreads the four rows over the 64 banks. With 384-byte rows (R = 192) odd rows
+// already start half-way round, so only bit 2 of the chunk is flipped, by bit 1
+// of the row, which keeps every chunk inside its row.
 template <int R, bool KC, int BK = 64>
 __device__ __forceinline__ int slot_of(int row, int ch) {
     if constexpr (KC) {
         if constexpr (BK == 64) return row * 8 + (ch ^ ((row >> 1) & 7));
         else return row * 4 + (ch ^ ((row >> 2) & 3));
-    } else {
+    } else if constexpr (R % 128 == 0) {
         return row * (R / 8) + (ch ^ (4 * (row & 3)));
+    } else {
+        static_assert(R == 192, "transposed tile width");
+        return row * (R / 8) + (ch ^ (4 * ((row >> 1) & 1)));
     }
 }
 
@@ -166,13 +173,13 @@ __device__ __forceinline__ int slot_of(int row, int ch) {
 // KC: tile rows r0.. (< rmax), k in [k0, kmax); not KC: k rows k0.. (< kmax),
 // contiguous rows r0.. (< rmax). kmax (KC) and rmax (not KC) are multiples of
 // 8, so a 16-byte chunk is either wholly in bounds or wholly zero-filled.
-template <int R, bool KC, int BK>
-__device__ __forceinline__ void tile_gload(uint4 (&regs)[R * BK / 2048], const bf16_t* base,
+template <int R, bool KC, int BK, int NT>
+__device__ __forceinline__ void tile_gload(uint4 (&regs)[R * BK / (8 * NT)], const bf16_t* base,
                                            int64_t ld, int64_t r0, int64_t rmax, int k0, int kmax, int tid) {
     constexpr int CPR = TileCfg<R, KC, BK>::CPR;
 #pragma unroll
-    for (int i = 0; i < TileCfg<R, KC, BK>::CHUNKS; ++i) {
-        const int c = tid + 256 * i;
+    for (int i = 0; i < R * BK / (8 * NT); ++i) {
+        const int c = tid + NT * i;
         uint4 v = make_uint4(0, 0, 0, 0);
         if constexpr (KC) {
             const int row = c / CPR;
@@ -188,12 +195,12 @@ __device__ __forceinline__ void tile_gload(uint4 (&regs)[R * BK / 2048], const b
     }
 }
 
-template <int R, bool KC, int BK>
-__device__ __forceinline__ void tile_sstore(char* lds, const uint4 (&regs)[R * BK / 2048], int tid) {
+template <int R, bool KC, int BK, int NT>
+__device__ __forceinline__ void tile_sstore(char* lds, const uint4 (&regs)[R * BK / (8 * NT)], int tid) {
     constexpr int CPR = TileCfg<R, KC, BK>::CPR;
 #pragma unroll
-    for (int i = 0; i < TileCfg<R, KC, BK>::CHUNKS; ++i) {
-        const int c = tid + 256 * i;
+    for (int i = 0; i < R * BK / (8 * NT); ++i) {
+        const int c = tid + NT * i;
         *(uint4*)(lds + 16 * slot_of<R, KC, BK>(c / CPR, c % CPR)) = regs[i];
     }
 }
@@ -205,9 +212,10 @@ __device__ __forceinline__ void tile_sstore(char* lds, const uint4 (&regs)[R * B
 // Rows past rmax are clamped to valid memory (their products land only in
 // discarded output rows or columns); a stage that would cross the end of K
 // takes the register path instead, which zero-fills the tail.
-template <int R, bool KC, int BK>
+template <int R, bool KC, int BK, int NW = 4>
 struct DmaPlan {
-    static constexpr int NI = TileCfg<R, KC, BK>::BYTES / 4096;  // 1 KB instructions per wave
+    static constexpr int NI = TileCfg<R, KC, BK>::BYTES / (1024 * NW);  // 1 KB instructions per wave (NW waves)
+    static_assert(NI * 1024 * NW == TileCfg<R, KC, BK>::BYTES, "stage must split evenly over the waves");
     static constexpr int CPR = TileCfg<R, KC, BK>::CPR;
     const bf16_t* src[NI];
     int64_t step;
@@ -266,14 +274,15 @@ __device__ __forceinline__ bf16x8 tile_frag(const char* lds, int rb, int kk, int
 }
 
 // One BK-deep stage from LDS: BK/16 steps of 16, every wave multiplying its
-// FM x FN grid of 32x32 fragments. The fragments of step kk+1 are read while
-// the MFMAs of step kk run (two register sets), so each step waits only for its
-// own LDS reads.
-template <int BM, int BN, bool AKC, bool BKC, int BK, int FM, int FN>
-__device__ __forceinline__ void mma_stage(const char* cur, f32x16 (&acc)[FM][FN], int wm, int wn, int lane) {
+// FM x FN grid of 32x32 fragments (a WM x WN block at (wm, wn)). With KS wave
+// groups splitting the contraction, group ks takes steps ks, ks + KS, ... The
+// fragments of the next step are read while the MFMAs of the current one run
+// (two register sets), so each step waits only for its own LDS reads.
+template <int BM, int BN, bool AKC, bool BKC, int BK, int FM, int FN, int WM, int WN, int KS>
+__device__ __forceinline__ void mma_stage(const char* cur, f32x16 (&acc)[FM][FN], int wm, int wn, int ks,
+                                          int lane) {
     constexpr int ABYTES = TileCfg<BM, AKC, BK>::BYTES;
-    constexpr int WM = BM / 2, WN = BN / 2;
-    constexpr int KK = BK / 16;
+    constexpr int KK = BK / 16 / KS;
 #if G2_GEMM_IGLP >= 0
     __builtin_amdgcn_iglp_opt(G2_GEMM_IGLP);
 #endif
@@ -284,10 +293,10 @@ __device__ __forceinline__ void mma_stage(const char* cur, f32x16 (&acc)[FM][FN]
 #pragma unroll
         for (int j = 0; j < FN; ++j) bv[buf][j] = tile_frag<BN, BKC, BK>(cur + ABYTES, wn * WN + j * 32, kk, lane);
     };
-    load(0, 0);
+    load(0, ks);
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
-        if (kk + 1 < KK) load((kk + 1) & 1, kk + 1);
+        if (kk + 1 < KK) load((kk + 1) & 1, ks + (kk + 1) * KS);
 #pragma unroll
         for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -348,21 +357,31 @@ __device__ __forceinline__ void tile_coords(int nm, int nn, int& tm, int& tn) {
     tn = r / gsize;
 }
 
-template <int BM, int BN, int BK, bool AKC, bool BKC, int EPI, int NS>
-__global__ __launch_bounds__(256) void gemm_bf16_kernel(GP p) {
+// Tile BM x BN, BK-deep stages in an NS-deep LDS ring. Waves form a WGM x WGN
+// grid over the tile (each a WM x WN block of 32x32 fragments), times KS groups
+// that split every stage's contraction steps; the KS partial sums are added
+// through LDS before the epilogue.
+template <int BM, int BN, int BK, bool AKC, bool BKC, int EPI, int NS, int WGM = 2, int WGN = 2, int KS = 1>
+__global__ __launch_bounds__(64 * WGM * WGN * KS) void gemm_bf16_kernel(GP p) {
     static_assert(NS >= 2 && NS <= 4, "pipeline depth");
+    static_assert(KS == 1 || KS == 2, "contraction split");
+    constexpr int NWQ = WGM * WGN;      // waves per group
+    constexpr int NW = NWQ * KS;        // waves per workgroup
+    constexpr int NT = 64 * NW;
     constexpr int ABYTES = TileCfg<BM, AKC, BK>::BYTES;
     constexpr int BBYTES = TileCfg<BN, BKC, BK>::BYTES;
     constexpr int STAGE = ABYTES + BBYTES;
-    constexpr int WM = BM / 2, WN = BN / 2, FM = WM / 32, FN = WN / 32;
+    constexpr int WM = BM / WGM, WN = BN / WGN, FM = WM / 32, FN = WN / 32;
+    static_assert(FM * 32 == WM && FN * 32 == WN && (BK / 16) % KS == 0, "wave tiling");
     constexpr int SP = WN + 4;  // epilogue: staged floats per row (padding spreads banks)
-    constexpr int EPI_BYTES = 4 * 32 * SP * 4;
+    constexpr int EPI_BYTES = NWQ * 32 * SP * 4;
     constexpr int SMEM = NS * STAGE > EPI_BYTES ? NS * STAGE : EPI_BYTES;
-    constexpr int DMA_OPS = DmaPlan<BM, AKC, BK>::NI + DmaPlan<BN, BKC, BK>::NI;  // per wave per stage
+    constexpr int DMA_OPS = DmaPlan<BM, AKC, BK, NW>::NI + DmaPlan<BN, BKC, BK, NW>::NI;  // per wave per stage
     __shared__ __attribute__((aligned(16))) char smem[SMEM];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
+    const int ks = wave / NWQ, wq = wave - ks * NWQ;
+    const int wm = wq / WGN, wn = wq - (wq / WGN) * WGN;
     int tm, tn;
     tile_coords((p.M + BM - 1) / BM, (p.N + BN - 1) / BN, tm, tn);
     const int64_t m0 = (int64_t)tm * BM;
@@ -386,8 +405,8 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GP p) {
     // slots (no staging registers). A stage that would cross the end of K takes
     // the register path, which zero-fills the tail and completes before it
     // returns, so only whole stages are ever in flight.
-    DmaPlan<BM, AKC, BK> dA;
-    DmaPlan<BN, BKC, BK> dB;
+    DmaPlan<BM, AKC, BK, NW> dA;
+    DmaPlan<BN, BKC, BK, NW> dB;
     dA.init(A, p.lda, m0, p.M, kbeg, wave, lane);
     dB.init(B, p.ldb, n0, p.N, kbeg, wave, lane);
     auto issue = [&](char* buf, int kt) {
@@ -396,11 +415,11 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GP p) {
             dA.issue(buf, wave);
             dB.issue(buf + ABYTES, wave);
         } else {
-            uint4 ra[TileCfg<BM, AKC, BK>::CHUNKS], rb[TileCfg<BN, BKC, BK>::CHUNKS];
-            tile_gload<BM, AKC, BK>(ra, A, p.lda, m0, p.M, k0, kend, tid);
-            tile_gload<BN, BKC, BK>(rb, B, p.ldb, n0, p.N, k0, kend, tid);
-            tile_sstore<BM, AKC, BK>(buf, ra, tid);
-            tile_sstore<BN, BKC, BK>(buf + ABYTES, rb, tid);
+            uint4 ra[BM * BK / (8 * NT)], rb[BN * BK / (8 * NT)];
+            tile_gload<BM, AKC, BK, NT>(ra, A, p.lda, m0, p.M, k0, kend, tid);
+            tile_gload<BN, BKC, BK, NT>(rb, B, p.ldb, n0, p.N, k0, kend, tid);
+            tile_sstore<BM, AKC, BK, NT>(buf, ra, tid);
+            tile_sstore<BN, BKC, BK, NT>(buf + ABYTES, rb, tid);
             dA.skip();
             dB.skip();
         }
@@ -430,35 +449,54 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GP p) {
         }
         lds_barrier();  // every wave's share of stage kt is in LDS; stage kt-1 is free
         if (kt + NS - 1 < nk) issue(smem + ((kt + NS - 1) % NS) * STAGE, kt + NS - 1);
-        mma_stage<BM, BN, AKC, BKC, BK, FM, FN>(smem + (kt % NS) * STAGE, acc, wm, wn, lane);
+        mma_stage<BM, BN, AKC, BKC, BK, FM, FN, WM, WN, KS>(smem + (kt % NS) * STAGE, acc, wm, wn, ks, lane);
     }
     __syncthreads();  // the epilogue reuses the stage buffers
-    // Epilogue: each wave stages one 32-row strip of its tile at a time through
-    // LDS (reusing the main-loop buffers) so that lanes then own 8 consecutive
-    // columns of a row. Accumulator (i, j, r) of lane l sits at row
-    // 8 (r/4) + 4 (l/32) + r%4 and column l%32 of fragment (i, j).
+    // Epilogue: each wave of group 0 stages one 32-row strip of its block at a
+    // time through LDS (reusing the main-loop buffers) so that lanes then own 8
+    // consecutive columns of a row; with KS = 2, group 1 first leaves its partial
+    // sums in the same slots and group 0 adds them in. Accumulator (i, j, r) of
+    // lane l sits at row 8 (r/4) + 4 (l/32) + r%4 and column l%32 of fragment (i, j).
+    // Every wave reaches every barrier.
     constexpr int LPR = WN / 8;                   // lanes per staged row
     constexpr int RPP = 64 / LPR;                 // rows per pass
     constexpr int NPASS = (32 + RPP - 1) / RPP;   // passes per 32-row strip
-    float* st = (float*)smem + wave * 32 * SP;
+    float* st = (float*)smem + wq * 32 * SP;
+    const int srow = 4 * (lane >> 5), scol = lane & 31;
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
+        if constexpr (KS > 1) {
+            if (ks == 1) {
 #pragma unroll
-        for (int j = 0; j < FN; ++j)
+                for (int j = 0; j < FN; ++j)
 #pragma unroll
-            for (int r = 0; r < 16; ++r)
-                st[(8 * (r >> 2) + 4 * (lane >> 5) + (r & 3)) * SP + j * 32 + (lane & 31)] = acc[i][j][r];
+                    for (int r = 0; r < 16; ++r)
+                        st[(8 * (r >> 2) + srow + (r & 3)) * SP + j * 32 + scol] = acc[i][j][r];
+            }
+            __syncthreads();
+        }
+        if (ks == 0) {
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    float* q = st + (8 * (r >> 2) + srow + (r & 3)) * SP + j * 32 + scol;
+                    *q = KS > 1 ? *q + acc[i][j][r] : acc[i][j][r];
+                }
+        }
         __syncthreads();
+        if (ks == 0) {
 #pragma unroll
-        for (int pass = 0; pass < NPASS; ++pass) {
-            const int rr = pass * RPP + lane / LPR;
-            const int cc = (lane % LPR) * 8;
-            if (lane < RPP * LPR && rr < 32) {  // WN = 96 leaves lanes 60..63 idle
-                float v[8];
-                ld8f(st + rr * SP + cc, v);
-                const int64_t m = m0 + wm * WM + i * 32 + rr;
-                const int n = n0 + wn * WN + cc;
-                if (m < p.M && n < p.N) epi_apply8<EPI>(p, m, n, v);
+            for (int pass = 0; pass < NPASS; ++pass) {
+                const int rr = pass * RPP + lane / LPR;
+                const int cc = (lane % LPR) * 8;
+                if (lane < RPP * LPR && rr < 32) {  // WN = 96 leaves lanes 60..63 idle
+                    float v[8];
+                    ld8f(st + rr * SP + cc, v);
+                    const int64_t m = m0 + wm * WM + i * 32 + rr;
+                    const int n = n0 + wn * WN + cc;
+                    if (m < p.M && n < p.N) epi_apply8<EPI>(p, m, n, v);
+                }
             }
         }
         __syncthreads();
@@ -562,45 +600,42 @@ __global__ void splitk_reduce4_kernel(const float* part, int splits, int64_t n, 
 #ifndef G2_GEMM_NS
 #define G2_GEMM_NS 2
 #endif
-template <int BM, int BN, bool AKC, bool BKC, int EPI, int BK = 64, int NS = G2_GEMM_NS>
+template <int BM, int BN, bool AKC, bool BKC, int EPI, int BK = 64, int NS = G2_GEMM_NS, int WGM = 2, int WGN = 2,
+          int KS = 1>
 static hipError_t launch_bf16(const GP& p, int splits, hipStream_t s) {
     const int64_t tiles = (int64_t)((p.N + BN - 1) / BN) * ((p.M + BM - 1) / BM);
     if (tiles > INT32_MAX) return hipErrorInvalidValue;
     dim3 grid((unsigned)tiles, 1, splits);
-    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, BK, AKC, BKC, EPI, NS>), grid, dim3(256), 0, s, p);
+    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, BK, AKC, BKC, EPI, NS, WGM, WGN, KS>), grid,
+                       dim3(64 * WGM * WGN * KS), 0, s, p);
     return hipGetLastError();
 }
 
 template <bool AKC, bool BKC, int EPI>
 static hipError_t pick_tile_bf16(const GP& p, int splits, hipStream_t s) {
 #if defined(G2_FORCE_TILE)  // tile experiments only
-#if G2_FORCE_TILE == 0
-    return launch_bf16<256, 256, AKC, BKC, EPI>(p, splits, s);
-#elif G2_FORCE_TILE == 2
-    return launch_bf16<128, 128, AKC, BKC, EPI>(p, splits, s);
-#elif G2_FORCE_TILE == 3
+#if G2_FORCE_TILE == 3
     return launch_bf16<128, 128, AKC, BKC, EPI, 32>(p, splits, s);
-#elif G2_FORCE_TILE == 4
-    return launch_bf16<256, 128, AKC, BKC, EPI, 32>(p, splits, s);
-#elif G2_FORCE_TILE == 5
-    if constexpr (AKC && BKC) return launch_bf16<192, 192, AKC, BKC, EPI, 32>(p, splits, s);
-#elif G2_FORCE_TILE == 6
-    if constexpr (AKC && BKC) return launch_bf16<192, 192, AKC, BKC, EPI, 64>(p, splits, s);
-#elif G2_FORCE_TILE == 7
-    if constexpr (AKC && BKC) return launch_bf16<192, 192, AKC, BKC, EPI, 64, 3>(p, splits, s);
-    if constexpr (!(AKC && BKC)) return launch_bf16<128, 128, AKC, BKC, EPI, AKC ? 32 : 64, 2>(p, splits, s);
+#elif G2_FORCE_TILE == 13
+    return launch_bf16<192, 192, AKC, BKC, EPI, 64, 2, 2, 2, 2>(p, splits, s);
+#elif G2_FORCE_TILE == 14
+    return launch_bf16<256, 256, AKC, BKC, EPI, 64, 2, 2, 4, 1>(p, splits, s);
 #endif
 #endif
-    // Tile policy from measurements on the 124M model's shapes: 128 x 128 tiles
-    // let two or three workgroups share a CU, which hides LDS and global latency
-    // better than one 256 x 256 workgroup. Products with K-contiguous operands
-    // (forward) and input gradients use 32-deep stages (32 KB of LDS, three
-    // workgroups per CU); the very wide vocabulary product uses 256 x 128; the
-    // weight gradients (two transposed operands, K = tokens) keep 64-deep stages.
+    // Tile policy from measurements on the 124M model's shapes (M = 12288 tokens):
+    //  - long contractions onto 768-wide outputs (K >= 2048, N a multiple of 192):
+    //    192 x 192 tiles, one per CU in a single wave of 256 tiles, eight waves in
+    //    two groups splitting each 64-deep stage;
+    //  - the vocabulary-wide forward product: 256 x 256 tiles, eight waves;
+    //  - otherwise 128 x 128 tiles, two or three workgroups per CU, 32-deep
+    //    stages when A is K-contiguous (forward and input gradients), 64-deep for
+    //    the weight gradients (both operands transposed, K = tokens).
     if constexpr (!AKC) {
         return launch_bf16<128, 128, AKC, BKC, EPI, 64>(p, splits, s);
     } else {
-        if (BKC && p.N >= 8192) return launch_bf16<256, 128, AKC, BKC, EPI, 32>(p, splits, s);
+        if (p.N % 192 == 0 && p.N <= 1536 && p.K >= 2048 && splits == 1)
+            return launch_bf16<192, 192, AKC, BKC, EPI, 64, 2, 2, 2, 2>(p, splits, s);
+        if (BKC && p.N >= 8192) return launch_bf16<256, 256, AKC, BKC, EPI, 64, 2, 2, 4, 1>(p, splits, s);
         return launch_bf16<128, 128, AKC, BKC, EPI, 32>(p, splits, s);
     }
 }

@@ -42,7 +42,9 @@ def check_out(dtype, got, ref, what):
         assert e <= 1e-2 and c >= 0.9999, (what, e, c)
 
 
-SHAPES = [(333, 264, 136), (512, 512, 256), (1, 8, 8), (130, 2304, 768)]
+# the last two reach the 192 x 192 (N = 768, K >= 2048) and 256 x 256 (N >= 8192)
+# tile paths with ragged row and column tiles
+SHAPES = [(333, 264, 136), (512, 512, 256), (1, 8, 8), (130, 2304, 768), (500, 768, 3072), (300, 8320, 768)]
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
@@ -62,7 +64,8 @@ def test_linear_fwd(b, oracle, dtype, M, N, K):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-@pytest.mark.parametrize("M,N,K", [(333, 264, 136), (1111, 512, 256), (2048, 768, 3072)])
+# (700, 3072, 768): the input gradient contracts over 3072 onto 768 columns (192 x 192 tiles)
+@pytest.mark.parametrize("M,N,K", [(333, 264, 136), (1111, 512, 256), (2048, 768, 3072), (700, 3072, 768)])
 def test_linear_bwd(b, oracle, dtype, M, N, K):
     import torch
     say(f"linear_bwd {dtype} M={M} N={N} K={K}")
