@@ -79,6 +79,26 @@ LABELS = ["gemm.fwd.qkv", "gemm.fwd.proj", "gemm.fwd.fc", "gemm.fwd.fc2", "gemm.
           "bias", "embed.fwd", "embed.bwd", "gradnorm", "adamw"]
 
 
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_gpt2_124m_12x1024.json")
+
+
+def measured_traffic(label: str):
+    """HBM bytes per launch of `label` (FETCH_SIZE + WRITE_SIZE, calibrated on a
+    copy of known size; written by bench_traffic.py), or None when there is no
+    measurement or the kernel sources changed after it was taken."""
+    try:
+        import bench_traffic
+        with open(TRAFFIC_FILE) as fh:
+            t = json.load(fh)
+        if t.get("source_sha256") != bench_traffic.source_hash():
+            return None
+        e = t["labels"][label]
+        return {"bytes": e["fetch_size_bytes_per_launch"] + e["write_size_bytes_per_launch"],
+                "fetch": e["fetch_size_bytes_per_launch"], "write": e["write_size_bytes_per_launch"]}
+    except (OSError, KeyError, ValueError):
+        return None
+
+
 def cpu_baseline(w: syn.Workload, named: dict, seq: int):
     """The oracle (fp32 instantiation, as it stands) on one sequence of `seq`
     tokens, forward + backward, plus one AdamW pass over every parameter;
@@ -206,8 +226,10 @@ def main():
     else:
         achieved = per_launch / avg_launch_s / 1e9
         peak = PEAK_HBM / 1e9
+    tr = measured_traffic(dominant)
     roofline = {"bound": bound, "kernel": dominant, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
-                "frac": round(achieved / peak, 4), "traffic": None,
+                "frac": round(achieved / peak, 4), "traffic": round(tr["bytes"]) if tr else None,
+                "traffic_fetch_write": [round(tr["fetch"]), round(tr["write"])] if tr else None,
                 "avg_launch_ms": round(avg_launch_s * 1e3, 4), "launches_timed": dom_n,
                 "work_per_launch": per_launch}
 
