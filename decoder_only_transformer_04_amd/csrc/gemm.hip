@@ -252,6 +252,13 @@ struct DmaPlan {
 #pragma unroll
         for (int i = 0; i < NI; ++i) src[i] += step;
     }
+    // instruction i of the current stage (no advance; call skip() after all NI)
+    __device__ __forceinline__ void issue_one(char* lds, int wave, int i) {
+#if defined(__HIP_DEVICE_COMPILE__)
+        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src[i],
+                                         (G2_LDS void*)(lds + (wave * NI + i) * 1024), 16, 0, 0);
+#endif
+    }
 };
 
 // MFMA operand fragment: lane l holds rows rb + (l & 31), k = 16 kk + 8 (l >> 5) + 0..7.
@@ -278,11 +285,15 @@ __device__ __forceinline__ bf16x8 tile_frag(const char* lds, int rb, int kk, int
 // groups splitting the contraction, group ks takes steps ks, ks + KS, ... The
 // fragments of the next step are read while the MFMAs of the current one run
 // (two register sets), so each step waits only for its own LDS reads.
-template <int BM, int BN, bool AKC, bool BKC, int BK, int FM, int FN, int WM, int WN, int KS>
+// `dma(d)` issues the d-th of the next stage's ND load instructions of this
+// wave, spread evenly between the MFMAs (ND = 0: the caller issued them before)
+template <int BM, int BN, bool AKC, bool BKC, int BK, int FM, int FN, int WM, int WN, int KS, int ND, class Dma>
 __device__ __forceinline__ void mma_stage(const char* cur, f32x16 (&acc)[FM][FN], int wm, int wn, int ks,
-                                          int lane) {
+                                          int lane, Dma&& dma) {
     constexpr int ABYTES = TileCfg<BM, AKC, BK>::BYTES;
     constexpr int KK = BK / 16 / KS;
+    constexpr int NMF = KK * FM * FN;
+    constexpr int EVERY = ND > 0 ? (NMF / ND > 0 ? NMF / ND : 1) : 1;
 #if G2_GEMM_IGLP >= 0
     __builtin_amdgcn_iglp_opt(G2_GEMM_IGLP);
 #endif
@@ -300,8 +311,16 @@ __device__ __forceinline__ void mma_stage(const char* cur, f32x16 (&acc)[FM][FN]
 #pragma unroll
         for (int i = 0; i < FM; ++i)
 #pragma unroll
-            for (int j = 0; j < FN; ++j)
+            for (int j = 0; j < FN; ++j) {
                 acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[kk & 1][i], bv[kk & 1][j], acc[i][j], 0, 0, 0);
+                const int q = (kk * FM + i) * FN + j;  // constant after unrolling
+                if (ND > 0 && q % EVERY == 0 && q / EVERY < ND) dma(q / EVERY);
+            }
+    }
+    if constexpr (ND > 0) {
+        // any instructions the spread did not reach
+#pragma unroll
+        for (int d = NMF / EVERY; d < ND; ++d) dma(d);
     }
 }
 
@@ -361,7 +380,9 @@ __device__ __forceinline__ void tile_coords(int nm, int nn, int& tm, int& tn) {
 // grid over the tile (each a WM x WN block of 32x32 fragments), times KS groups
 // that split every stage's contraction steps; the KS partial sums are added
 // through LDS before the epilogue.
-template <int BM, int BN, int BK, bool AKC, bool BKC, int EPI, int NS, int WGM = 2, int WGN = 2, int KS = 1>
+// SPREAD: the next stage's loads are issued between the MFMAs instead of before them.
+template <int BM, int BN, int BK, bool AKC, bool BKC, int EPI, int NS, int WGM = 2, int WGN = 2, int KS = 1,
+          bool SPREAD = false>
 __global__ __launch_bounds__(64 * WGM * WGN * KS) void gemm_bf16_kernel(GP p) {
     static_assert(NS >= 2 && NS <= 4, "pipeline depth");
     static_assert(KS == 1 || KS == 2, "contraction split");
@@ -448,8 +469,21 @@ __global__ __launch_bounds__(64 * WGM * WGN * KS) void gemm_bf16_kernel(GP p) {
             wait_vmcnt<0>();
         }
         lds_barrier();  // every wave's share of stage kt is in LDS; stage kt-1 is free
-        if (kt + NS - 1 < nk) issue(smem + ((kt + NS - 1) % NS) * STAGE, kt + NS - 1);
-        mma_stage<BM, BN, AKC, BKC, BK, FM, FN, WM, WN, KS>(smem + (kt % NS) * STAGE, acc, wm, wn, ks, lane);
+        const int knext = kt + NS - 1;
+        char* nbuf = smem + (knext % NS) * STAGE;
+        const bool spread = SPREAD && knext < nk && kbeg + knext * BK + BK <= kend;
+        if (!spread && knext < nk) issue(nbuf, knext);
+        constexpr int NIA = DmaPlan<BM, AKC, BK, NW>::NI, NIB = DmaPlan<BN, BKC, BK, NW>::NI;
+        mma_stage<BM, BN, AKC, BKC, BK, FM, FN, WM, WN, KS, SPREAD ? NIA + NIB : 0>(
+            smem + (kt % NS) * STAGE, acc, wm, wn, ks, lane, [&](int d) {
+                if (!spread) return;
+                if (d < NIA) dA.issue_one(nbuf, wave, d);
+                else dB.issue_one(nbuf + ABYTES, wave, d - NIA);
+            });
+        if (spread) {
+            dA.skip();
+            dB.skip();
+        }
     }
     __syncthreads();  // the epilogue reuses the stage buffers
     // Epilogue: each wave of group 0 stages one 32-row strip of its block at a
@@ -601,12 +635,12 @@ __global__ void splitk_reduce4_kernel(const float* part, int splits, int64_t n, 
 #define G2_GEMM_NS 2
 #endif
 template <int BM, int BN, bool AKC, bool BKC, int EPI, int BK = 64, int NS = G2_GEMM_NS, int WGM = 2, int WGN = 2,
-          int KS = 1>
+          int KS = 1, bool SPREAD = false>
 static hipError_t launch_bf16(const GP& p, int splits, hipStream_t s) {
     const int64_t tiles = (int64_t)((p.N + BN - 1) / BN) * ((p.M + BM - 1) / BM);
     if (tiles > INT32_MAX) return hipErrorInvalidValue;
     dim3 grid((unsigned)tiles, 1, splits);
-    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, BK, AKC, BKC, EPI, NS, WGM, WGN, KS>), grid,
+    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, BK, AKC, BKC, EPI, NS, WGM, WGN, KS, SPREAD>), grid,
                        dim3(64 * WGM * WGN * KS), 0, s, p);
     return hipGetLastError();
 }
@@ -625,7 +659,8 @@ static hipError_t pick_tile_bf16(const GP& p, int splits, hipStream_t s) {
     // Tile policy from measurements on the 124M model's shapes (M = 12288 tokens):
     //  - long contractions onto 768-wide outputs (K >= 2048, N a multiple of 192):
     //    192 x 192 tiles, one per CU in a single wave of 256 tiles, eight waves in
-    //    two groups splitting each 64-deep stage;
+    //    two groups splitting each 64-deep stage; for the very long input-gradient
+    //    contraction (K >= 8192) the next stage's loads are spread between the MFMAs;
     //  - the vocabulary-wide forward product: 256 x 256 tiles, eight waves;
     //  - otherwise 128 x 128 tiles, two or three workgroups per CU, 32-deep
     //    stages when A is K-contiguous (forward and input gradients), 64-deep for
@@ -633,8 +668,10 @@ static hipError_t pick_tile_bf16(const GP& p, int splits, hipStream_t s) {
     if constexpr (!AKC) {
         return launch_bf16<128, 128, AKC, BKC, EPI, 64>(p, splits, s);
     } else {
-        if (p.N % 192 == 0 && p.N <= 1536 && p.K >= 2048 && splits == 1)
+        if (p.N % 192 == 0 && p.N <= 1536 && p.K >= 2048 && splits == 1) {
+            if (!BKC && p.K >= 8192) return launch_bf16<192, 192, AKC, BKC, EPI, 64, 2, 2, 2, 2, true>(p, splits, s);
             return launch_bf16<192, 192, AKC, BKC, EPI, 64, 2, 2, 2, 2>(p, splits, s);
+        }
         if (BKC && p.N >= 8192) return launch_bf16<256, 256, AKC, BKC, EPI, 64, 2, 2, 4, 1>(p, splits, s);
         return launch_bf16<128, 128, AKC, BKC, EPI, 32>(p, splits, s);
     }
