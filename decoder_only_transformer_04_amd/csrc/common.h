@@ -112,12 +112,16 @@ hipError_t encoder_fwd(int dtype, const int32_t* idx, const float* wte32, const 
                        uint32_t* status, hipStream_t s);
 hipError_t layernorm_fwd(int dtype, const float* x, const float* g, const float* b, float eps, void* y,
                          float* mean, float* rstd, int64_t rows, int C, hipStream_t s);
+// with_res: the partial rows also carry the column sums of the updated dres
+// (layout per partial row: dg[C], db[C], dres[C]; else dg[C], db[C])
 hipError_t layernorm_bwd(int dtype, const float* dy, const float* x, const float* mean, const float* rstd,
-                         const float* g, float* dres, void* dres_act, float* part, int part_rows, int64_t rows,
-                         int C, int add, hipStream_t s);
+                         const float* g, float* dres, void* dres_act, float* part, int part_rows, int64_t rows, int C,
+                         int add, int with_res, hipStream_t s);
 int ln_bwd_partial_rows(int64_t rows);  // partial rows layernorm_bwd writes
 hipError_t colsum_finish2(const float* part, int part_rows, int ld, float* out_a, int na, float* out_b, int nb,
                           int accumulate, hipStream_t s);
+hipError_t colsum_finish3(const float* part, int part_rows, int ld, float* out_a, int na, float* out_b, int nb,
+                          float* out_c, int nc, int accumulate, hipStream_t s);
 hipError_t bias_grad(int dtype, const void* dY, int64_t rows, int N, float* part, int part_rows, float* db,
                      int accumulate, hipStream_t s);
 hipError_t attention_fwd(int dtype, int B, int T, int C, int H, const void* qkv, void* out, float* lse,

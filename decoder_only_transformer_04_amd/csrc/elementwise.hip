@@ -339,17 +339,18 @@ int ln_bwd_partial_rows(int64_t rows) { return (int)((rows + 15) / 16); }
 template <int NJ4, class T>
 __global__ __launch_bounds__(256) void ln_bwd_v4(const float* dy, const float* x, const float* mean, const float* rstd,
                                                  const float* g, float* dres, T* dres_act, float* part, int64_t rows,
-                                                 int C, int add) {
-    __shared__ float red[4][2][256 * NJ4];
+                                                 int C, int add, int with_res) {
+    __shared__ float red[4][256 * NJ4];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int C4 = C / 4;
-    float4 gg[NJ4], pg[NJ4], pb[NJ4];
+    float4 gg[NJ4], pg[NJ4], pb[NJ4], pr[NJ4];
 #pragma unroll
     for (int j = 0; j < NJ4; ++j) {
         const int c4 = lane + 64 * j;
         gg[j] = c4 < C4 ? ((const float4*)g)[c4] : make_float4(0.f, 0.f, 0.f, 0.f);
         pg[j] = make_float4(0.f, 0.f, 0.f, 0.f);
         pb[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+        pr[j] = make_float4(0.f, 0.f, 0.f, 0.f);
     }
     for (int rr = 0; rr < 4; ++rr) {
         const int64_t row = (int64_t)blockIdx.x * 16 + wave * 4 + rr;
@@ -394,34 +395,39 @@ __global__ __launch_bounds__(256) void ln_bwd_v4(const float* dy, const float* x
                 }
                 *dp = o;
                 if (dres_act) st4<T>(dres_act + row * C + 4 * c4, o);
+                pr[j].x += o.x; pr[j].y += o.y; pr[j].z += o.z; pr[j].w += o.w;
             }
         }
     }
+    // block partials, one quantity at a time through the same LDS rows:
+    // dg (dy * xhat), db (dy) and, with with_res, the column sums of the
+    // updated dres (the bias gradient of the linear layer that feeds it)
+    float* out = part + (int64_t)blockIdx.x * (with_res ? 3 : 2) * C;
+    auto emit = [&](const float4 (&v)[NJ4], float* dst) {
 #pragma unroll
-    for (int j = 0; j < NJ4; ++j) {
-        const int c = 4 * (lane + 64 * j);
-        red[wave][0][c] = pg[j].x; red[wave][0][c + 1] = pg[j].y; red[wave][0][c + 2] = pg[j].z; red[wave][0][c + 3] = pg[j].w;
-        red[wave][1][c] = pb[j].x; red[wave][1][c + 1] = pb[j].y; red[wave][1][c + 2] = pb[j].z; red[wave][1][c + 3] = pb[j].w;
-    }
-    __syncthreads();
-    for (int c = threadIdx.x; c < C; c += 256) {
-        part[(int64_t)blockIdx.x * 2 * C + c] = ((red[0][0][c] + red[1][0][c]) + red[2][0][c]) + red[3][0][c];
-        part[(int64_t)blockIdx.x * 2 * C + C + c] = ((red[0][1][c] + red[1][1][c]) + red[2][1][c]) + red[3][1][c];
-    }
+        for (int j = 0; j < NJ4; ++j) *(float4*)&red[wave][4 * (lane + 64 * j)] = v[j];
+        __syncthreads();
+        for (int c = threadIdx.x; c < C; c += 256) dst[c] = ((red[0][c] + red[1][c]) + red[2][c]) + red[3][c];
+        __syncthreads();
+    };
+    emit(pg, out);
+    emit(pb, out + C);
+    if (with_res) emit(pr, out + 2 * C);
 }
 
 template <int NJ, class T>
 __global__ __launch_bounds__(256) void ln_bwd_kernel(const float* dy, const float* x, const float* mean,
                                                      const float* rstd, const float* g, float* dres, T* dres_act,
-                                                     float* part, int64_t rows, int C, int add) {
-    __shared__ float red[4][2][64 * NJ];
+                                                     float* part, int64_t rows, int C, int add, int with_res) {
+    __shared__ float red[4][64 * NJ];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    float pg[NJ], pb[NJ], gg[NJ];
+    float pg[NJ], pb[NJ], pr[NJ], gg[NJ];
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
         const int c = lane + 64 * j;
         pg[j] = 0.0f;
         pb[j] = 0.0f;
+        pr[j] = 0.0f;
         gg[j] = c < C ? g[c] : 0.0f;
     }
     for (int rr = 0; rr < 4; ++rr) {
@@ -451,31 +457,33 @@ __global__ __launch_bounds__(256) void ln_bwd_kernel(const float* dy, const floa
                 const float o = add ? dres[row * C + c] + dx : dx;
                 dres[row * C + c] = o;
                 if (dres_act) Act<T>::st(dres_act, row * C + c, o);
+                pr[j] += o;
             }
         }
     }
+    float* out = part + (int64_t)blockIdx.x * (with_res ? 3 : 2) * C;
+    auto emit = [&](const float (&v)[NJ], float* dst) {
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-        red[wave][0][lane + 64 * j] = pg[j];
-        red[wave][1][lane + 64 * j] = pb[j];
-    }
-    __syncthreads();
-    for (int c = threadIdx.x; c < C; c += 256) {
-        part[(int64_t)blockIdx.x * 2 * C + c] = ((red[0][0][c] + red[1][0][c]) + red[2][0][c]) + red[3][0][c];
-        part[(int64_t)blockIdx.x * 2 * C + C + c] = ((red[0][1][c] + red[1][1][c]) + red[2][1][c]) + red[3][1][c];
-    }
+        for (int j = 0; j < NJ; ++j) red[wave][lane + 64 * j] = v[j];
+        __syncthreads();
+        for (int c = threadIdx.x; c < C; c += 256) dst[c] = ((red[0][c] + red[1][c]) + red[2][c]) + red[3][c];
+        __syncthreads();
+    };
+    emit(pg, out);
+    emit(pb, out + C);
+    if (with_res) emit(pr, out + 2 * C);
 }
 
 template <class T>
 static hipError_t ln_bwd_dispatch(const float* dy, const float* x, const float* mean, const float* rstd,
                                   const float* g, float* dres, T* dres_act, float* part, int64_t rows, int C, int add,
-                                  hipStream_t s) {
+                                  int with_res, hipStream_t s) {
     dim3 grid(nblk(rows, 16)), blk(256);
     if (C % 4 == 0) {
         const int nj4 = (C / 4 + 63) / 64;
 #define G2_LNB4(N)                                                                                              \
     hipLaunchKernelGGL((ln_bwd_v4<N, T>), grid, blk, 0, s, dy, x, mean, rstd, g, dres, dres_act, part, rows, C, \
-                       add)
+                       add, with_res)
         if (nj4 <= 1) G2_LNB4(1);
         else if (nj4 <= 2) G2_LNB4(2);
         else if (nj4 <= 3) G2_LNB4(3);
@@ -489,7 +497,7 @@ static hipError_t ln_bwd_dispatch(const float* dy, const float* x, const float* 
     const int nj = (C + 63) / 64;
 #define G2_LNB(N)                                                                                                  \
     hipLaunchKernelGGL((ln_bwd_kernel<N, T>), grid, blk, 0, s, dy, x, mean, rstd, g, dres, dres_act, part, rows, C, \
-                       add)
+                       add, with_res)
     if (nj <= 2) G2_LNB(2);
     else if (nj <= 4) G2_LNB(4);
     else if (nj <= 6) G2_LNB(6);
@@ -503,31 +511,37 @@ static hipError_t ln_bwd_dispatch(const float* dy, const float* x, const float* 
 
 hipError_t layernorm_bwd(int dtype, const float* dy, const float* x, const float* mean, const float* rstd,
                          const float* g, float* dres, void* dres_act, float* part, int part_rows, int64_t rows, int C,
-                         int add, hipStream_t s) {
+                         int add, int with_res, hipStream_t s) {
     if (rows == 0) return hipSuccess;
     if (part_rows < ln_bwd_partial_rows(rows)) return hipErrorInvalidValue;
     if (dtype == GPT2_DTYPE_BF16)
-        return ln_bwd_dispatch<bf16_t>(dy, x, mean, rstd, g, dres, (bf16_t*)dres_act, part, rows, C, add, s);
-    return ln_bwd_dispatch<float>(dy, x, mean, rstd, g, dres, (float*)dres_act, part, rows, C, add, s);
+        return ln_bwd_dispatch<bf16_t>(dy, x, mean, rstd, g, dres, (bf16_t*)dres_act, part, rows, C, add, with_res, s);
+    return ln_bwd_dispatch<float>(dy, x, mean, rstd, g, dres, (float*)dres_act, part, rows, C, add, with_res, s);
 }
 
-// out_a[c] (+)= sum_p part[p][c] for c < na; out_b[c] (+)= sum_p part[p][na + c] for c < nb.
+// Column sums of partial rows into up to three outputs: out_a[c] (+)= sum_p
+// part[p][c] for c < na, then out_b for the next nb columns, out_c for the next nc.
+__device__ __forceinline__ float* colsum_dst(int col, float* out_a, int na, float* out_b, int nb, float* out_c) {
+    return col < na ? out_a + col : col < na + nb ? out_b + (col - na) : out_c + (col - na - nb);
+}
+
 // 64 columns per block, 16 row slices summed in a fixed order.
 __global__ __launch_bounds__(1024) void colsum_kernel(const float* part, int prows, int ld, float* out_a, int na,
-                                                      float* out_b, int nb, int accumulate) {
+                                                      float* out_b, int nb, float* out_c, int nc, int accumulate) {
     __shared__ float red[16][65];
     const int cl = threadIdx.x & 63, sl = threadIdx.x >> 6;
     const int c = blockIdx.x * 64 + cl;
+    const int ncol = na + nb + nc;
     float s = 0.0f;
-    if (c < na + nb)
+    if (c < ncol)
         for (int p = sl; p < prows; p += 16) s += part[(int64_t)p * ld + c];
     red[sl][cl] = s;
     __syncthreads();
-    if (sl == 0 && c < na + nb) {
+    if (sl == 0 && c < ncol) {
         float t = red[0][cl];
 #pragma unroll
         for (int k = 1; k < 16; ++k) t += red[k][cl];
-        float* o = c < na ? out_a + c : out_b + (c - na);
+        float* o = colsum_dst(c, out_a, na, out_b, nb, out_c);
         *o = accumulate ? *o + t : t;
     }
 }
@@ -536,11 +550,12 @@ __global__ __launch_bounds__(1024) void colsum_kernel(const float* part, int pro
 // independent accumulators (so a thread keeps four loads in flight), then the
 // slices are combined in a fixed order through LDS.
 __global__ __launch_bounds__(1024) void colsum4_kernel(const float* part, int prows, int ld, float* out_a, int na,
-                                                       float* out_b, int nb, int accumulate) {
+                                                       float* out_b, int nb, float* out_c, int nc, int accumulate) {
     __shared__ float4 red[64][17];
     const int cl = threadIdx.x & 15, sl = threadIdx.x >> 4;
     const int c = blockIdx.x * 64 + cl * 4;
-    const bool ok = c < na + nb;
+    const int ncol = na + nb + nc;
+    const bool ok = c < ncol;
     float4 acc[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) acc[u] = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -573,24 +588,29 @@ __global__ __launch_bounds__(1024) void colsum4_kernel(const float* part, int pr
         float sum = 0.0f;
         for (int k = 0; k < 64; ++k) sum += (&red[k][q].x)[e];
         const int col = blockIdx.x * 64 + j;
-        if (col < na + nb) {
-            float* o = col < na ? out_a + col : out_b + (col - na);
+        if (col < ncol) {
+            float* o = colsum_dst(col, out_a, na, out_b, nb, out_c);
             *o = accumulate ? *o + sum : sum;
         }
     }
 }
 
-hipError_t colsum_finish2(const float* part, int part_rows, int ld, float* out_a, int na, float* out_b, int nb,
-                          int accumulate, hipStream_t s) {
-    if (na + nb == 0) return hipSuccess;
-    if (na % 4 == 0 && nb % 4 == 0 && ld % 4 == 0) {
-        hipLaunchKernelGGL(colsum4_kernel, dim3(nblk(na + nb, 64)), dim3(1024), 0, s, part, part_rows, ld, out_a, na,
-                           out_b, nb, accumulate);
+hipError_t colsum_finish3(const float* part, int part_rows, int ld, float* out_a, int na, float* out_b, int nb,
+                          float* out_c, int nc, int accumulate, hipStream_t s) {
+    const int ncol = na + nb + nc;
+    if (ncol == 0) return hipSuccess;
+    if (na % 4 == 0 && nb % 4 == 0 && nc % 4 == 0 && ld % 4 == 0) {
+        hipLaunchKernelGGL(colsum4_kernel, dim3(nblk(ncol, 64)), dim3(1024), 0, s, part, part_rows, ld, out_a, na,
+                           out_b, nb, out_c, nc, accumulate);
         return hipGetLastError();
     }
-    hipLaunchKernelGGL(colsum_kernel, dim3(nblk(na + nb, 64)), dim3(1024), 0, s, part, part_rows, ld, out_a, na,
-                       out_b, nb, accumulate);
+    hipLaunchKernelGGL(colsum_kernel, dim3(nblk(ncol, 64)), dim3(1024), 0, s, part, part_rows, ld, out_a, na, out_b,
+                       nb, out_c, nc, accumulate);
     return hipGetLastError();
+}
+hipError_t colsum_finish2(const float* part, int part_rows, int ld, float* out_a, int na, float* out_b, int nb,
+                          int accumulate, hipStream_t s) {
+    return colsum_finish3(part, part_rows, ld, out_a, na, out_b, nb, nullptr, 0, accumulate, s);
 }
 
 // bias gradient: column sums of dY [rows, N] (act). Vector path (N % 8 == 0):

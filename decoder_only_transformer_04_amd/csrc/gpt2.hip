@@ -362,29 +362,37 @@ int gpt2_backward(gpt2_ctx* x, float loss_scale, int32_t zero_grads) {
     G2_T("gemm.dgrad.head", linear_dgrad(dt, s, EPI_F32, M, Vp, C, at<char>(x, ap.logits), Vp, wptr(x, pl.wte), dtmp, nullptr, alpha));
     G2_T("gemm.wgrad.head", linear_wgrad(dt, s, M, Vp, C, at<char>(x, ap.logits), Vp, at<char>(x, ap.xf), gf(x, pl.wte), acc, alpha, sb,
                         sbytes));
+    // Each LayerNorm backward also sums the columns of the residual gradient it
+    // leaves behind, which is the bias gradient of the linear layer writing into
+    // the residual stream just before it: fc2 of the layer below for ln_f and
+    // ln1, the attention projection for ln2.
+    const int Ltop = c.n_layer - 1;
+    float* b_fc2_top = gf(x, pl.layer[Ltop].b_fc2);
     G2_T("ln.bwd", layernorm_bwd(dt, dtmp, at<float>(x, ap.xL), at<float>(x, ap.mf), at<float>(x, ap.rf), pf(x, pl.lnf_g),
-                         dres, bf ? dres_act : nullptr, part, ap.ln_part_rows, M, C, 0, s));
-    G2_T("colsum", colsum_finish2(part, ln_bwd_partial_rows(M), 2 * C, gf(x, pl.lnf_g), C, gf(x, pl.lnf_b), C, acc, s));
+                         dres, bf ? dres_act : nullptr, part, ap.ln_part_rows, M, C, 0, b_fc2_top != nullptr, s));
+    G2_T("colsum", colsum_finish3(part, ln_bwd_partial_rows(M), (b_fc2_top ? 3 : 2) * C, gf(x, pl.lnf_g), C,
+                                  gf(x, pl.lnf_b), C, b_fc2_top, b_fc2_top ? C : 0, acc, s));
     for (int l = c.n_layer - 1; l >= 0; --l) {
         const LayerW& w = pl.layer[l];
         // x_out = x_mid + fc2(gelu(fc(ln2(x_mid))))
         G2_T("gemm.dgrad.fc2", linear_dgrad(dt, s, EPI_GELU_BWD, M, C, F, dres_act, C, wptr(x, w.w_fc2), at<char>(x, ap.dF),
                             at<char>(x, ap.fch[l]), 1.0f));
         G2_T("gemm.wgrad.fc2", linear_wgrad(dt, s, M, C, F, dres_act, C, at<char>(x, ap.fcg[l]), gf(x, w.w_fc2), acc, 1.0f, sb, sbytes));
-        if (w.b_fc2 >= 0) G2_T("bias", bias_grad(dt, dres_act, M, C, bpart, ap.bias_part_rows, gf(x, w.b_fc2), acc, s));
         G2_T("gemm.dgrad.fc", linear_dgrad(dt, s, EPI_F32, M, F, C, at<char>(x, ap.dF), F, wptr(x, w.w_fc), dtmp, nullptr, 1.0f));
         G2_T("gemm.wgrad.fc", linear_wgrad(dt, s, M, F, C, at<char>(x, ap.dF), F, at<char>(x, ap.ln2[l]), gf(x, w.w_fc), acc, 1.0f, sb,
                             sbytes));
         if (w.b_fc >= 0) G2_T("bias", bias_grad(dt, at<char>(x, ap.dF), M, F, bpart, ap.bias_part_rows, gf(x, w.b_fc), acc, s));
+        float* b_proj = gf(x, w.b_proj);
         G2_T("ln.bwd", layernorm_bwd(dt, dtmp, at<float>(x, ap.xmid[l]), at<float>(x, ap.m2[l]), at<float>(x, ap.r2[l]),
-                             pf(x, w.ln2_g), dres, bf ? dres_act : nullptr, part, ap.ln_part_rows, M, C, 1, s));
-        G2_T("colsum", colsum_finish2(part, ln_bwd_partial_rows(M), 2 * C, gf(x, w.ln2_g), C, gf(x, w.ln2_b), C, acc, s));
+                             pf(x, w.ln2_g), dres, bf ? dres_act : nullptr, part, ap.ln_part_rows, M, C, 1,
+                             b_proj != nullptr, s));
+        G2_T("colsum", colsum_finish3(part, ln_bwd_partial_rows(M), (b_proj ? 3 : 2) * C, gf(x, w.ln2_g), C,
+                                      gf(x, w.ln2_b), C, b_proj, b_proj ? C : 0, acc, s));
         // x_mid = x_in + proj(attn(ln1(x_in)))
         G2_T("gemm.dgrad.proj", linear_dgrad(dt, s, EPI_STORE, M, C, C, dres_act, C, wptr(x, w.w_proj), at<char>(x, ap.datt), nullptr,
                             1.0f));
         G2_T("gemm.wgrad.proj", linear_wgrad(dt, s, M, C, C, dres_act, C, at<char>(x, ap.att[l]), gf(x, w.w_proj), acc, 1.0f, sb,
                             sbytes));
-        if (w.b_proj >= 0) G2_T("bias", bias_grad(dt, dres_act, M, C, bpart, ap.bias_part_rows, gf(x, w.b_proj), acc, s));
         {
             const char* qkv_l = at<char>(x, ap.qkv[l]);
             const char* att_l = at<char>(x, ap.att[l]);
@@ -407,9 +415,12 @@ int gpt2_backward(gpt2_ctx* x, float loss_scale, int32_t zero_grads) {
                             1.0f, sb, sbytes));
         if (w.b_qkv >= 0)
             G2_T("bias", bias_grad(dt, at<char>(x, ap.dqkv), M, 3 * C, bpart, ap.bias_part_rows, gf(x, w.b_qkv), acc, s));
+        float* b_fc2_below = l > 0 ? gf(x, pl.layer[l - 1].b_fc2) : nullptr;
         G2_T("ln.bwd", layernorm_bwd(dt, dtmp, at<float>(x, ap.x[l]), at<float>(x, ap.m1[l]), at<float>(x, ap.r1[l]),
-                             pf(x, w.ln1_g), dres, bf ? dres_act : nullptr, part, ap.ln_part_rows, M, C, 1, s));
-        G2_T("colsum", colsum_finish2(part, ln_bwd_partial_rows(M), 2 * C, gf(x, w.ln1_g), C, gf(x, w.ln1_b), C, acc, s));
+                             pf(x, w.ln1_g), dres, bf ? dres_act : nullptr, part, ap.ln_part_rows, M, C, 1,
+                             b_fc2_below != nullptr, s));
+        G2_T("colsum", colsum_finish3(part, ln_bwd_partial_rows(M), (b_fc2_below ? 3 : 2) * C, gf(x, w.ln1_g), C,
+                                      gf(x, w.ln1_b), C, b_fc2_below, b_fc2_below ? C : 0, acc, s));
     }
     // embedding: dwte[idx[m]] += dres[m] (after the head's contribution), dwpe[t] (=|+=) sum_b dres[b,t]
     G2_T("embed.bwd", encoder_bwd(at<int32_t>(x, x->idx_save), dres, gf(x, pl.wte), gf(x, pl.wpe), M, T, C, c.vocab,
@@ -576,7 +587,7 @@ int gpt2_op_layernorm_bwd(int64_t rows, int32_t C, const float* d_dy, const floa
     const int pr = std::max(1, ln_bwd_partial_rows(rows));
     float* tmp = nullptr;
     if (hipMallocAsync((void**)&tmp, (size_t)pr * 2 * C * 4, s) != hipSuccess) return GPT2_EHIP;
-    hipError_t e = layernorm_bwd(GPT2_DTYPE_F32, d_dy, d_x, d_mean, d_rstd, d_g, d_dx, nullptr, tmp, pr, rows, C, 1, s);
+    hipError_t e = layernorm_bwd(GPT2_DTYPE_F32, d_dy, d_x, d_mean, d_rstd, d_g, d_dx, nullptr, tmp, pr, rows, C, 1, 0, s);
     if (e == hipSuccess) e = colsum_finish2(tmp, ln_bwd_partial_rows(rows), 2 * C, d_dg, C, d_db, C, 0, s);
     (void)hipFreeAsync(tmp, s);
     return e == hipSuccess ? GPT2_OK : GPT2_EHIP;

@@ -134,7 +134,7 @@ ArenaPlan make_arena_plan(const gpt2_config& c, const ParamLayout& pl, int B, in
         a.datt = take(M * C * ab);
         a.attD = take((size_t)B * H * T * 4);
         a.ln_part_rows = (int)((M + 15) / 16);
-        a.ln_part = take((size_t)a.ln_part_rows * 2 * C * 4);
+        a.ln_part = take((size_t)a.ln_part_rows * 3 * C * 4);  // dg, db and the dres column sums
         size_t maxN = 3 * C > F ? 3 * C : F;
         a.bias_part_rows = (int)((M + 63) / 64);
         a.bias_part = take((size_t)a.bias_part_rows * maxN * 4);
