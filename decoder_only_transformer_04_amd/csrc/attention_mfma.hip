@@ -22,6 +22,7 @@
 // row reads (MFMA operands with the contraction index along the row) and for
 // transpose reads (contraction index down the rows).
 #include <cmath>
+#include <type_traits>
 
 #include "device.h"
 
@@ -68,6 +69,49 @@ __device__ __forceinline__ void tile_store(char* lds, const TileRegs& t, int tid
         const int row = c >> 3, ch = c & 7;
         *(uint4*)(lds + row * 128 + ((ch ^ swz(row)) << 4)) = t.v[i];
     }
+}
+
+// 64 x 64 bf16 tile streamed straight into LDS (gfx950 global_load_lds_dwordx4):
+// wave w fills rows 16 w .. 16 w + 15 with two 1 KB instructions; lane l of
+// instruction i lands at row 16 w + 8 i + l / 8, slot l % 8, so it fetches the
+// chunk that the swizzle places there. Rows past the end are clamped to the
+// last row (finite data; every consumer masks those keys or queries).
+struct TileDma {
+    int roff[2];  // tile row of this lane's chunk in each instruction
+    int coff[2];  // element offset of the chunk within the row
+    __device__ __forceinline__ void init(int w, int lane) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int row = 16 * w + 8 * i + (lane >> 3);
+            roff[i] = row;
+            coff[i] = ((lane & 7) ^ swz(row)) * 8;
+        }
+    }
+    __device__ __forceinline__ void issue(char* lds, const bf16_t* g, int64_t ld, int r0, int rmax, int w) const {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const bf16_t* src = g + (int64_t)min(r0 + roff[i], rmax - 1) * ld + coff[i];
+#if defined(__HIP_DEVICE_COMPILE__)
+            __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
+                                             (G2_LDS void*)(lds + (2 * w + i) * 1024), 16, 0, 0);
+#endif
+        }
+    }
+};
+
+// wait until at most N vector-memory operations of this wave are outstanding
+template <int N>
+__device__ __forceinline__ void att_wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+// workgroup barrier ordering LDS only (a __syncthreads() would also drain the
+// DMA loads still in flight for later tiles)
+__device__ __forceinline__ void att_lds_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
 }
 
 // operand with the contraction index along the tile row: lane l holds row
@@ -133,9 +177,20 @@ __device__ __forceinline__ void block_coords(int T, int H, bool late_first, int&
 }  // namespace
 
 // ------------------------------------------------------------------ forward
-__global__ __launch_bounds__(256) void attn_fwd_d64(const bf16_t* qkv, bf16_t* out, float* lse, int T, int C, int H,
-                                                    float sl2) {
-    __shared__ __attribute__((aligned(16))) char smem[2][2][kTileBytes];
+// Lazy rescaling: the running maximum m (scaled, base 2) only moves when some
+// lane's tile maximum exceeds it by more than kLazy; otherwise the stale m is
+// kept and probabilities may reach 2^kLazy. O and l use the same m throughout,
+// so the final O / l and lse = m + log2(l) are exact up to rounding.
+constexpr float kLazy = 8.0f;
+
+#ifndef G2_ATT_FWD_OCC
+#define G2_ATT_FWD_OCC 3
+#endif
+// three workgroups (waves per SIMD) per CU: registers capped at 168. K/V tiles
+// stream into a three-deep LDS ring (48 KB) by DMA, two tiles ahead.
+__global__ __launch_bounds__(256, G2_ATT_FWD_OCC) void attn_fwd_d64(const bf16_t* qkv, bf16_t* out, float* lse, int T,
+                                                                    int C, int H, float sl2) {
+    __shared__ __attribute__((aligned(16))) char smem[3][2][kTileBytes];
     int qb, h, b;
     block_coords(T, H, true, qb, h, b);
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 5;
@@ -146,28 +201,35 @@ __global__ __launch_bounds__(256) void attn_fwd_d64(const bf16_t* qkv, bf16_t* o
     const bf16_t* Vg = base + 2 * C + h * 64;
     const int q0 = qb * 128 + w * 32;
     const int qi = q0 + (lane & 31);
+    const int kend = min(T, qb * 128 + 128);
+    const int nkt = (kend + 63) / 64;
+    TileDma dma;
+    dma.init(w, lane);
+    auto issue = [&](int kt) {
+        char* buf = smem[kt % 3][0];
+        dma.issue(buf, Kg, rs, kt * 64, T, w);
+        dma.issue(buf + kTileBytes, Vg, rs, kt * 64, T, w);
+    };
+    issue(0);
+    if (nkt > 1) issue(1);
     bf16x8 qf[4];
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) qf[kk] = load8(Qg + (int64_t)qi * rs + 16 * kk + 8 * g, qi < T);
     f32x16 o[2] = {zero16(), zero16()};
+    // m is shared by the two half-waves (they hold different keys of the same
+    // query); l is kept per half-wave and combined at the end
     float m = -INFINITY, l = 0.0f;
-    const int kend = min(T, qb * 128 + 128);
-    const int nkt = (kend + 63) / 64;
-    TileRegs rk, rv;
-    tile_load(rk, Kg, rs, 0, T, tid);
-    tile_load(rv, Vg, rs, 0, T, tid);
-    tile_store(smem[0][0], rk, tid);
-    tile_store(smem[0][1], rv, tid);
-    __syncthreads();
     for (int kt = 0; kt < nkt; ++kt) {
+        // tile kt has landed once at most the next tile's 4 loads are pending
+        // (the Q loads above were issued after tiles 0 and 1 and are waited for
+        // by the compiler before their first use)
+        if (kt + 1 < nkt) att_wait_vmcnt<4>();
+        else att_wait_vmcnt<0>();
+        att_lds_barrier();  // every wave's share of tile kt is in LDS; tile kt-1's slot is free
+        if (kt + 2 < nkt) issue(kt + 2);
         const int k0 = kt * 64;
-        const bool more = kt + 1 < nkt;
-        if (more) {
-            tile_load(rk, Kg, rs, k0 + 64, T, tid);
-            tile_load(rv, Vg, rs, k0 + 64, T, tid);
-        }
-        const char* Ks = smem[kt & 1][0];
-        const char* Vs = smem[kt & 1][1];
+        const char* Ks = smem[kt % 3][0];
+        const char* Vs = smem[kt % 3][1];
         if (k0 <= q0 + 31) {
             f32x16 s[2];
 #pragma unroll
@@ -191,40 +253,33 @@ __global__ __launch_bounds__(256) void attn_fwd_d64(const bf16_t* qkv, bf16_t* o
             for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kh][r]);
-            mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-            // running max in the scaled base-2 domain; raw scores scale by sl2 > 0
-            const float mn = fmaxf(m, mx * sl2);
-            if (__any(mn != m)) {
+            const float mt = fmaxf(mx, __shfl_xor(mx, 32, 64)) * sl2;  // raw scores scale by sl2 > 0
+            if (__any(mt > m + kLazy)) {
+                const float mn = fmaxf(m, mt);
                 const float corr = fexp2(m - mn);
                 l *= corr;
 #pragma unroll
                 for (int dt = 0; dt < 2; ++dt)
 #pragma unroll
                     for (int r = 0; r < 16; ++r) o[dt][r] *= corr;
+                m = mn;
             }
-            float ls = 0.0f;
             bf16x8 pk[4];
 #pragma unroll
             for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    const float p = fexp2(fmaf(s[kh][r], sl2, -mn));
-                    ls += p;
+                    const float p = fexp2(fmaf(s[kh][r], sl2, -m));
+                    l += p;
                     pk[2 * kh + (r >> 3)][r & 7] = (__bf16)p;
                 }
-            l += ls + __shfl_xor(ls, 32, 64);
-            m = mn;
 #pragma unroll
             for (int dt = 0; dt < 2; ++dt)
 #pragma unroll
                 for (int u = 0; u < 4; ++u) o[dt] = mfma(frag_col(Vs, 16 * u, 32 * dt, lane), pk[u], o[dt]);
         }
-        if (more) {
-            tile_store(smem[(kt + 1) & 1][0], rk, tid);
-            tile_store(smem[(kt + 1) & 1][1], rv, tid);
-        }
-        __syncthreads();
     }
+    l += __shfl_xor(l, 32, 64);
     if (qi < T) {
         const float inv = 1.0f / l;
         bf16_t* orow = out + ((int64_t)b * T + qi) * C + h * 64;
@@ -245,9 +300,11 @@ __global__ __launch_bounds__(256) void attn_fwd_d64(const bf16_t* qkv, bf16_t* o
 // ------------------------------------------------------------------ backward: D = rowsum(dO * O)
 // Eight lanes per (token, head) row, each taking 16 bytes of O and of dO, so a
 // wave reads 1 KB of contiguous memory from each; the eight partial dot
-// products are combined with lane shuffles (fixed order).
-__global__ __launch_bounds__(256) void attn_bwd_pre_d64(const bf16_t* out, const bf16_t* dout, float* Dbuf, int B,
-                                                        int T, int C, int H) {
+// products are combined with lane shuffles (fixed order). Dbuf holds D in its
+// first B H T floats and lse in base 2 (lse * log2 e) in the next B H T, the
+// form both backward kernels consume.
+__global__ __launch_bounds__(256) void attn_bwd_pre_d64(const bf16_t* out, const bf16_t* dout, const float* lse,
+                                                        float* Dbuf, int B, int T, int C, int H) {
     const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     const int64_t n = (int64_t)B * T * H * 8;
     const bool ok = t < n;
@@ -269,7 +326,9 @@ __global__ __launch_bounds__(256) void attn_bwd_pre_d64(const bf16_t* out, const
     s += __shfl_xor(s, 4, 64);
     if (ok && c == 0) {
         const int64_t b = m / T, i = m - b * T;
-        Dbuf[(b * H + h) * T + i] = s;
+        const int64_t r = (b * H + h) * T + i;
+        Dbuf[r] = s;
+        Dbuf[(int64_t)B * H * T + r] = lse[r] * kLog2e;
     }
 }
 
@@ -277,7 +336,7 @@ __global__ __launch_bounds__(256) void attn_bwd_pre_d64(const bf16_t* out, const
 __global__ __launch_bounds__(256) void attn_bwd_dq_d64(const bf16_t* qkv, const bf16_t* dout, const float* lse,
                                                        const float* Dbuf, bf16_t* dqkv, int T, int C, int H,
                                                        float sl2, float scale) {
-    __shared__ __attribute__((aligned(16))) char smem[2][2][kTileBytes];
+    __shared__ __attribute__((aligned(16))) char smem[3][2][kTileBytes];
     int qb, h, b;
     block_coords(T, H, true, qb, h, b);
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 5;
@@ -290,6 +349,18 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_d64(const bf16_t* qkv, const 
     const int q0 = qb * 128 + w * 32;
     const int qi = q0 + (lane & 31);
     const bool qok = qi < T;
+    const int kend = min(T, qb * 128 + 128);
+    const int nkt = (kend + 63) / 64;
+    // K/V tiles stream into a three-deep LDS ring by DMA, two tiles ahead
+    TileDma dma;
+    dma.init(w, lane);
+    auto issue = [&](int kt) {
+        char* buf = smem[kt % 3][0];
+        dma.issue(buf, Kg, rs, kt * 64, T, w);
+        dma.issue(buf + kTileBytes, Vg, rs, kt * 64, T, w);
+    };
+    issue(0);
+    if (nkt > 1) issue(1);
     bf16x8 qf[4], df[4];
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
@@ -297,26 +368,18 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_d64(const bf16_t* qkv, const 
         df[kk] = load8(dOg + (int64_t)qi * C + 16 * kk + 8 * g, qok);
     }
     const int64_t lb = ((int64_t)b * H + h) * T;
-    const float lse2 = qok ? lse[lb + qi] * kLog2e : 0.0f;
+    const float* L2 = Dbuf + (int64_t)gridDim.x / ((T + 127) / 128) * T;  // lse * log2 e after the B H T values of D
+    const float lse2 = qok ? L2[lb + qi] : 0.0f;
     const float Dq = qok ? Dbuf[lb + qi] : 0.0f;
     f32x16 dq[2] = {zero16(), zero16()};
-    const int kend = min(T, qb * 128 + 128);
-    const int nkt = (kend + 63) / 64;
-    TileRegs rk, rv;
-    tile_load(rk, Kg, rs, 0, T, tid);
-    tile_load(rv, Vg, rs, 0, T, tid);
-    tile_store(smem[0][0], rk, tid);
-    tile_store(smem[0][1], rv, tid);
-    __syncthreads();
     for (int kt = 0; kt < nkt; ++kt) {
+        if (kt + 1 < nkt) att_wait_vmcnt<4>();
+        else att_wait_vmcnt<0>();
+        att_lds_barrier();  // every wave's share of tile kt is in LDS; tile kt-1's slot is free
+        if (kt + 2 < nkt) issue(kt + 2);
         const int k0 = kt * 64;
-        const bool more = kt + 1 < nkt;
-        if (more) {
-            tile_load(rk, Kg, rs, k0 + 64, T, tid);
-            tile_load(rv, Vg, rs, k0 + 64, T, tid);
-        }
-        const char* Ks = smem[kt & 1][0];
-        const char* Vs = smem[kt & 1][1];
+        const char* Ks = smem[kt % 3][0];
+        const char* Vs = smem[kt % 3][1];
         if (k0 <= q0 + 31) {
             f32x16 s[2], dp[2];
 #pragma unroll
@@ -346,11 +409,6 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_d64(const bf16_t* qkv, const 
 #pragma unroll
                 for (int u = 0; u < 4; ++u) dq[dt] = mfma(frag_col(Ks, 16 * u, 32 * dt, lane), dsk[u], dq[dt]);
         }
-        if (more) {
-            tile_store(smem[(kt + 1) & 1][0], rk, tid);
-            tile_store(smem[(kt + 1) & 1][1], rv, tid);
-        }
-        __syncthreads();
     }
     if (qok) {
         bf16_t* drow = dqkv + ((int64_t)b * T + qi) * rs + h * 64;
@@ -383,6 +441,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_d64(const bf16_t* qkv, cons
     const bf16_t* Vg = base + 2 * C + h * 64;
     const bf16_t* dOg = dout + (int64_t)b * T * C + h * 64;
     const int64_t lb = ((int64_t)b * H + h) * T;
+    const float* L2 = Dbuf + (int64_t)gridDim.x / ((T + 127) / 128) * T;  // lse * log2 e after the B H T values of D
     const int k0w = kb * 128 + w * 32;
     const int kj = k0w + (lane & 31);
     bf16x8 kf[4], vf[4];
@@ -401,7 +460,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_d64(const bf16_t* qkv, cons
         tile_load(rd, dOg, C, qt * 64, T, tid);
         if (tid < 64) {
             const int q = qt * 64 + tid;
-            pl = q < T ? lse[lb + q] * kLog2e : INFINITY;  // rows past T get probability 0
+            pl = q < T ? L2[lb + q] : INFINITY;  // rows past T get probability 0
             pd = q < T ? Dbuf[lb + q] : 0.0f;
         }
     };
@@ -497,7 +556,7 @@ hipError_t attention_bwd(int dtype, int B, int Tn, int C, int H, const void* qkv
         const dim3 grid((unsigned)((Tn + 127) / 128 * H * B));
         if (stages & ATT_BWD_PRE)
             hipLaunchKernelGGL(attn_bwd_pre_d64, dim3((unsigned)((n * 8 + 255) / 256)), dim3(256), 0, s,
-                               (const bf16_t*)out, (const bf16_t*)dout, Dbuf, B, Tn, C, H);
+                               (const bf16_t*)out, (const bf16_t*)dout, lse, Dbuf, B, Tn, C, H);
         if (stages & ATT_BWD_DQ)
             hipLaunchKernelGGL(attn_bwd_dq_d64, grid, dim3(256), 0, s, (const bf16_t*)qkv, (const bf16_t*)dout, lse,
                                (const float*)Dbuf, (bf16_t*)dqkv, Tn, C, H, sl2, scale);

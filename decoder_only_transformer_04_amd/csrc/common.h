@@ -127,7 +127,8 @@ hipError_t bias_grad(int dtype, const void* dY, int64_t rows, int N, float* part
 hipError_t attention_fwd(int dtype, int B, int T, int C, int H, const void* qkv, void* out, float* lse,
                          hipStream_t s);
 // attention backward runs as three launches (D = rowsum(dO*O), dQ, dK/dV) on the MFMA
-// path; `stages` selects which of them to enqueue (the scalar path takes all only)
+// path; `stages` selects which of them to enqueue (the scalar path takes all only).
+// Dbuf: 2 B H T floats (D, then lse in base 2).
 enum { ATT_BWD_PRE = 1, ATT_BWD_DQ = 2, ATT_BWD_DKDV = 4, ATT_BWD_ALL = 7 };
 bool attention_bwd_staged(int dtype, int C, int H);
 hipError_t attention_bwd(int dtype, int B, int T, int C, int H, const void* qkv, const void* out,

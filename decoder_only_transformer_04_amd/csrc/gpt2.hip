@@ -609,7 +609,7 @@ int gpt2_op_attention_bwd(int32_t dtype, int32_t B, int32_t T, int32_t C, int32_
     hipStream_t s = (hipStream_t)hip_stream;
     float* Dbuf = nullptr;
     const size_t n = (size_t)std::max<int64_t>(1, (int64_t)B * H * T);
-    if (hipMallocAsync((void**)&Dbuf, n * 4, s) != hipSuccess) return GPT2_EHIP;
+    if (hipMallocAsync((void**)&Dbuf, 2 * n * 4, s) != hipSuccess) return GPT2_EHIP;  // D and base-2 lse
     hipError_t e = attention_bwd(dtype, B, T, C, H, d_qkv, d_out, d_lse, d_dout, d_dqkv, Dbuf, s);
     (void)hipFreeAsync(Dbuf, s);
     return e == hipSuccess ? GPT2_OK : GPT2_EHIP;

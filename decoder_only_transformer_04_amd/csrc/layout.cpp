@@ -132,7 +132,7 @@ ArenaPlan make_arena_plan(const gpt2_config& c, const ParamLayout& pl, int B, in
         a.dF = take(M * F * ab);
         a.dqkv = take(M * 3 * C * ab);
         a.datt = take(M * C * ab);
-        a.attD = take((size_t)B * H * T * 4);
+        a.attD = take((size_t)B * H * T * 4 * 2);  // D and base-2 lse for the attention backward
         a.ln_part_rows = (int)((M + 15) / 16);
         a.ln_part = take((size_t)a.ln_part_rows * 3 * C * 4);  // dg, db and the dres column sums
         size_t maxN = 3 * C > F ? 3 * C : F;
