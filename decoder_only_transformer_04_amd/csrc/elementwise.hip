@@ -79,54 +79,76 @@ __global__ void enc_count_kernel(const int32_t* idx, int M, int V, int32_t* coun
     }
 }
 
-// one block: exclusive scans of count[] (row starts) and of the segment counts
-__global__ void enc_scan_kernel(const int32_t* count, int32_t* start, int32_t* seg_start, int32_t* nseg_total, int V) {
-    __shared__ int32_t sums[1024], segs[1024];
+// Exclusive scans of count[] (row starts) and of the per-token segment counts,
+// in two passes: each 1024-entry block scans its slice and leaves its totals;
+// the second pass adds the totals of the blocks before it.
+__global__ __launch_bounds__(1024) void enc_scan1_kernel(const int32_t* count, int32_t* start, int32_t* seg_start,
+                                                         int32_t* block_tot, int V) {
+    __shared__ int32_t sc[1024], ss[1024];
     const int tid = threadIdx.x;
-    const int per = (V + 1023) / 1024;
-    const int b = tid * per, e = min(V, b + per);
-    int32_t s = 0, sg = 0;
-    for (int i = b; i < e; ++i) {
-        s += count[i];
-        sg += (count[i] + kEncSeg - 1) / kEncSeg;
-    }
-    sums[tid] = s;
-    segs[tid] = sg;
+    const int v = blockIdx.x * 1024 + tid;
+    const int32_t c = v < V ? count[v] : 0;
+    const int32_t sg = (c + kEncSeg - 1) / kEncSeg;
+    sc[tid] = c;
+    ss[tid] = sg;
     __syncthreads();
     for (int o = 1; o < 1024; o <<= 1) {
-        const int32_t v = tid >= o ? sums[tid - o] : 0;
-        const int32_t w = tid >= o ? segs[tid - o] : 0;
+        const int32_t x = tid >= o ? sc[tid - o] : 0;
+        const int32_t y = tid >= o ? ss[tid - o] : 0;
         __syncthreads();
-        sums[tid] += v;
-        segs[tid] += w;
+        sc[tid] += x;
+        ss[tid] += y;
         __syncthreads();
     }
-    int32_t run = tid > 0 ? sums[tid - 1] : 0;
-    int32_t srun = tid > 0 ? segs[tid - 1] : 0;
-    for (int i = b; i < e; ++i) {
-        start[i] = run;
-        seg_start[i] = srun;
-        run += count[i];
-        srun += (count[i] + kEncSeg - 1) / kEncSeg;
+    if (v < V) {
+        start[v] = sc[tid] - c;  // exclusive within the block
+        seg_start[v] = ss[tid] - sg;
     }
-    if (tid == 1023) *nseg_total = segs[1023];
+    if (tid == 1023) {
+        block_tot[2 * blockIdx.x] = sc[1023];
+        block_tot[2 * blockIdx.x + 1] = ss[1023];
+    }
+}
+__global__ __launch_bounds__(1024) void enc_scan2_kernel(int32_t* start, int32_t* seg_start,
+                                                         const int32_t* block_tot, int nblocks, int32_t* nseg_total,
+                                                         int V) {
+    const int v = blockIdx.x * 1024 + threadIdx.x;
+    int32_t oc = 0, os = 0;
+    for (int j = 0; j < (int)blockIdx.x; ++j) {
+        oc += block_tot[2 * j];
+        os += block_tot[2 * j + 1];
+    }
+    if (v < V) {
+        start[v] += oc;
+        seg_start[v] += os;
+    }
+    if (blockIdx.x == nblocks - 1 && threadIdx.x == 0) *nseg_total = os + block_tot[2 * blockIdx.x + 1];
 }
 
-__global__ void enc_rank_kernel(const int32_t* idx, int M, int V, const int32_t* start, int32_t* order) {
+// Stable rank of each position among the earlier positions holding the same
+// token: rank[m] = #{j < m : idx[j] == idx[m]}. Block (bm, bj) with bj <= bm
+// compares the 256 positions of block bm with those of block bj and adds its
+// match counts with integer atomics (the sum does not depend on their order).
+__global__ __launch_bounds__(256) void enc_rank_kernel(const int32_t* idx, int M, int32_t* rank) {
     __shared__ int32_t tile[256];
-    const int m = blockIdx.x * 256 + threadIdx.x;
+    const int bm = blockIdx.y, bj = blockIdx.x;
+    if (bj > bm) return;
+    const int m = bm * 256 + threadIdx.x;
+    const int j = bj * 256 + threadIdx.x;
+    tile[threadIdx.x] = j < M ? idx[j] : -2;
     const int mine = m < M ? idx[m] : -1;
-    int rank = 0;
-    const int mend = min(M, (int)(blockIdx.x + 1) * 256);
-    for (int b0 = 0; b0 < mend; b0 += 256) {
-        const int j = b0 + threadIdx.x;
-        tile[threadIdx.x] = j < M ? idx[j] : -2;
-        __syncthreads();
-        const int lim = min(256, m - b0);
-        for (int t = 0; t < lim; ++t) rank += tile[t] == mine;
-        __syncthreads();
-    }
-    if (m < M && mine >= 0 && mine < V) order[start[mine] + rank] = m;
+    __syncthreads();
+    const int lim = bj < bm ? 256 : (int)threadIdx.x;  // on the diagonal only earlier positions
+    int cnt = 0;
+    for (int t = 0; t < lim; ++t) cnt += tile[t] == mine;
+    if (m < M && cnt) atomicAdd(&rank[m], cnt);
+}
+__global__ void enc_place_kernel(const int32_t* idx, int M, int V, const int32_t* start, const int32_t* rank,
+                                 int32_t* order) {
+    const int m = blockIdx.x * blockDim.x + threadIdx.x;
+    if (m >= M) return;
+    const int t = idx[m];
+    if (t >= 0 && t < V) order[start[t] + rank[m]] = m;
 }
 
 __global__ void enc_segfill_kernel(const int32_t* count, const int32_t* seg_start, int32_t* seg_tok, int V) {
@@ -178,11 +200,22 @@ hipError_t encoder_bwd(const int32_t* idx, const float* dres, float* dwte, float
                        int32_t* count, int32_t* start, int32_t* seg_start, int32_t* order, int32_t* seg_tok,
                        int32_t* nseg_total, float* seg_part, int accumulate_wpe, hipStream_t s) {
     if (M == 0) return hipSuccess;
+    // scratch inside seg_part (M x C floats, written only later by the segment sums):
+    // rank[M], then the scan's block totals
+    int32_t* rank = (int32_t*)seg_part;
+    int32_t* block_tot = rank + M;
+    const int nsb = (int)nblk(V, 1024);
+    if ((int64_t)M + 2 * nsb > (int64_t)M * C) return hipErrorInvalidValue;
     hipError_t e = fill_zero(count, (size_t)V * 4, s);
+    if (e == hipSuccess) e = fill_zero(rank, (size_t)M * 4, s);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(enc_count_kernel, dim3(nblk(M, 256)), dim3(256), 0, s, idx, M, V, count);
-    hipLaunchKernelGGL(enc_scan_kernel, dim3(1), dim3(1024), 0, s, count, start, seg_start, nseg_total, V);
-    hipLaunchKernelGGL(enc_rank_kernel, dim3(nblk(M, 256)), dim3(256), 0, s, idx, M, V, start, order);
+    hipLaunchKernelGGL(enc_scan1_kernel, dim3(nsb), dim3(1024), 0, s, count, start, seg_start, block_tot, V);
+    hipLaunchKernelGGL(enc_scan2_kernel, dim3(nsb), dim3(1024), 0, s, start, seg_start, block_tot, nsb, nseg_total,
+                       V);
+    const int nmb = (int)nblk(M, 256);
+    hipLaunchKernelGGL(enc_rank_kernel, dim3(nmb, nmb), dim3(256), 0, s, idx, M, rank);
+    hipLaunchKernelGGL(enc_place_kernel, dim3(nblk(M, 256)), dim3(256), 0, s, idx, M, V, start, rank, order);
     hipLaunchKernelGGL(enc_segfill_kernel, dim3(nblk(V, 256)), dim3(256), 0, s, count, seg_start, seg_tok, V);
     // at most M segments (each holds at least one position)
     hipLaunchKernelGGL(enc_segsum_kernel, dim3(M), dim3(256), 0, s, dres, C, count, start, seg_start, order, seg_tok,
