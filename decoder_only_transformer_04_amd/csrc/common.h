@@ -101,6 +101,9 @@ struct GemmArgs {
     const void* R; int64_t ldr;
     int accumulate;
     void* split_buf; size_t split_bytes;  // fp32 scratch for split-K partials (nullable)
+    // EPI_GELU_BWD only (nullable): column sums of the output over each 64-row
+    // block, written to colsum_part[(m / 64) * N + n] (the bias gradient's partials)
+    float* colsum_part;
 };
 
 #ifdef __HIPCC__

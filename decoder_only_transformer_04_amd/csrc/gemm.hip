@@ -41,6 +41,7 @@ struct GP {
     const void* R;
     int64_t ldr;
     int accumulate;
+    float* cpart;  // GELU_BWD: per-64-row column sums of the output (nullable)
 };
 
 // ------------------------------------------------------------------ epilogue
@@ -95,14 +96,13 @@ __device__ __forceinline__ void st8f(float* p, const float (&o)[8]) {
 }
 
 template <int EPI>
-__device__ __forceinline__ void epi_apply8(const GP& p, int64_t m, int n, const float (&v)[8]) {
+__device__ __forceinline__ void epi_apply8(const GP& p, int64_t m, int n, const float (&v)[8], float (&o)[8]) {
     float bv[8];
     if (p.bias) ld8f(p.bias + n, bv);
     else {
 #pragma unroll
         for (int k = 0; k < 8; ++k) bv[k] = 0.0f;
     }
-    float o[8];
     if constexpr (EPI == EPI_STORE) {
 #pragma unroll
         for (int k = 0; k < 8; ++k) o[k] = p.alpha * v[k] + bv[k];
@@ -497,6 +497,12 @@ __global__ __launch_bounds__(64 * WGM * WGN * KS) void gemm_bf16_kernel(GP p) {
     constexpr int NPASS = (32 + RPP - 1) / RPP;   // passes per 32-row strip
     float* st = (float*)smem + wq * 32 * SP;
     const int srow = 4 * (lane >> 5), scol = lane & 31;
+    // GELU_BWD with column sums: each lane sums its 8 output columns over the
+    // rows it writes; lanes holding the same columns are combined below
+    constexpr bool CSUM = EPI == EPI_GELU_BWD && KS == 1 && WM == 64 && (LPR & (LPR - 1)) == 0 && RPP * LPR == 64;
+    float csum[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) csum[k] = 0.0f;
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
         if constexpr (KS > 1) {
@@ -525,15 +531,36 @@ __global__ __launch_bounds__(64 * WGM * WGN * KS) void gemm_bf16_kernel(GP p) {
                 const int rr = pass * RPP + lane / LPR;
                 const int cc = (lane % LPR) * 8;
                 if (lane < RPP * LPR && rr < 32) {  // WN = 96 leaves lanes 60..63 idle
-                    float v[8];
+                    float v[8], o[8];
                     ld8f(st + rr * SP + cc, v);
                     const int64_t m = m0 + wm * WM + i * 32 + rr;
                     const int n = n0 + wn * WN + cc;
-                    if (m < p.M && n < p.N) epi_apply8<EPI>(p, m, n, v);
+                    if (m < p.M && n < p.N) {
+                        epi_apply8<EPI>(p, m, n, v, o);
+                        if constexpr (CSUM) {
+#pragma unroll
+                            for (int k = 0; k < 8; ++k) csum[k] += o[k];
+                        }
+                    }
                 }
             }
         }
         __syncthreads();
+    }
+    if constexpr (CSUM) {
+        if (p.cpart && ks == 0) {
+            // lanes l, l + LPR, l + 2 LPR, ... hold the same 8 columns
+#pragma unroll
+            for (int off = LPR; off < 64; off <<= 1)
+#pragma unroll
+                for (int k = 0; k < 8; ++k) csum[k] += __shfl_xor(csum[k], off, 64);
+            const int n = n0 + wn * WN + lane * 8;
+            // one partial row per 64-row block that starts inside the matrix
+            if (lane < LPR && n < p.N && m0 + wm * WM < p.M) {
+                float* dst = p.cpart + ((m0 + wm * WM) / 64) * p.N + n;
+                st8f(dst, csum);
+            }
+        }
     }
 }
 
@@ -668,6 +695,9 @@ static hipError_t pick_tile_bf16(const GP& p, int splits, hipStream_t s) {
     if constexpr (!AKC) {
         return launch_bf16<128, 128, AKC, BKC, EPI, 64>(p, splits, s);
     } else {
+        // the column sums of the GELU-derivative epilogue are per 64-row wave block
+        if constexpr (EPI == EPI_GELU_BWD)
+            if (p.cpart) return launch_bf16<128, 128, AKC, BKC, EPI, 32>(p, splits, s);
         if (p.N % 192 == 0 && p.N <= 1536 && p.K >= 2048 && splits == 1) {
             if (!BKC && p.K >= 8192) return launch_bf16<192, 192, AKC, BKC, EPI, 64, 2, 2, 2, 2, true>(p, splits, s);
             return launch_bf16<192, 192, AKC, BKC, EPI, 64, 2, 2, 2, 2>(p, splits, s);
@@ -699,6 +729,7 @@ hipError_t gemm(int dtype, const GemmArgs& a, hipStream_t s) {
     p.C = a.C; p.ldc = a.ldc; p.c_split_stride = 0;
     p.C2 = a.C2; p.ldc2 = a.ldc2; p.R = a.R; p.ldr = a.ldr;
     p.accumulate = a.accumulate;
+    p.cpart = a.epi == EPI_GELU_BWD ? a.colsum_part : nullptr;
     if (a.M <= 0 || a.N <= 0) return hipSuccess;
     if (a.K <= 0) {
         // empty contraction: the product is zero

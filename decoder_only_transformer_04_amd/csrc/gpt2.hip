@@ -131,8 +131,9 @@ hipError_t linear_fwd(gpt2_ctx* x, int epi, int64_t M, int N, int K, const void*
 
 // dX[M,K] = dY[M,N] W[N,K] (epilogue epi, alpha), with optional GELU' operand R
 hipError_t linear_dgrad(int dtype, hipStream_t s, int epi, int64_t M, int N, int K, const void* dY, int64_t ldy,
-                        const void* W, void* dX, const void* R, float alpha) {
+                        const void* W, void* dX, const void* R, float alpha, float* colsum_part = nullptr) {
     GemmArgs a = gemm_args();
+    a.colsum_part = colsum_part;
     a.M = M; a.N = K; a.K = N;
     a.A = dY; a.lda = ldy; a.a_kc = true;
     a.B = W; a.ldb = K; a.b_kc = false;
@@ -375,13 +376,19 @@ int gpt2_backward(gpt2_ctx* x, float loss_scale, int32_t zero_grads) {
     for (int l = c.n_layer - 1; l >= 0; --l) {
         const LayerW& w = pl.layer[l];
         // x_out = x_mid + fc2(gelu(fc(ln2(x_mid))))
+        // bf16: the GELU-derivative epilogue also leaves per-64-row column sums of
+        // dF, the partials of the fc bias gradient (bias_part has (M + 63) / 64 rows)
+        const bool fuse_bfc = bf && w.b_fc >= 0;
         G2_T("gemm.dgrad.fc2", linear_dgrad(dt, s, EPI_GELU_BWD, M, C, F, dres_act, C, wptr(x, w.w_fc2), at<char>(x, ap.dF),
-                            at<char>(x, ap.fch[l]), 1.0f));
+                            at<char>(x, ap.fch[l]), 1.0f, fuse_bfc ? bpart : nullptr));
         G2_T("gemm.wgrad.fc2", linear_wgrad(dt, s, M, C, F, dres_act, C, at<char>(x, ap.fcg[l]), gf(x, w.w_fc2), acc, 1.0f, sb, sbytes));
         G2_T("gemm.dgrad.fc", linear_dgrad(dt, s, EPI_F32, M, F, C, at<char>(x, ap.dF), F, wptr(x, w.w_fc), dtmp, nullptr, 1.0f));
         G2_T("gemm.wgrad.fc", linear_wgrad(dt, s, M, F, C, at<char>(x, ap.dF), F, at<char>(x, ap.ln2[l]), gf(x, w.w_fc), acc, 1.0f, sb,
                             sbytes));
-        if (w.b_fc >= 0) G2_T("bias", bias_grad(dt, at<char>(x, ap.dF), M, F, bpart, ap.bias_part_rows, gf(x, w.b_fc), acc, s));
+        if (fuse_bfc)
+            G2_T("colsum", colsum_finish2(bpart, ap.bias_part_rows, F, gf(x, w.b_fc), F, nullptr, 0, acc, s));
+        else if (w.b_fc >= 0)
+            G2_T("bias", bias_grad(dt, at<char>(x, ap.dF), M, F, bpart, ap.bias_part_rows, gf(x, w.b_fc), acc, s));
         float* b_proj = gf(x, w.b_proj);
         G2_T("ln.bwd", layernorm_bwd(dt, dtmp, at<float>(x, ap.xmid[l]), at<float>(x, ap.m2[l]), at<float>(x, ap.r2[l]),
                              pf(x, w.ln2_g), dres, bf ? dres_act : nullptr, part, ap.ln_part_rows, M, C, 1,
