@@ -65,7 +65,6 @@ def kernel_work(label: str, w: syn.Workload):
         "ln.bwd": (2 * L + 1) * M * C * (4 * 4 + 2),  # dy, x, dres in/out (fp32), bf16 copy
         "embed.fwd": M * C * 4 * 3,
         "embed.bwd": M * C * 4 * 2,
-        "attn.bwd.pre": L * (M * C * 2 * 2 + B * H * T * 4),  # read O, dO (bf16); write D (fp32)
     }
     if label in bytes_:
         return "hbm", bytes_[label], "GB/s"
@@ -75,7 +74,7 @@ def kernel_work(label: str, w: syn.Workload):
 LABELS = ["gemm.fwd.qkv", "gemm.fwd.proj", "gemm.fwd.fc", "gemm.fwd.fc2", "gemm.fwd.head",
           "gemm.dgrad.head", "gemm.wgrad.head", "gemm.dgrad.fc2", "gemm.wgrad.fc2", "gemm.dgrad.fc",
           "gemm.wgrad.fc", "gemm.dgrad.proj", "gemm.wgrad.proj", "gemm.dgrad.qkv", "gemm.wgrad.qkv",
-          "attn.fwd", "attn.bwd.pre", "attn.bwd.dq", "attn.bwd.dkdv", "ln.fwd", "ln.bwd", "ce", "loss", "colsum",
+          "attn.fwd", "attn.bwd.dq", "attn.bwd.dkdv", "ln.fwd", "ln.bwd", "ce", "loss", "colsum",
           "bias", "embed.fwd", "embed.bwd", "gradnorm", "adamw"]
 
 

@@ -297,45 +297,12 @@ __global__ __launch_bounds__(256, G2_ATT_FWD_OCC) void attn_fwd_d64(const bf16_t
     }
 }
 
-// ------------------------------------------------------------------ backward: D = rowsum(dO * O)
-// Eight lanes per (token, head) row, each taking 16 bytes of O and of dO, so a
-// wave reads 1 KB of contiguous memory from each; the eight partial dot
-// products are combined with lane shuffles (fixed order). Dbuf holds D in its
-// first B H T floats and lse in base 2 (lse * log2 e) in the next B H T, the
-// form both backward kernels consume.
-__global__ __launch_bounds__(256) void attn_bwd_pre_d64(const bf16_t* out, const bf16_t* dout, const float* lse,
-                                                        float* Dbuf, int B, int T, int C, int H) {
-    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    const int64_t n = (int64_t)B * T * H * 8;
-    const bool ok = t < n;
-    const int64_t row = t >> 3;  // (token, head)
-    const int c = (int)(t & 7);
-    const int64_t m = row / H;
-    const int h = (int)(row - m * H);
-    float s = 0.0f;
-    if (ok) {
-        const int64_t off = m * C + h * 64 + c * 8;
-        float a[8], d[8];
-        unpack8f(*(const uint4*)(out + off), a);
-        unpack8f(*(const uint4*)(dout + off), d);
-#pragma unroll
-        for (int k = 0; k < 8; ++k) s = fmaf(a[k], d[k], s);
-    }
-    s += __shfl_xor(s, 1, 64);
-    s += __shfl_xor(s, 2, 64);
-    s += __shfl_xor(s, 4, 64);
-    if (ok && c == 0) {
-        const int64_t b = m / T, i = m - b * T;
-        const int64_t r = (b * H + h) * T + i;
-        Dbuf[r] = s;
-        Dbuf[(int64_t)B * H * T + r] = lse[r] * kLog2e;
-    }
-}
-
 // ------------------------------------------------------------------ backward: dQ
-__global__ __launch_bounds__(256) void attn_bwd_dq_d64(const bf16_t* qkv, const bf16_t* dout, const float* lse,
-                                                       const float* Dbuf, bf16_t* dqkv, int T, int C, int H,
-                                                       float sl2, float scale) {
+// D_i = dO_i . O_i is formed here from the dO rows already in registers and
+// written, with lse in base 2, to Dbuf for the dK/dV kernel that runs next.
+__global__ __launch_bounds__(256) void attn_bwd_dq_d64(const bf16_t* qkv, const bf16_t* outp, const bf16_t* dout,
+                                                       const float* lse, float* Dbuf, bf16_t* dqkv, int T, int C,
+                                                       int H, float sl2, float scale) {
     __shared__ __attribute__((aligned(16))) char smem[3][2][kTileBytes];
     int qb, h, b;
     block_coords(T, H, true, qb, h, b);
@@ -361,16 +328,25 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_d64(const bf16_t* qkv, const 
     };
     issue(0);
     if (nkt > 1) issue(1);
+    const bf16_t* Og = outp + (int64_t)b * T * C + h * 64;
     bf16x8 qf[4], df[4];
+    float dpart = 0.0f;  // this half-wave's share of dO . O
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
         qf[kk] = load8(Qg + (int64_t)qi * rs + 16 * kk + 8 * g, qok);
         df[kk] = load8(dOg + (int64_t)qi * C + 16 * kk + 8 * g, qok);
+        const bf16x8 of = load8(Og + (int64_t)qi * C + 16 * kk + 8 * g, qok);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) dpart = fmaf((float)df[kk][e], (float)of[e], dpart);
     }
     const int64_t lb = ((int64_t)b * H + h) * T;
-    const float* L2 = Dbuf + (int64_t)gridDim.x / ((T + 127) / 128) * T;  // lse * log2 e after the B H T values of D
-    const float lse2 = qok ? L2[lb + qi] : 0.0f;
-    const float Dq = qok ? Dbuf[lb + qi] : 0.0f;
+    float* L2 = Dbuf + (int64_t)gridDim.x / ((T + 127) / 128) * T;  // lse * log2 e after the B H T values of D
+    const float lse2 = qok ? lse[lb + qi] * kLog2e : 0.0f;
+    const float Dq = dpart + __shfl_xor(dpart, 32, 64);
+    if (qok && g == 0) {
+        Dbuf[lb + qi] = Dq;
+        L2[lb + qi] = lse2;
+    }
     f32x16 dq[2] = {zero16(), zero16()};
     for (int kt = 0; kt < nkt; ++kt) {
         if (kt + 1 < nkt) att_wait_vmcnt<4>();
@@ -552,14 +528,10 @@ hipError_t attention_bwd(int dtype, int B, int Tn, int C, int H, const void* qkv
     if (attention_bwd_staged(dtype, C, H)) {
         const float sl2 = kLog2e / 8.0f;
         const float scale = 0.125f;
-        const int64_t n = (int64_t)B * H * Tn;
         const dim3 grid((unsigned)((Tn + 127) / 128 * H * B));
-        if (stages & ATT_BWD_PRE)
-            hipLaunchKernelGGL(attn_bwd_pre_d64, dim3((unsigned)((n * 8 + 255) / 256)), dim3(256), 0, s,
-                               (const bf16_t*)out, (const bf16_t*)dout, lse, Dbuf, B, Tn, C, H);
         if (stages & ATT_BWD_DQ)
-            hipLaunchKernelGGL(attn_bwd_dq_d64, grid, dim3(256), 0, s, (const bf16_t*)qkv, (const bf16_t*)dout, lse,
-                               (const float*)Dbuf, (bf16_t*)dqkv, Tn, C, H, sl2, scale);
+            hipLaunchKernelGGL(attn_bwd_dq_d64, grid, dim3(256), 0, s, (const bf16_t*)qkv, (const bf16_t*)out,
+                               (const bf16_t*)dout, lse, Dbuf, (bf16_t*)dqkv, Tn, C, H, sl2, scale);
         if (stages & ATT_BWD_DKDV)
             hipLaunchKernelGGL(attn_bwd_dkdv_d64, grid, dim3(256), 0, s, (const bf16_t*)qkv, (const bf16_t*)dout,
                                lse, (const float*)Dbuf, (bf16_t*)dqkv, Tn, C, H, sl2, scale);

@@ -129,10 +129,11 @@ hipError_t bias_grad(int dtype, const void* dY, int64_t rows, int N, float* part
                      int accumulate, hipStream_t s);
 hipError_t attention_fwd(int dtype, int B, int T, int C, int H, const void* qkv, void* out, float* lse,
                          hipStream_t s);
-// attention backward runs as three launches (D = rowsum(dO*O), dQ, dK/dV) on the MFMA
-// path; `stages` selects which of them to enqueue (the scalar path takes all only).
+// attention backward runs as two launches on the MFMA path: dQ (which also forms
+// D = rowsum(dO*O) and writes it with lse in base 2 to Dbuf) and then dK/dV;
+// `stages` selects which of them to enqueue (the scalar path takes both only).
 // Dbuf: 2 B H T floats (D, then lse in base 2).
-enum { ATT_BWD_PRE = 1, ATT_BWD_DQ = 2, ATT_BWD_DKDV = 4, ATT_BWD_ALL = 7 };
+enum { ATT_BWD_DQ = 2, ATT_BWD_DKDV = 4, ATT_BWD_ALL = 6 };
 bool attention_bwd_staged(int dtype, int C, int H);
 hipError_t attention_bwd(int dtype, int B, int T, int C, int H, const void* qkv, const void* out,
                          const float* lse, const void* dout, void* dqkv, float* Dbuf, hipStream_t s,

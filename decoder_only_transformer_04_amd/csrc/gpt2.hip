@@ -408,7 +408,6 @@ int gpt2_backward(gpt2_ctx* x, float loss_scale, int32_t zero_grads) {
             char* dqkv = at<char>(x, ap.dqkv);
             float* attD = at<float>(x, ap.attD);
             if (attention_bwd_staged(dt, C, H)) {
-                G2_T("attn.bwd.pre", attention_bwd(dt, ap.B, T, C, H, qkv_l, att_l, lse_l, datt, dqkv, attD, s, ATT_BWD_PRE));
                 G2_T("attn.bwd.dq", attention_bwd(dt, ap.B, T, C, H, qkv_l, att_l, lse_l, datt, dqkv, attD, s, ATT_BWD_DQ));
                 G2_T("attn.bwd.dkdv",
                      attention_bwd(dt, ap.B, T, C, H, qkv_l, att_l, lse_l, datt, dqkv, attD, s, ATT_BWD_DKDV));

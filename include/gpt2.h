@@ -167,9 +167,9 @@ int gpt2_clear_status(gpt2_ctx* ctx);
  * timed, and stops timing. Labels: "embed.fwd", "ln.fwd", "gemm.fwd.{qkv,proj,
  * fc,fc2,head}", "attn.fwd", "ce", "loss", "gemm.dgrad.{head,fc2,fc,proj,qkv}",
  * "gemm.wgrad.{head,fc2,fc,proj,qkv}", "ln.bwd", "colsum", "bias",
- * "attn.bwd.{pre,dq,dkdv}" (bf16, head size 64; "attn.bwd" otherwise), "embed.bwd",
+ * "attn.bwd.{dq,dkdv}" (bf16, head size 64; "attn.bwd" otherwise), "embed.bwd",
  * "gradnorm", "adamw". A prefix also times the labels that extend it by a
- * '.'-separated part ("attn.bwd" covers the three backward launches); an empty
+ * '.'-separated part ("attn.bwd" covers both backward launches); an empty
  * prefix times every launch. */
 int gpt2_timing_begin(gpt2_ctx* ctx, const char* prefix);
 int gpt2_timing_end(gpt2_ctx* ctx, float* total_ms, int32_t* launches);
