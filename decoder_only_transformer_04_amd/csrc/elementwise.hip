@@ -242,50 +242,78 @@ template <> __device__ __forceinline__ void st4<bf16_t>(bf16_t* p, float4 v) {
 }
 __device__ __forceinline__ float hsum4(float4 v) { return (v.x + v.y) + (v.z + v.w); }
 
-template <int NJ4, class T>
+// NR rows per wave, their loads issued together and their reductions
+// interleaved, so one wave keeps NR independent dependency chains in flight.
+template <int NJ4, int NR, class T>
 __global__ __launch_bounds__(256) void ln_fwd_v4(const float* x, const float* g, const float* b, float eps, T* y,
                                                  float* mean, float* rstd, int64_t rows, int C) {
     const int lane = threadIdx.x & 63;
-    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (row >= rows) return;
+    const int64_t row0 = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * NR;
+    if (row0 >= rows) return;
     const int C4 = C / 4;
-    const float4* xr = (const float4*)(x + row * C);
-    float4 v[NJ4];
-    float s = 0.0f;
+    float4 v[NR][NJ4];
+    float s[NR], q[NR], mu[NR], rs[NR];
 #pragma unroll
-    for (int j = 0; j < NJ4; ++j) {
-        const int c4 = lane + 64 * j;
-        v[j] = c4 < C4 ? xr[c4] : make_float4(0.f, 0.f, 0.f, 0.f);
-        s += hsum4(v[j]);
-    }
-    const float mu = wave_sum(s) / (float)C;
-    float q = 0.0f;
+    for (int r = 0; r < NR; ++r) {
+        const bool ok = row0 + r < rows;
+        const float4* xr = (const float4*)(x + (row0 + r) * C);
+        s[r] = 0.0f;
 #pragma unroll
-    for (int j = 0; j < NJ4; ++j) {
-        const int c4 = lane + 64 * j;
-        if (c4 < C4) {
-            const float a = v[j].x - mu, bq = v[j].y - mu, c = v[j].z - mu, d = v[j].w - mu;
-            q += (a * a + bq * bq) + (c * c + d * d);
+        for (int j = 0; j < NJ4; ++j) {
+            const int c4 = lane + 64 * j;
+            v[r][j] = ok && c4 < C4 ? xr[c4] : make_float4(0.f, 0.f, 0.f, 0.f);
+            s[r] += hsum4(v[r][j]);
         }
     }
-    const float var = wave_sum(q) / (float)C;
-    const float rs = 1.0f / sqrtf(var + eps);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1)
+#pragma unroll
+        for (int r = 0; r < NR; ++r) s[r] += __shfl_xor(s[r], o, 64);
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+        mu[r] = s[r] / (float)C;
+        q[r] = 0.0f;
+#pragma unroll
+        for (int j = 0; j < NJ4; ++j) {
+            const int c4 = lane + 64 * j;
+            if (c4 < C4) {
+                const float a = v[r][j].x - mu[r], bq = v[r][j].y - mu[r], c = v[r][j].z - mu[r],
+                            d = v[r][j].w - mu[r];
+                q[r] += (a * a + bq * bq) + (c * c + d * d);
+            }
+        }
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1)
+#pragma unroll
+        for (int r = 0; r < NR; ++r) q[r] += __shfl_xor(q[r], o, 64);
+#pragma unroll
+    for (int r = 0; r < NR; ++r) rs[r] = 1.0f / sqrtf(q[r] / (float)C + eps);
 #pragma unroll
     for (int j = 0; j < NJ4; ++j) {
         const int c4 = lane + 64 * j;
         if (c4 < C4) {
             const float4 gg = ((const float4*)g)[c4], bb = ((const float4*)b)[c4];
-            float4 o;
-            o.x = (v[j].x - mu) * rs * gg.x + bb.x;
-            o.y = (v[j].y - mu) * rs * gg.y + bb.y;
-            o.z = (v[j].z - mu) * rs * gg.z + bb.z;
-            o.w = (v[j].w - mu) * rs * gg.w + bb.w;
-            st4<T>(y + row * C + 4 * c4, o);
+#pragma unroll
+            for (int r = 0; r < NR; ++r) {
+                if (row0 + r < rows) {
+                    float4 o;
+                    o.x = (v[r][j].x - mu[r]) * rs[r] * gg.x + bb.x;
+                    o.y = (v[r][j].y - mu[r]) * rs[r] * gg.y + bb.y;
+                    o.z = (v[r][j].z - mu[r]) * rs[r] * gg.z + bb.z;
+                    o.w = (v[r][j].w - mu[r]) * rs[r] * gg.w + bb.w;
+                    st4<T>(y + (row0 + r) * C + 4 * c4, o);
+                }
+            }
         }
     }
     if (lane == 0) {
-        mean[row] = mu;
-        rstd[row] = rs;
+#pragma unroll
+        for (int r = 0; r < NR; ++r)
+            if (row0 + r < rows) {
+                mean[row0 + r] = mu[r];
+                rstd[row0 + r] = rs[r];
+            }
     }
 }
 
@@ -331,7 +359,15 @@ static hipError_t ln_fwd_dispatch(const float* x, const float* g, const float* b
     dim3 grid(nblk(rows, 4)), blk(256);
     if (C % 4 == 0) {
         const int nj4 = (C / 4 + 63) / 64;
-#define G2_LNF4(N) hipLaunchKernelGGL((ln_fwd_v4<N, T>), grid, blk, 0, s, x, g, b, eps, y, mean, rstd, rows, C)
+        // two rows per wave for the model's widths (up to 1024 columns)
+        dim3 grid2(nblk(rows, 8));
+#define G2_LNF4(N)                                                                                             \
+    do {                                                                                                       \
+        if (N <= 4)                                                                                            \
+            hipLaunchKernelGGL((ln_fwd_v4<N, 2, T>), grid2, blk, 0, s, x, g, b, eps, y, mean, rstd, rows, C); \
+        else                                                                                                   \
+            hipLaunchKernelGGL((ln_fwd_v4<N, 1, T>), grid, blk, 0, s, x, g, b, eps, y, mean, rstd, rows, C);  \
+    } while (0)
         if (nj4 <= 1) G2_LNF4(1);
         else if (nj4 <= 2) G2_LNF4(2);
         else if (nj4 <= 3) G2_LNF4(3);
@@ -802,6 +838,8 @@ __global__ __launch_bounds__(256) void ce_kernel(T* logits, int64_t rows, int V,
 // Single HBM pass for bf16 logits: a 512-thread block holds its whole row in
 // registers (KC 16-byte chunks per thread), reduces max/argmax, then sum of
 // exp(z - max), and overwrites the row with softmax - onehot from registers.
+constexpr float kLog2eF = 1.4426950408889634f;
+
 template <int KC>
 __global__ __launch_bounds__(512) void ce_reg_kernel(bf16_t* logits, int64_t rows, int V, int ld,
                                                      const int32_t* targets, float* loss_rows, int32_t* argmax,
@@ -818,7 +856,8 @@ __global__ __launch_bounds__(512) void ce_reg_kernel(bf16_t* logits, int64_t row
         const int c = tid + 512 * k;
         r[k] = c < nch ? ((const uint4*)z)[c] : make_uint4(0, 0, 0, 0);
     }
-    // max and argmax (lowest column among equal maxima)
+    // max and argmax (lowest column among equal maxima); chunks wholly inside
+    // the vocabulary skip the per-column bounds test
     float bv = -INFINITY;
     int bi = 0x7fffffff;
 #pragma unroll
@@ -827,10 +866,16 @@ __global__ __launch_bounds__(512) void ce_reg_kernel(bf16_t* logits, int64_t row
         if (c < nch) {
             float v[8];
             unpack8f(r[k], v);
+            if (8 * c + 8 <= V) {
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int col = 8 * c + e;
-                if (col < V && v[e] > bv) { bv = v[e]; bi = col; }
+                for (int e = 0; e < 8; ++e)
+                    if (v[e] > bv) { bv = v[e]; bi = 8 * c + e; }
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int col = 8 * c + e;
+                    if (col < V && v[e] > bv) { bv = v[e]; bi = col; }
+                }
             }
         }
     }
@@ -847,6 +892,7 @@ __global__ __launch_bounds__(512) void ce_reg_kernel(bf16_t* logits, int64_t row
     for (int w = 1; w < 8; ++w)
         if (sv[w] > bv || (sv[w] == bv && si[w] < bi)) { bv = sv[w]; bi = si[w]; }
     const float mx = bv;
+    const float mx2 = mx * kLog2eF;
     float sum = 0.0f;
 #pragma unroll
     for (int k = 0; k < KC; ++k) {
@@ -854,9 +900,14 @@ __global__ __launch_bounds__(512) void ce_reg_kernel(bf16_t* logits, int64_t row
         if (c < nch) {
             float v[8];
             unpack8f(r[k], v);
+            if (8 * c + 8 <= V) {
 #pragma unroll
-            for (int e = 0; e < 8; ++e)
-                if (8 * c + e < V) sum += __expf(v[e] - mx);
+                for (int e = 0; e < 8; ++e) sum += __builtin_amdgcn_exp2f(fmaf(v[e], kLog2eF, -mx2));
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    if (8 * c + e < V) sum += __builtin_amdgcn_exp2f(fmaf(v[e], kLog2eF, -mx2));
+            }
         }
     }
     sum = wave_sum(sum);
@@ -873,34 +924,41 @@ __global__ __launch_bounds__(512) void ce_reg_kernel(bf16_t* logits, int64_t row
         if (argmax) argmax[row] = bi;
         if (loss_rows && tgt < 0) loss_rows[row] = 0.0f;
     }
-    if (tgt >= 0 && loss_rows) {
-        // the thread holding the target column reports the loss
+    // the thread holding the target column reads its logit: it reports the loss
+    // and, below, rewrites that column of the gradient
+    const bool owns = tgt >= 0 && (tgt / 8) % 512 == tid;
+    float zt = 0.0f;
+    if (owns) {
         const int c = tgt / 8;
-        if (c % 512 == tid) {
 #pragma unroll
-            for (int k = 0; k < KC; ++k)
-                if (k == c / 512) {  // constant register index after unrolling
-                    float v[8];
-                    unpack8f(r[k], v);
-                    float zt = v[0];
+        for (int k = 0; k < KC; ++k)
+            if (k == c / 512) {  // constant register index after unrolling
+                float v[8];
+                unpack8f(r[k], v);
+                zt = v[0];
 #pragma unroll
-                    for (int e = 1; e < 8; ++e)
-                        if (e == tgt % 8) zt = v[e];
-                    loss_rows[row] = lse - zt;
-                }
-        }
+                for (int e = 1; e < 8; ++e)
+                    if (e == tgt % 8) zt = v[e];
+            }
+        if (loss_rows) loss_rows[row] = lse - zt;
     }
     if (!write_grad) return;
+    // softmax everywhere (0 past V); the thread owning the target column then
+    // rewrites that one element as softmax - 1
+    const float lse2 = lse * kLog2eF;
 #pragma unroll
     for (int k = 0; k < KC; ++k) {
         const int c = tid + 512 * k;
         if (c < nch) {
             float v[8], o[8];
             unpack8f(r[k], v);
+            if (8 * c + 8 <= V) {
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int col = 8 * c + e;
-                o[e] = col < V ? __expf(v[e] - lse) - (col == tgt ? 1.0f : 0.0f) : 0.0f;
+                for (int e = 0; e < 8; ++e) o[e] = __builtin_amdgcn_exp2f(fmaf(v[e], kLog2eF, -lse2));
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    o[e] = 8 * c + e < V ? __builtin_amdgcn_exp2f(fmaf(v[e], kLog2eF, -lse2)) : 0.0f;
             }
             uint4 u;
             u.x = pack2bf(o[0], o[1]);
@@ -910,6 +968,8 @@ __global__ __launch_bounds__(512) void ce_reg_kernel(bf16_t* logits, int64_t row
             ((uint4*)z)[c] = u;
         }
     }
+    // same thread, same address, after its chunk store: softmax - 1 at the target
+    if (owns) z[tgt] = f2bf(__builtin_amdgcn_exp2f(fmaf(zt, kLog2eF, -lse2)) - 1.0f);
 }
 
 hipError_t cross_entropy(int dtype, void* logits, int64_t rows, int V, int ld, const int32_t* targets,
