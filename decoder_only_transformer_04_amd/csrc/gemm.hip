@@ -195,6 +195,26 @@ __device__ __forceinline__ void tile_gload(uint4 (&regs)[R * BK / (8 * NT)], con
     }
 }
 
+// Global -> registers for a whole BK-deep stage (no k bound); rows (KC) or
+// column chunks (not KC) past rmax are clamped to valid memory, like the DMA
+// path: their products land only in discarded outputs.
+template <int R, bool KC, int BK, int NT>
+__device__ __forceinline__ void tile_gload_full(uint4 (&regs)[R * BK / (8 * NT)], const bf16_t* base, int64_t ld,
+                                                int64_t r0, int64_t rmax, int k0, int tid) {
+    constexpr int CPR = TileCfg<R, KC, BK>::CPR;
+#pragma unroll
+    for (int i = 0; i < R * BK / (8 * NT); ++i) {
+        const int c = tid + NT * i;
+        if constexpr (KC) {
+            const int64_t gr = min(r0 + c / CPR, rmax - 1);
+            regs[i] = *(const uint4*)(base + gr * ld + k0 + (c % CPR) * 8);
+        } else {
+            const int64_t gc = min(r0 + (c % CPR) * 8, rmax - 8);
+            regs[i] = *(const uint4*)(base + (int64_t)(k0 + c / CPR) * ld + gc);
+        }
+    }
+}
+
 template <int R, bool KC, int BK, int NT>
 __device__ __forceinline__ void tile_sstore(char* lds, const uint4 (&regs)[R * BK / (8 * NT)], int tid) {
     constexpr int CPR = TileCfg<R, KC, BK>::CPR;
@@ -381,8 +401,10 @@ __device__ __forceinline__ void tile_coords(int nm, int nn, int& tm, int& tn) {
 // that split every stage's contraction steps; the KS partial sums are added
 // through LDS before the epilogue.
 // SPREAD: the next stage's loads are issued between the MFMAs instead of before them.
+// REGLOAD: operands go global -> registers -> LDS (one stage ahead in
+// registers, two LDS buffers) instead of by DMA.
 template <int BM, int BN, int BK, bool AKC, bool BKC, int EPI, int NS, int WGM = 2, int WGN = 2, int KS = 1,
-          bool SPREAD = false>
+          bool SPREAD = false, bool REGLOAD = false>
 __global__ __launch_bounds__(64 * WGM * WGN * KS) void gemm_bf16_kernel(GP p) {
     static_assert(NS >= 2 && NS <= 4, "pipeline depth");
     static_assert(KS == 1 || KS == 2, "contraction split");
@@ -396,7 +418,8 @@ __global__ __launch_bounds__(64 * WGM * WGN * KS) void gemm_bf16_kernel(GP p) {
     static_assert(FM * 32 == WM && FN * 32 == WN && (BK / 16) % KS == 0, "wave tiling");
     constexpr int SP = WN + 4;  // epilogue: staged floats per row (padding spreads banks)
     constexpr int EPI_BYTES = NWQ * 32 * SP * 4;
-    constexpr int SMEM = NS * STAGE > EPI_BYTES ? NS * STAGE : EPI_BYTES;
+    constexpr int NSB = REGLOAD ? 2 : NS;  // LDS stage buffers
+    constexpr int SMEM = NSB * STAGE > EPI_BYTES ? NSB * STAGE : EPI_BYTES;
     constexpr int DMA_OPS = DmaPlan<BM, AKC, BK, NW>::NI + DmaPlan<BN, BKC, BK, NW>::NI;  // per wave per stage
     __shared__ __attribute__((aligned(16))) char smem[SMEM];
 
@@ -445,6 +468,38 @@ __global__ __launch_bounds__(64 * WGM * WGN * KS) void gemm_bf16_kernel(GP p) {
             dB.skip();
         }
     };
+    if constexpr (REGLOAD) {
+        uint4 ra[BM * BK / (8 * NT)], rb[BN * BK / (8 * NT)];
+        auto gload = [&](int kt) {
+            const int k0 = kbeg + kt * BK;
+            if (k0 + BK <= kend) {
+                tile_gload_full<BM, AKC, BK, NT>(ra, A, p.lda, m0, p.M, k0, tid);
+                tile_gload_full<BN, BKC, BK, NT>(rb, B, p.ldb, n0, p.N, k0, tid);
+            } else {
+                tile_gload<BM, AKC, BK, NT>(ra, A, p.lda, m0, p.M, k0, kend, tid);
+                tile_gload<BN, BKC, BK, NT>(rb, B, p.ldb, n0, p.N, k0, kend, tid);
+            }
+        };
+        auto sstore = [&](char* buf) {
+            tile_sstore<BM, AKC, BK, NT>(buf, ra, tid);
+            tile_sstore<BN, BKC, BK, NT>(buf + ABYTES, rb, tid);
+        };
+        if (nk > 0) {
+            gload(0);
+            sstore(smem);
+        }
+        if (nk > 1) gload(1);
+        __syncthreads();
+        for (int kt = 0; kt < nk; ++kt) {
+            // registers hold stage kt+1; its LDS buffer was last read in
+            // iteration kt-1, before the barrier that ended it
+            if (kt + 1 < nk) sstore(smem + ((kt + 1) & 1) * STAGE);
+            if (kt + 2 < nk) gload(kt + 2);
+            mma_stage<BM, BN, AKC, BKC, BK, FM, FN, WM, WN, KS, 0>(smem + (kt & 1) * STAGE, acc, wm, wn, ks, lane,
+                                                                   [](int) {});
+            lds_barrier();  // stage kt+1 is in LDS; stage kt is free (loads in flight target registers)
+        }
+    } else {
     // stages [0, nfull) are whole BK-deep stages loaded by DMA
     const int nfull = (kend - kbeg) / BK;
 #pragma unroll
@@ -484,6 +539,7 @@ __global__ __launch_bounds__(64 * WGM * WGN * KS) void gemm_bf16_kernel(GP p) {
             dA.skip();
             dB.skip();
         }
+    }
     }
     __syncthreads();  // the epilogue reuses the stage buffers
     // Epilogue: each wave of group 0 stages one 32-row strip of its block at a
@@ -662,12 +718,12 @@ __global__ void splitk_reduce4_kernel(const float* part, int splits, int64_t n, 
 #define G2_GEMM_NS 2
 #endif
 template <int BM, int BN, bool AKC, bool BKC, int EPI, int BK = 64, int NS = G2_GEMM_NS, int WGM = 2, int WGN = 2,
-          int KS = 1, bool SPREAD = false>
+          int KS = 1, bool SPREAD = false, bool REGLOAD = false>
 static hipError_t launch_bf16(const GP& p, int splits, hipStream_t s) {
     const int64_t tiles = (int64_t)((p.N + BN - 1) / BN) * ((p.M + BM - 1) / BM);
     if (tiles > INT32_MAX) return hipErrorInvalidValue;
     dim3 grid((unsigned)tiles, 1, splits);
-    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, BK, AKC, BKC, EPI, NS, WGM, WGN, KS, SPREAD>), grid,
+    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, BK, AKC, BKC, EPI, NS, WGM, WGN, KS, SPREAD, REGLOAD>), grid,
                        dim3(64 * WGM * WGN * KS), 0, s, p);
     return hipGetLastError();
 }
@@ -681,6 +737,16 @@ static hipError_t pick_tile_bf16(const GP& p, int splits, hipStream_t s) {
     return launch_bf16<192, 192, AKC, BKC, EPI, 64, 2, 2, 2, 2>(p, splits, s);
 #elif G2_FORCE_TILE == 14
     return launch_bf16<256, 256, AKC, BKC, EPI, 64, 2, 2, 4, 1>(p, splits, s);
+#elif G2_FORCE_TILE == 30
+    if constexpr (AKC) return launch_bf16<128, 128, AKC, BKC, EPI, 32, 2, 2, 2, 1, false, true>(p, splits, s);
+    else return launch_bf16<128, 128, AKC, BKC, EPI, 64, 2, 2, 2, 1, false, true>(p, splits, s);
+#elif G2_FORCE_TILE == 31
+    return launch_bf16<192, 192, AKC, BKC, EPI, 64, 2, 2, 2, 2, false, true>(p, splits, s);
+#elif G2_FORCE_TILE == 32
+    return launch_bf16<256, 256, AKC, BKC, EPI, 64, 2, 2, 4, 1, false, true>(p, splits, s);
+#elif G2_FORCE_TILE == 33
+    if constexpr (AKC) return launch_bf16<128, 128, AKC, BKC, EPI, 64, 2, 2, 2, 1, false, true>(p, splits, s);
+    else return launch_bf16<128, 128, AKC, BKC, EPI, 64, 2, 2, 2, 1, false, true>(p, splits, s);
 #endif
 #endif
     // Tile policy from measurements on the 124M model's shapes (M = 12288 tokens):
@@ -693,13 +759,17 @@ static hipError_t pick_tile_bf16(const GP& p, int splits, hipStream_t s) {
     //    stages when A is K-contiguous (forward and input gradients), 64-deep for
     //    the weight gradients (both operands transposed, K = tokens).
     if constexpr (!AKC) {
+        // the vocabulary-wide weight gradient (M = padded vocabulary, unsplit):
+        // 256 x 256 tiles, eight waves, operands staged through registers
+        if (!BKC && p.M >= 8192 && splits == 1 && p.K % 64 == 0)
+            return launch_bf16<256, 256, AKC, BKC, EPI, 64, 2, 2, 4, 1, false, true>(p, splits, s);
         return launch_bf16<128, 128, AKC, BKC, EPI, 64>(p, splits, s);
     } else {
         // the column sums of the GELU-derivative epilogue are per 64-row wave block
         if constexpr (EPI == EPI_GELU_BWD)
             if (p.cpart) return launch_bf16<128, 128, AKC, BKC, EPI, 32>(p, splits, s);
         if (p.N % 192 == 0 && p.N <= 1536 && p.K >= 2048 && splits == 1) {
-            if (!BKC && p.K >= 8192) return launch_bf16<192, 192, AKC, BKC, EPI, 64, 2, 2, 2, 2, true>(p, splits, s);
+            if (!BKC && p.K >= 8192) return launch_bf16<192, 192, AKC, BKC, EPI, 64, 2, 2, 2, 2, false, true>(p, splits, s);
             return launch_bf16<192, 192, AKC, BKC, EPI, 64, 2, 2, 2, 2>(p, splits, s);
         }
         if (BKC && p.N >= 8192) return launch_bf16<256, 256, AKC, BKC, EPI, 64, 2, 2, 4, 1>(p, splits, s);
