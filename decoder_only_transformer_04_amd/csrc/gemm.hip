@@ -730,49 +730,47 @@ static hipError_t launch_bf16(const GP& p, int splits, hipStream_t s) {
 
 template <bool AKC, bool BKC, int EPI>
 static hipError_t pick_tile_bf16(const GP& p, int splits, hipStream_t s) {
-#if defined(G2_FORCE_TILE)  // tile experiments only
-#if G2_FORCE_TILE == 3
-    return launch_bf16<128, 128, AKC, BKC, EPI, 32>(p, splits, s);
-#elif G2_FORCE_TILE == 13
+#if defined(G2_FORCE_TILE)  // tile experiments only: one configuration for every product
+#if G2_FORCE_TILE == 40
+    return launch_bf16<128, 128, AKC, BKC, EPI, AKC ? 32 : 64>(p, splits, s);
+#elif G2_FORCE_TILE == 41
     return launch_bf16<192, 192, AKC, BKC, EPI, 64, 2, 2, 2, 2>(p, splits, s);
-#elif G2_FORCE_TILE == 14
+#elif G2_FORCE_TILE == 42
     return launch_bf16<256, 256, AKC, BKC, EPI, 64, 2, 2, 4, 1>(p, splits, s);
-#elif G2_FORCE_TILE == 30
-    if constexpr (AKC) return launch_bf16<128, 128, AKC, BKC, EPI, 32, 2, 2, 2, 1, false, true>(p, splits, s);
-    else return launch_bf16<128, 128, AKC, BKC, EPI, 64, 2, 2, 2, 1, false, true>(p, splits, s);
-#elif G2_FORCE_TILE == 31
+#elif G2_FORCE_TILE == 43
+    return launch_bf16<128, 128, AKC, BKC, EPI, AKC ? 32 : 64, 2, 2, 2, 1, false, true>(p, splits, s);
+#elif G2_FORCE_TILE == 44
     return launch_bf16<192, 192, AKC, BKC, EPI, 64, 2, 2, 2, 2, false, true>(p, splits, s);
-#elif G2_FORCE_TILE == 32
+#elif G2_FORCE_TILE == 45
     return launch_bf16<256, 256, AKC, BKC, EPI, 64, 2, 2, 4, 1, false, true>(p, splits, s);
-#elif G2_FORCE_TILE == 33
-    if constexpr (AKC) return launch_bf16<128, 128, AKC, BKC, EPI, 64, 2, 2, 2, 1, false, true>(p, splits, s);
-    else return launch_bf16<128, 128, AKC, BKC, EPI, 64, 2, 2, 2, 1, false, true>(p, splits, s);
 #endif
 #endif
-    // Tile policy from measurements on the 124M model's shapes (M = 12288 tokens):
-    //  - long contractions onto 768-wide outputs (K >= 2048, N a multiple of 192):
-    //    192 x 192 tiles, one per CU in a single wave of 256 tiles, eight waves in
-    //    two groups splitting each 64-deep stage; for the very long input-gradient
-    //    contraction (K >= 8192) the next stage's loads are spread between the MFMAs;
-    //  - the vocabulary-wide forward product: 256 x 256 tiles, eight waves;
-    //  - otherwise 128 x 128 tiles, two or three workgroups per CU, 32-deep
-    //    stages when A is K-contiguous (forward and input gradients), 64-deep for
-    //    the weight gradients (both operands transposed, K = tokens).
+    // Tile policy from per-product timings inside the 124M training step (M = 12288
+    // tokens; each of the six configurations forced on every product in turn):
+    //  - weight gradients (both operands transposed, K = tokens): operands staged
+    //    through registers; 256 x 256 tiles for the vocabulary-wide one (unsplit),
+    //    128 x 128 with split-K for the others;
+    //  - input gradients (B transposed) onto at most 1536 columns that split into
+    //    192-wide tiles: 192 x 192, eight waves in two groups splitting each stage's
+    //    k-steps, operands staged through registers; the GELU-derivative product,
+    //    whose epilogue takes per-64-row column sums, keeps 128 x 128;
+    //  - forward products: 256 x 256 (eight waves, DMA) for the vocabulary-wide
+    //    one; 192 x 192 (DMA) for long contractions onto <= 1536 columns; else
+    //    128 x 128, operands streamed global -> LDS by DMA (32-deep stages).
     if constexpr (!AKC) {
-        // the vocabulary-wide weight gradient (M = padded vocabulary, unsplit):
-        // 256 x 256 tiles, eight waves, operands staged through registers
         if (!BKC && p.M >= 8192 && splits == 1 && p.K % 64 == 0)
             return launch_bf16<256, 256, AKC, BKC, EPI, 64, 2, 2, 4, 1, false, true>(p, splits, s);
-        return launch_bf16<128, 128, AKC, BKC, EPI, 64>(p, splits, s);
-    } else {
-        // the column sums of the GELU-derivative epilogue are per 64-row wave block
+        return launch_bf16<128, 128, AKC, BKC, EPI, 64, 2, 2, 2, 1, false, true>(p, splits, s);
+    } else if constexpr (!BKC) {
         if constexpr (EPI == EPI_GELU_BWD)
             if (p.cpart) return launch_bf16<128, 128, AKC, BKC, EPI, 32>(p, splits, s);
-        if (p.N % 192 == 0 && p.N <= 1536 && p.K >= 2048 && splits == 1) {
-            if (!BKC && p.K >= 8192) return launch_bf16<192, 192, AKC, BKC, EPI, 64, 2, 2, 2, 2, false, true>(p, splits, s);
+        if (p.N % 192 == 0 && p.N <= 1536 && splits == 1)
+            return launch_bf16<192, 192, AKC, BKC, EPI, 64, 2, 2, 2, 2, false, true>(p, splits, s);
+        return launch_bf16<128, 128, AKC, BKC, EPI, 32>(p, splits, s);
+    } else {
+        if (p.N >= 8192) return launch_bf16<256, 256, AKC, BKC, EPI, 64, 2, 2, 4, 1>(p, splits, s);
+        if (p.N % 192 == 0 && p.N <= 1536 && p.K >= 2048 && splits == 1)
             return launch_bf16<192, 192, AKC, BKC, EPI, 64, 2, 2, 2, 2>(p, splits, s);
-        }
-        if (BKC && p.N >= 8192) return launch_bf16<256, 256, AKC, BKC, EPI, 64, 2, 2, 4, 1>(p, splits, s);
         return launch_bf16<128, 128, AKC, BKC, EPI, 32>(p, splits, s);
     }
 }
