@@ -33,11 +33,11 @@ BENCH_ARGS = ["--steps", "2", "--warmup", "1", "--no-breakdown", "--no-cpu-basel
 # that another label shares with shorter launches)
 LABELS = {
     "gemm.dgrad.fc2": (r"gemm_bf16_kernel<128, 128, 32, true, false, 4,", "all"),
-    "gemm.dgrad.head": (r"gemm_bf16_kernel<192, 192, 64, true, false, 3,", "longest"),
+    "gemm.dgrad.head": (r"gemm_bf16_kernel<192, 192, 64, true, false, 3, 2, 2, 2, 2, false, true>", "longest"),
     "gemm.fwd.head": (r"gemm_bf16_kernel<256, 256, 64, true, true, 0,", "all"),
     "gemm.fwd.fc2": (r"gemm_bf16_kernel<192, 192, 64, true, true, 2,", "all"),
     "gemm.fwd.fc": (r"gemm_bf16_kernel<128, 128, 32, true, true, 1,", "all"),
-    "gemm.wgrad.head": (r"gemm_bf16_kernel<128, 128, 64, false, false, 3,", "longest"),
+    "gemm.wgrad.head": (r"gemm_bf16_kernel<256, 256, 64, false, false, 3,", "all"),
     "attn.fwd": (r"attn_fwd_d64", "all"),
     "attn.bwd.dq": (r"attn_bwd_dq_d64", "all"),
     "attn.bwd.dkdv": (r"attn_bwd_dkdv_d64", "all"),

@@ -227,6 +227,32 @@ def test_gpt2_124m_full_batch_sampled_rows(b, oracle):
     torch.cuda.synchronize()
 
 
+def test_gpt2_124m_eval_64x1024_sampled_rows(b, oracle):
+    """Forward-only evaluation of the 124M model on 64 x 1024 tokens (65,536 rows
+    of full-vocabulary cross-entropy, bf16): the oracle recomputes the first and
+    the last sequence on their own, whose per-position losses must agree; the
+    device mean equals the mean of the device's own per-row losses."""
+    w = syn.WORKLOADS["gpt2_124m_eval"]
+    say("gpt2_124m eval 64x1024 bf16, sequences 0 and 63")
+    named = syn.init_params(w.model)
+    x, y = syn.batch(w)
+    assert x.shape == (64, 1024)
+    g = gpu_model(b, w.model, "bf16", w.batch, w.seq, named, mode=b.MODE_EVAL)
+    g.forward(dev_tokens(x), dev_tokens(y))
+    assert g.sync_status() == 0
+    loss = float(g.loss.item())
+    rows = g.arena_tensor("loss_rows").detach().cpu().numpy()[:, 0].astype(np.float64)
+    assert rows.shape[0] == 64 * 1024
+    assert abs(rows.mean() - loss) <= 1e-5 * abs(loss)
+    cfg = ocfg(oracle, w.model)
+    p = oracle.pack(cfg, named, np.float32)
+    for s in (0, 63):
+        rl, _, rr = oracle.step(cfg, 1, w.seq, p, x[s:s + 1], y[s:s + 1], want_loss_rows=True)
+        got = rows[s * w.seq:(s + 1) * w.seq]
+        assert abs(got.mean() - rl) <= 2e-2, (s, got.mean(), rl)
+        assert np.max(np.abs(got - rr)) <= 0.1, s
+
+
 def test_determinism_bitwise(b):
     import torch
     w = syn.WORKLOADS["char_bf16"]
