@@ -755,8 +755,12 @@ static hipError_t pick_tile_bf16(const GP& p, int splits, hipStream_t s) {
     //    k-steps, operands staged through registers; the GELU-derivative product,
     //    whose epilogue takes per-64-row column sums, keeps 128 x 128;
     //  - forward products: 256 x 256 (eight waves, DMA) for the vocabulary-wide
-    //    one; 192 x 192 (DMA) for long contractions onto <= 1536 columns; else
-    //    128 x 128, operands streamed global -> LDS by DMA (32-deep stages).
+    //    one; 128 x 128 with 64-deep stages and eight waves (32 x 64 each) for
+    //    short contractions onto 2048..8191 columns; 192 x 192 (DMA) for long
+    //    contractions onto <= 1536 columns; else 128 x 128, operands streamed
+    //    global -> LDS by DMA (32-deep stages). A 64-deep stage reads whole
+    //    128-byte rows: L2 serves half-line (64-byte) row reads at about half
+    //    the rate of whole lines.
     if constexpr (!AKC) {
         if (!BKC && p.M >= 8192 && splits == 1 && p.K % 64 == 0)
             return launch_bf16<256, 256, AKC, BKC, EPI, 64, 2, 2, 4, 1, false, true>(p, splits, s);
@@ -768,6 +772,8 @@ static hipError_t pick_tile_bf16(const GP& p, int splits, hipStream_t s) {
             return launch_bf16<192, 192, AKC, BKC, EPI, 64, 2, 2, 2, 2, false, true>(p, splits, s);
         return launch_bf16<128, 128, AKC, BKC, EPI, 32>(p, splits, s);
     } else {
+        if (p.N >= 2048 && p.N < 8192 && p.K <= 1024 && p.K % 64 == 0)
+            return launch_bf16<128, 128, AKC, BKC, EPI, 64, 2, 4, 2, 1>(p, splits, s);
         if (p.N >= 8192) return launch_bf16<256, 256, AKC, BKC, EPI, 64, 2, 2, 4, 1>(p, splits, s);
         if (p.N % 192 == 0 && p.N <= 1536 && p.K >= 2048 && splits == 1)
             return launch_bf16<192, 192, AKC, BKC, EPI, 64, 2, 2, 2, 2>(p, splits, s);

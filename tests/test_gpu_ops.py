@@ -44,7 +44,8 @@ def check_out(dtype, got, ref, what):
 
 # the last two reach the 192 x 192 (N = 768, K >= 2048) and 256 x 256 (N >= 8192)
 # tile paths with ragged row and column tiles
-SHAPES = [(333, 264, 136), (512, 512, 256), (1, 8, 8), (130, 2304, 768), (500, 768, 3072), (300, 8320, 768)]
+SHAPES = [(333, 264, 136), (512, 512, 256), (1, 8, 8), (130, 2304, 768), (257, 2120, 640), (500, 768, 3072),
+          (300, 8320, 768)]
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
