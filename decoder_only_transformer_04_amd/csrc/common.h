@@ -82,10 +82,10 @@ enum ScalarSlot {
 // --------------------------------------------------------------- GEMM
 enum Epilogue {
     EPI_STORE = 0,      // C(act) = alpha*acc + bias
-    EPI_GELU = 1,       // C(act) = u = acc + bias; C2(act) = gelu_tanh(u)
+    EPI_GELU = 1,       // u = acc + bias: C(act) = gelu_tanh'(u), C2(act) = gelu_tanh(u)
     EPI_RESID = 2,      // C(f32) = R(f32) + acc + bias      (C may alias R)
     EPI_F32 = 3,        // C(f32) = alpha*acc (+ C if accumulate)
-    EPI_GELU_BWD = 4    // C(act) = acc * gelu_tanh'(R(act))
+    EPI_GELU_BWD = 4    // C(act) = acc * R(act), R the GELU derivative EPI_GELU wrote
 };
 
 struct GemmArgs {

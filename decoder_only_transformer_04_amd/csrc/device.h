@@ -55,11 +55,13 @@ __device__ __forceinline__ float gelu_sig(float u) {
     const float k0x2 = 1.5957691216057308f, k1 = 0.044715f;  // 2 sqrt(2/pi)
     return __builtin_amdgcn_rcpf(1.0f + __expf(-k0x2 * (u + k1 * u * u * u)));
 }
-__device__ __forceinline__ float gelu_tanh(float u) { return u * gelu_sig(u); }
-__device__ __forceinline__ float gelu_tanh_grad(float u) {
+// GELU and its derivative at u from the same exponential; the forward stores the
+// derivative for the backward, which then needs no exponential of its own
+__device__ __forceinline__ void gelu_tanh_and_grad(float u, float& g, float& dg) {
     const float k0 = 0.7978845608028654f, k1 = 0.044715f;
     const float sg = gelu_sig(u);
-    return sg + 2.0f * u * sg * (1.0f - sg) * k0 * (1.0f + 3.0f * k1 * u * u);
+    g = u * sg;
+    dg = sg + 2.0f * u * sg * (1.0f - sg) * k0 * (1.0f + 3.0f * k1 * u * u);
 }
 
 // Two gfx950 LDS transpose loads (ds_read_b64_tr_b16) 'gap' bytes apart, packed

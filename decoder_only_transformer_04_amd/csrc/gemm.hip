@@ -51,9 +51,10 @@ __device__ __forceinline__ void epi_apply(const GP& p, int64_t m, int n, float v
     if constexpr (EPI == EPI_STORE) {
         Act<T>::st((T*)p.C, m * p.ldc + n, p.alpha * v + bias);
     } else if constexpr (EPI == EPI_GELU) {
-        float u = v + bias;
-        Act<T>::st((T*)p.C, m * p.ldc + n, u);
-        Act<T>::st((T*)p.C2, m * p.ldc2 + n, gelu_tanh(u));
+        float g, dg;
+        gelu_tanh_and_grad(v + bias, g, dg);
+        Act<T>::st((T*)p.C, m * p.ldc + n, dg);
+        Act<T>::st((T*)p.C2, m * p.ldc2 + n, g);
     } else if constexpr (EPI == EPI_RESID) {
         float r = ((const float*)p.R)[m * p.ldr + n];
         ((float*)p.C)[m * p.ldc + n] = r + v + bias;
@@ -63,13 +64,12 @@ __device__ __forceinline__ void epi_apply(const GP& p, int64_t m, int n, float v
         if (p.accumulate) o += *c;
         *c = o;
     } else if constexpr (EPI == EPI_GELU_BWD) {
-        float u = Act<T>::ld((const T*)p.R, m * p.ldr + n);
-        Act<T>::st((T*)p.C, m * p.ldc + n, v * gelu_tanh_grad(u));
+        Act<T>::st((T*)p.C, m * p.ldc + n, v * Act<T>::ld((const T*)p.R, m * p.ldr + n));
     }
 }
 
 // Eight consecutive columns n..n+7 of row m (n % 8 == 0, N % 8 == 0): vector
-// loads of bias / residual / pre-activation and 16- or 32-byte stores.
+// loads of bias / residual / GELU derivative and 16- or 32-byte stores.
 __device__ __forceinline__ uint4 pack8(const float (&o)[8]) {
     uint4 r;
     r.x = pack2bf(o[0], o[1]);
@@ -110,10 +110,7 @@ __device__ __forceinline__ void epi_apply8(const GP& p, int64_t m, int n, const 
     } else if constexpr (EPI == EPI_GELU) {
         float gl[8];
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
-            o[k] = v[k] + bv[k];
-            gl[k] = gelu_tanh(o[k]);
-        }
+        for (int k = 0; k < 8; ++k) gelu_tanh_and_grad(v[k] + bv[k], gl[k], o[k]);
         *(uint4*)((bf16_t*)p.C + m * p.ldc + n) = pack8(o);
         *(uint4*)((bf16_t*)p.C2 + m * p.ldc2 + n) = pack8(gl);
     } else if constexpr (EPI == EPI_RESID) {
@@ -130,10 +127,10 @@ __device__ __forceinline__ void epi_apply8(const GP& p, int64_t m, int n, const 
         for (int k = 0; k < 8; ++k) o[k] = p.alpha * v[k] + (p.accumulate ? prev[k] : 0.0f);
         st8f(c, o);
     } else if constexpr (EPI == EPI_GELU_BWD) {
-        float u[8];
-        unpack8(*(const uint4*)((const bf16_t*)p.R + m * p.ldr + n), u);
+        float dg[8];
+        unpack8(*(const uint4*)((const bf16_t*)p.R + m * p.ldr + n), dg);
 #pragma unroll
-        for (int k = 0; k < 8; ++k) o[k] = v[k] * gelu_tanh_grad(u[k]);
+        for (int k = 0; k < 8; ++k) o[k] = v[k] * dg[k];
         *(uint4*)((bf16_t*)p.C + m * p.ldc + n) = pack8(o);
     }
 }

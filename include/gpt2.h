@@ -178,7 +178,8 @@ int gpt2_timing_end(gpt2_ctx* ctx, float* total_ms, int32_t* launches);
  * name in {"x", "xmid", "ln1", "ln2", "qkv", "att", "lse", "fch", "fcg", "xf",
  * "logits", "loss_rows"}; layer ignored for the last three. *elem_bytes receives
  * 2 or 4. In TRAIN mode "logits" holds the logits gradient after a forward with
- * targets. */
+ * targets. "fcg" is the GELU output of the MLP's first layer and "fch" the GELU
+ * derivative at its pre-activation (the factor the backward applies). */
 int gpt2_arena_tensor(const gpt2_ctx* ctx, const char* name, int32_t layer, size_t* byte_offset,
                       int32_t* elem_bytes, int64_t* rows, int64_t* cols);
 
