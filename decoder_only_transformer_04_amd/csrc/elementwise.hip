@@ -427,14 +427,19 @@ __global__ __launch_bounds__(256) void ln_bwd_v4(const float* dy, const float* x
         const float mu = mean[row], rs = rstd[row];
         const float4* xr = (const float4*)(x + row * C);
         const float4* dr = (const float4*)(dy + row * C);
-        float4 xh[NJ4], d[NJ4];
+        float4* dp = (float4*)(dres + row * C);
+        float4 xh[NJ4], d[NJ4], old[NJ4];
         float a = 0.0f, bb = 0.0f;
+        // the residual gradient being added to is loaded with x and dy, so each
+        // row costs one round trip to memory
 #pragma unroll
         for (int j = 0; j < NJ4; ++j) {
             const int c4 = lane + 64 * j;
+            old[j] = make_float4(0.f, 0.f, 0.f, 0.f);
             if (c4 < C4) {
                 const float4 xv = xr[c4];
                 d[j] = dr[c4];
+                if (add) old[j] = dp[c4];
                 xh[j] = make_float4((xv.x - mu) * rs, (xv.y - mu) * rs, (xv.z - mu) * rs, (xv.w - mu) * rs);
             } else {
                 d[j] = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -457,12 +462,8 @@ __global__ __launch_bounds__(256) void ln_bwd_v4(const float* dy, const float* x
                                        rs * (gg[j].y * d[j].y - a - xh[j].y * bb),
                                        rs * (gg[j].z * d[j].z - a - xh[j].z * bb),
                                        rs * (gg[j].w * d[j].w - a - xh[j].w * bb));
-                float4* dp = (float4*)(dres + row * C) + c4;
-                if (add) {
-                    const float4 old = *dp;
-                    o.x += old.x; o.y += old.y; o.z += old.z; o.w += old.w;
-                }
-                *dp = o;
+                o.x += old[j].x; o.y += old[j].y; o.z += old[j].z; o.w += old[j].w;
+                dp[c4] = o;
                 if (dres_act) st4<T>(dres_act + row * C + 4 * c4, o);
                 pr[j].x += o.x; pr[j].y += o.y; pr[j].z += o.z; pr[j].w += o.w;
             }
