@@ -60,7 +60,13 @@ struct ArenaPlan {
     std::vector<Region> x, xmid, ln1, m1, r1, qkv, att, lse, ln2, m2, r2, fch, fcg;
     Region xL, xf, mf, rf, logits, loss_rows;
     // backward scratch
-    Region dres, dres_act, dtmp, dF, dqkv, datt, attD, ln_part, bias_part;
+    Region dres, dres_act, dtmp, dF, dqkv, datt, attD;
+    // parameter-gradient partials, one buffer per producer so that all of them
+    // are reduced by one launch at the end of the backward: LayerNorm backward
+    // calls in issue order (ln_f, then ln2 and ln1 of each layer from the top),
+    // and per layer the fc and the qkv bias partials
+    std::vector<Region> ln_part, bias_part;
+    Region colsum_jobs;  // the ColsumJob table of those reductions
     Region enc_count, enc_start, enc_segstart, enc_order, enc_segtok;
     size_t total = 0;
     int ln_part_rows = 0;    // partial rows of the LayerNorm parameter-gradient reduction
@@ -125,6 +131,22 @@ hipError_t colsum_finish2(const float* part, int part_rows, int ld, float* out_a
                           int accumulate, hipStream_t s);
 hipError_t colsum_finish3(const float* part, int part_rows, int ld, float* out_a, int na, float* out_b, int nb,
                           float* out_c, int nc, int accumulate, hipStream_t s);
+// One deferred column-sum reduction: out (+)= sums over prows rows of `part`
+// (row stride ld) of its first na + nb + nc columns, split over up to three
+// outputs as colsum_finish3 does; blk0 is the job's first block in the batch.
+struct ColsumJob {
+    const float* part;
+    float* out_a;
+    float* out_b;
+    float* out_c;
+    int prows, ld, na, nb, nc, blk0;
+    int pad[2];
+};
+bool colsum_job_vector(const ColsumJob& j);  // the batched kernel needs multiples of 4
+int colsum_job_blocks(const ColsumJob& j);
+hipError_t colsum_jobs(const ColsumJob* d_jobs, int njobs, int nblocks, int accumulate, hipStream_t s);
+int bias_partial_rows(int64_t rows, int N);  // partial rows bias_partials writes
+hipError_t bias_partials(int dtype, const void* dY, int64_t rows, int N, float* part, int part_rows, hipStream_t s);
 hipError_t bias_grad(int dtype, const void* dY, int64_t rows, int N, float* part, int part_rows, float* db,
                      int accumulate, hipStream_t s);
 hipError_t attention_fwd(int dtype, int B, int T, int C, int H, const void* qkv, void* out, float* lse,

@@ -619,11 +619,11 @@ __global__ __launch_bounds__(1024) void colsum_kernel(const float* part, int pro
 // lanes, 64 row slices each summing every 64th partial row with four
 // independent accumulators (so a thread keeps four loads in flight), then the
 // slices are combined in a fixed order through LDS.
-__global__ __launch_bounds__(1024) void colsum4_kernel(const float* part, int prows, int ld, float* out_a, int na,
-                                                       float* out_b, int nb, float* out_c, int nc, int accumulate) {
+__device__ __forceinline__ void colsum4_block(const float* part, int prows, int ld, float* out_a, int na,
+                                              float* out_b, int nb, float* out_c, int nc, int accumulate, int bx) {
     __shared__ float4 red[64][17];
     const int cl = threadIdx.x & 15, sl = threadIdx.x >> 4;
-    const int c = blockIdx.x * 64 + cl * 4;
+    const int c = bx * 64 + cl * 4;
     const int ncol = na + nb + nc;
     const bool ok = c < ncol;
     float4 acc[4];
@@ -657,12 +657,30 @@ __global__ __launch_bounds__(1024) void colsum4_kernel(const float* part, int pr
         const int j = threadIdx.x, q = j >> 2, e = j & 3;
         float sum = 0.0f;
         for (int k = 0; k < 64; ++k) sum += (&red[k][q].x)[e];
-        const int col = blockIdx.x * 64 + j;
+        const int col = bx * 64 + j;
         if (col < ncol) {
             float* o = colsum_dst(col, out_a, na, out_b, nb, out_c);
             *o = accumulate ? *o + sum : sum;
         }
     }
+}
+__global__ __launch_bounds__(1024) void colsum4_kernel(const float* part, int prows, int ld, float* out_a, int na,
+                                                       float* out_b, int nb, float* out_c, int nc, int accumulate) {
+    colsum4_block(part, prows, ld, out_a, na, out_b, nb, out_c, nc, accumulate, (int)blockIdx.x);
+}
+// Every deferred reduction of a backward pass in one launch: block b serves the
+// job j with jobs[j].blk0 <= b < jobs[j + 1].blk0 (jobs sorted by blk0).
+__global__ __launch_bounds__(1024) void colsum_jobs_kernel(const ColsumJob* jobs, int njobs, int accumulate) {
+    __shared__ int sj;
+    if (threadIdx.x == 0) {
+        int j = 0;
+        while (j + 1 < njobs && jobs[j + 1].blk0 <= (int)blockIdx.x) ++j;
+        sj = j;
+    }
+    __syncthreads();
+    const ColsumJob& jb = jobs[sj];
+    colsum4_block(jb.part, jb.prows, jb.ld, jb.out_a, jb.na, jb.out_b, jb.nb, jb.out_c, jb.nc, accumulate,
+                  (int)blockIdx.x - jb.blk0);
 }
 
 hipError_t colsum_finish3(const float* part, int part_rows, int ld, float* out_a, int na, float* out_b, int nb,
@@ -681,6 +699,15 @@ hipError_t colsum_finish3(const float* part, int part_rows, int ld, float* out_a
 hipError_t colsum_finish2(const float* part, int part_rows, int ld, float* out_a, int na, float* out_b, int nb,
                           int accumulate, hipStream_t s) {
     return colsum_finish3(part, part_rows, ld, out_a, na, out_b, nb, nullptr, 0, accumulate, s);
+}
+
+bool colsum_job_vector(const ColsumJob& j) { return j.na % 4 == 0 && j.nb % 4 == 0 && j.nc % 4 == 0 && j.ld % 4 == 0; }
+int colsum_job_blocks(const ColsumJob& j) { return nblk(j.na + j.nb + j.nc, 64); }
+
+hipError_t colsum_jobs(const ColsumJob* d_jobs, int njobs, int nblocks, int accumulate, hipStream_t s) {
+    if (njobs == 0 || nblocks == 0) return hipSuccess;
+    hipLaunchKernelGGL(colsum_jobs_kernel, dim3(nblocks), dim3(1024), 0, s, d_jobs, njobs, accumulate);
+    return hipGetLastError();
 }
 
 // bias gradient: column sums of dY [rows, N] (act). Vector path (N % 8 == 0):
@@ -741,33 +768,38 @@ __global__ void colpart_kernel(const T* dY, int64_t rows, int N, float* part) {
     for (int64_t r = r0; r < r1; ++r) s += Act<T>::ld(dY, r * N + c);
     part[(int64_t)blockIdx.y * N + c] = s;
 }
-hipError_t bias_grad(int dtype, const void* dY, int64_t rows, int N, float* part, int part_rows, float* db,
-                     int accumulate, hipStream_t s) {
-    if (N == 0) return hipSuccess;
-    if (rows == 0) return colsum_finish2(part, 0, N, db, N, nullptr, 0, accumulate, s);
+int bias_partial_rows(int64_t rows, int N) {
+    return N % 8 == 0 ? (int)((rows + 255) / 256) : (int)((rows + 63) / 64);
+}
+
+hipError_t bias_partials(int dtype, const void* dY, int64_t rows, int N, float* part, int part_rows, hipStream_t s) {
+    if (N == 0 || rows == 0) return hipSuccess;
+    const int pr = bias_partial_rows(rows, N);
+    if (pr > part_rows) return hipErrorInvalidValue;
     if (N % 8 == 0) {
         const int rps = 256;
-        const int pr = (int)((rows + rps - 1) / rps);
-        if (pr > part_rows) return hipErrorInvalidValue;
         dim3 grid(nblk(N, 64), pr);
         if (dtype == GPT2_DTYPE_BF16)
             hipLaunchKernelGGL(colpart8_kernel<bf16_t>, grid, dim3(256), 0, s, (const bf16_t*)dY, rows, N, rps, part);
         else
             hipLaunchKernelGGL(colpart8_kernel<float>, grid, dim3(256), 0, s, (const float*)dY, rows, N, rps, part);
-        hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
-        return colsum_finish2(part, pr, N, db, N, nullptr, 0, accumulate, s);
+        return hipGetLastError();
     }
-    const int pr = (int)((rows + 63) / 64);
-    if (pr > part_rows) return hipErrorInvalidValue;
     dim3 grid(nblk(N, 256), pr);
     if (dtype == GPT2_DTYPE_BF16)
         hipLaunchKernelGGL(colpart_kernel<bf16_t>, grid, dim3(256), 0, s, (const bf16_t*)dY, rows, N, part);
     else
         hipLaunchKernelGGL(colpart_kernel<float>, grid, dim3(256), 0, s, (const float*)dY, rows, N, part);
-    hipError_t e = hipGetLastError();
+    return hipGetLastError();
+}
+
+hipError_t bias_grad(int dtype, const void* dY, int64_t rows, int N, float* part, int part_rows, float* db,
+                     int accumulate, hipStream_t s) {
+    if (N == 0) return hipSuccess;
+    if (rows == 0) return colsum_finish2(part, 0, N, db, N, nullptr, 0, accumulate, s);
+    hipError_t e = bias_partials(dtype, dY, rows, N, part, part_rows, s);
     if (e != hipSuccess) return e;
-    return colsum_finish2(part, pr, N, db, N, nullptr, 0, accumulate, s);
+    return colsum_finish2(part, bias_partial_rows(rows, N), N, db, N, nullptr, 0, accumulate, s);
 }
 
 // ------------------------------------------------------------------ cross-entropy

@@ -27,6 +27,12 @@ struct gpt2_ctx {
     bool have_idx;  // token ids of the last forward saved for the embedding backward
     Region idx_save;
     Region split;   // split-K partials of the weight-gradient GEMMs
+    // the parameter-gradient column sums of a backward pass, reduced together
+    // at its end (table mirrored in the arena when every job suits the batched
+    // kernel, else reduced one job at a time)
+    std::vector<ColsumJob> cjobs;
+    int cjob_blocks = 0;
+    bool cjob_batched = false;
     // optional per-launch timing (gpt2_timing_begin/end)
     bool timing = false;
     std::string timing_prefix;
@@ -99,6 +105,66 @@ hipEvent_t ev_get(gpt2_ctx* x) {
     } while (0)
 
 uint32_t* status_ptr(gpt2_ctx* x) { return at<uint32_t>(x, x->ap.scalars) + SLOT_STATUS; }
+
+float* gf(gpt2_ctx* x, int64_t off);
+
+// The column sums every backward pass leaves to its end, one job per partial
+// buffer: each LayerNorm backward (dgamma, dbeta and, where a Linear bias feeds
+// the residual stream below it, that bias), the fc bias and the qkv bias.
+void build_colsum_jobs(gpt2_ctx* x) {
+    const gpt2_config& c = x->cfg;
+    const ArenaPlan& ap = x->ap;
+    const ParamLayout& pl = x->pl;
+    const int M = ap.M, C = c.n_embd, F = c.mlp_hidden, L = c.n_layer;
+    const bool bf = c.dtype == GPT2_DTYPE_BF16;
+    x->cjobs.clear();
+    auto job = [&](const Region& part, int prows, int ld, float* a, int na, float* b, int nb, float* cc, int nc) {
+        ColsumJob j;
+        std::memset(&j, 0, sizeof(j));
+        j.part = at<float>(x, part);
+        j.prows = prows;
+        j.ld = ld;
+        j.out_a = a; j.na = na;
+        j.out_b = b; j.nb = nb;
+        j.out_c = cc; j.nc = nc;
+        x->cjobs.push_back(j);
+    };
+    auto ln_job = [&](int i, int64_t g_off, int64_t b_off, float* res_bias) {
+        job(ap.ln_part[i], ln_bwd_partial_rows(M), (res_bias ? 3 : 2) * C, gf(x, g_off), C, gf(x, b_off), C, res_bias,
+            res_bias ? C : 0);
+    };
+    ln_job(0, pl.lnf_g, pl.lnf_b, gf(x, pl.layer[L - 1].b_fc2));
+    for (int l = L - 1; l >= 0; --l) {
+        const LayerW& w = pl.layer[l];
+        const int k = L - 1 - l;
+        ln_job(1 + 2 * k, w.ln2_g, w.ln2_b, gf(x, w.b_proj));
+        ln_job(2 + 2 * k, w.ln1_g, w.ln1_b, l > 0 ? gf(x, pl.layer[l - 1].b_fc2) : nullptr);
+        if (w.b_fc >= 0)  // bf16: partials from the GELU-derivative epilogue, 64 rows each
+            job(ap.bias_part[2 * l], bf ? ap.bias_part_rows : bias_partial_rows(M, F), F, gf(x, w.b_fc), F, nullptr, 0,
+                nullptr, 0);
+        if (w.b_qkv >= 0)
+            job(ap.bias_part[2 * l + 1], bias_partial_rows(M, 3 * C), 3 * C, gf(x, w.b_qkv), 3 * C, nullptr, 0,
+                nullptr, 0);
+    }
+    x->cjob_batched = true;
+    int blk = 0;
+    for (ColsumJob& j : x->cjobs) {
+        x->cjob_batched = x->cjob_batched && colsum_job_vector(j);
+        j.blk0 = blk;
+        blk += colsum_job_blocks(j);
+    }
+    x->cjob_blocks = blk;
+}
+
+hipError_t run_colsum_jobs(gpt2_ctx* x, int accumulate, hipStream_t s) {
+    if (x->cjob_batched)
+        return colsum_jobs(at<ColsumJob>(x, x->ap.colsum_jobs), (int)x->cjobs.size(), x->cjob_blocks, accumulate, s);
+    for (const ColsumJob& j : x->cjobs) {
+        hipError_t e = colsum_finish3(j.part, j.prows, j.ld, j.out_a, j.na, j.out_b, j.nb, j.out_c, j.nc, accumulate, s);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
 
 // weight pointer for GEMM operands: bf16 copy or fp32 master
 const void* wptr(gpt2_ctx* x, int64_t off) {
@@ -251,8 +317,12 @@ int gpt2_init(gpt2_ctx** out, const gpt2_config* cfg, const gpt2_buffers* bufs, 
     std::vector<uint8_t> tab((size_t)(x->pl.n_flat / kParamAlign), 0);
     for (const TensorDesc& t : x->pl.tensors)
         for (int64_t c = t.offset / kParamAlign; c < (t.offset + t.reserved) / kParamAlign; ++c) tab[c] = (uint8_t)t.decay;
+    if (x->ap.mode == GPT2_MODE_TRAIN) build_colsum_jobs(x);
     if (hipMemcpyAsync(at<uint8_t>(x, x->ap.decay_tab), tab.data(), tab.size(), hipMemcpyHostToDevice, x->stream) !=
             hipSuccess ||
+        (!x->cjobs.empty() &&
+         hipMemcpyAsync(at<ColsumJob>(x, x->ap.colsum_jobs), x->cjobs.data(), x->cjobs.size() * sizeof(ColsumJob),
+                        hipMemcpyHostToDevice, x->stream) != hipSuccess) ||
         fill_zero(at<char>(x, x->ap.scalars), 256, x->stream) != hipSuccess ||
         hipStreamSynchronize(x->stream) != hipSuccess) {
         delete x;
@@ -355,8 +425,8 @@ int gpt2_backward(gpt2_ctx* x, float loss_scale, int32_t zero_grads) {
     float* dres = at<float>(x, ap.dres);
     void* dres_act = bf ? (void*)at<char>(x, ap.dres_act) : (void*)dres;
     float* dtmp = at<float>(x, ap.dtmp);
-    float* part = at<float>(x, ap.ln_part);
-    float* bpart = at<float>(x, ap.bias_part);
+    // every LayerNorm backward and bias leaves its column-sum partials in a buffer
+    // of its own; run_colsum_jobs reduces them all at the end
     const ParamLayout& pl = x->pl;
 
     // head: dxf = alpha dz . wte ; dwte (=|+=) alpha dz^T . xf
@@ -370,31 +440,29 @@ int gpt2_backward(gpt2_ctx* x, float loss_scale, int32_t zero_grads) {
     const int Ltop = c.n_layer - 1;
     float* b_fc2_top = gf(x, pl.layer[Ltop].b_fc2);
     G2_T("ln.bwd", layernorm_bwd(dt, dtmp, at<float>(x, ap.xL), at<float>(x, ap.mf), at<float>(x, ap.rf), pf(x, pl.lnf_g),
-                         dres, bf ? dres_act : nullptr, part, ap.ln_part_rows, M, C, 0, b_fc2_top != nullptr, s));
-    G2_T("colsum", colsum_finish3(part, ln_bwd_partial_rows(M), (b_fc2_top ? 3 : 2) * C, gf(x, pl.lnf_g), C,
-                                  gf(x, pl.lnf_b), C, b_fc2_top, b_fc2_top ? C : 0, acc, s));
+                         dres, bf ? dres_act : nullptr, at<float>(x, ap.ln_part[0]), ap.ln_part_rows, M, C, 0,
+                         b_fc2_top != nullptr, s));
     for (int l = c.n_layer - 1; l >= 0; --l) {
         const LayerW& w = pl.layer[l];
+        const int k = c.n_layer - 1 - l;
+        float* bpart_fc = at<float>(x, ap.bias_part[2 * l]);
+        float* bpart_qkv = at<float>(x, ap.bias_part[2 * l + 1]);
         // x_out = x_mid + fc2(gelu(fc(ln2(x_mid))))
         // bf16: the GELU-derivative epilogue also leaves per-64-row column sums of
         // dF, the partials of the fc bias gradient (bias_part has (M + 63) / 64 rows)
         const bool fuse_bfc = bf && w.b_fc >= 0;
         G2_T("gemm.dgrad.fc2", linear_dgrad(dt, s, EPI_GELU_BWD, M, C, F, dres_act, C, wptr(x, w.w_fc2), at<char>(x, ap.dF),
-                            at<char>(x, ap.fch[l]), 1.0f, fuse_bfc ? bpart : nullptr));
+                            at<char>(x, ap.fch[l]), 1.0f, fuse_bfc ? bpart_fc : nullptr));
         G2_T("gemm.wgrad.fc2", linear_wgrad(dt, s, M, C, F, dres_act, C, at<char>(x, ap.fcg[l]), gf(x, w.w_fc2), acc, 1.0f, sb, sbytes));
         G2_T("gemm.dgrad.fc", linear_dgrad(dt, s, EPI_F32, M, F, C, at<char>(x, ap.dF), F, wptr(x, w.w_fc), dtmp, nullptr, 1.0f));
         G2_T("gemm.wgrad.fc", linear_wgrad(dt, s, M, F, C, at<char>(x, ap.dF), F, at<char>(x, ap.ln2[l]), gf(x, w.w_fc), acc, 1.0f, sb,
                             sbytes));
-        if (fuse_bfc)
-            G2_T("colsum", colsum_finish2(bpart, ap.bias_part_rows, F, gf(x, w.b_fc), F, nullptr, 0, acc, s));
-        else if (w.b_fc >= 0)
-            G2_T("bias", bias_grad(dt, at<char>(x, ap.dF), M, F, bpart, ap.bias_part_rows, gf(x, w.b_fc), acc, s));
+        if (!fuse_bfc && w.b_fc >= 0)
+            G2_T("bias", bias_partials(dt, at<char>(x, ap.dF), M, F, bpart_fc, ap.bias_part_rows, s));
         float* b_proj = gf(x, w.b_proj);
         G2_T("ln.bwd", layernorm_bwd(dt, dtmp, at<float>(x, ap.xmid[l]), at<float>(x, ap.m2[l]), at<float>(x, ap.r2[l]),
-                             pf(x, w.ln2_g), dres, bf ? dres_act : nullptr, part, ap.ln_part_rows, M, C, 1,
-                             b_proj != nullptr, s));
-        G2_T("colsum", colsum_finish3(part, ln_bwd_partial_rows(M), (b_proj ? 3 : 2) * C, gf(x, w.ln2_g), C,
-                                      gf(x, w.ln2_b), C, b_proj, b_proj ? C : 0, acc, s));
+                             pf(x, w.ln2_g), dres, bf ? dres_act : nullptr, at<float>(x, ap.ln_part[1 + 2 * k]),
+                             ap.ln_part_rows, M, C, 1, b_proj != nullptr, s));
         // x_mid = x_in + proj(attn(ln1(x_in)))
         G2_T("gemm.dgrad.proj", linear_dgrad(dt, s, EPI_STORE, M, C, C, dres_act, C, wptr(x, w.w_proj), at<char>(x, ap.datt), nullptr,
                             1.0f));
@@ -420,13 +488,11 @@ int gpt2_backward(gpt2_ctx* x, float loss_scale, int32_t zero_grads) {
         G2_T("gemm.wgrad.qkv", linear_wgrad(dt, s, M, 3 * C, C, at<char>(x, ap.dqkv), 3 * C, at<char>(x, ap.ln1[l]), gf(x, w.w_qkv), acc,
                             1.0f, sb, sbytes));
         if (w.b_qkv >= 0)
-            G2_T("bias", bias_grad(dt, at<char>(x, ap.dqkv), M, 3 * C, bpart, ap.bias_part_rows, gf(x, w.b_qkv), acc, s));
+            G2_T("bias", bias_partials(dt, at<char>(x, ap.dqkv), M, 3 * C, bpart_qkv, ap.bias_part_rows, s));
         float* b_fc2_below = l > 0 ? gf(x, pl.layer[l - 1].b_fc2) : nullptr;
         G2_T("ln.bwd", layernorm_bwd(dt, dtmp, at<float>(x, ap.x[l]), at<float>(x, ap.m1[l]), at<float>(x, ap.r1[l]),
-                             pf(x, w.ln1_g), dres, bf ? dres_act : nullptr, part, ap.ln_part_rows, M, C, 1,
-                             b_fc2_below != nullptr, s));
-        G2_T("colsum", colsum_finish3(part, ln_bwd_partial_rows(M), (b_fc2_below ? 3 : 2) * C, gf(x, w.ln1_g), C,
-                                      gf(x, w.ln1_b), C, b_fc2_below, b_fc2_below ? C : 0, acc, s));
+                             pf(x, w.ln1_g), dres, bf ? dres_act : nullptr, at<float>(x, ap.ln_part[2 + 2 * k]),
+                             ap.ln_part_rows, M, C, 1, b_fc2_below != nullptr, s));
     }
     // embedding: dwte[idx[m]] += dres[m] (after the head's contribution), dwpe[t] (=|+=) sum_b dres[b,t]
     G2_T("embed.bwd", encoder_bwd(at<int32_t>(x, x->idx_save), dres, gf(x, pl.wte), gf(x, pl.wpe), M, T, C, c.vocab,
@@ -434,6 +500,8 @@ int gpt2_backward(gpt2_ctx* x, float loss_scale, int32_t zero_grads) {
                                   at<int32_t>(x, ap.enc_segstart), at<int32_t>(x, ap.enc_order),
                                   at<int32_t>(x, ap.enc_segtok), at<int32_t>(x, ap.scalars) + SLOT_NSEG, dtmp,
                                   acc, s));
+    // LayerNorm and bias parameter gradients: every column sum of the pass
+    G2_T("colsum", run_colsum_jobs(x, acc, s));
     return GPT2_OK;
 }
 

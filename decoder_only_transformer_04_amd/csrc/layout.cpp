@@ -134,10 +134,12 @@ ArenaPlan make_arena_plan(const gpt2_config& c, const ParamLayout& pl, int B, in
         a.datt = take(M * C * ab);
         a.attD = take((size_t)B * H * T * 4 * 2);  // D and base-2 lse for the attention backward
         a.ln_part_rows = (int)((M + 15) / 16);
-        a.ln_part = take((size_t)a.ln_part_rows * 3 * C * 4);  // dg, db and the dres column sums
+        for (int i = 0; i < 2 * c.n_layer + 1; ++i)
+            a.ln_part.push_back(take((size_t)a.ln_part_rows * 3 * C * 4));  // dg, db and the dres column sums
         size_t maxN = 3 * C > F ? 3 * C : F;
         a.bias_part_rows = (int)((M + 63) / 64);
-        a.bias_part = take((size_t)a.bias_part_rows * maxN * 4);
+        for (int i = 0; i < 2 * c.n_layer; ++i) a.bias_part.push_back(take((size_t)a.bias_part_rows * maxN * 4));
+        a.colsum_jobs = take((size_t)(4 * c.n_layer + 1) * sizeof(ColsumJob));
         a.enc_count = take(Vp * 4);
         a.enc_start = take(Vp * 4);
         a.enc_segstart = take(Vp * 4);
