@@ -84,6 +84,23 @@ def test_tiny_f32_ragged_batch(b, oracle):
     assert np.all(gg["wpe"][37:] == 0)
 
 
+def test_odd_width_f32_step_matches_oracle(b, oracle):
+    """Widths that are not multiples of 4 (C = 30, three heads of 10, MLP 120,
+    with biases) take the scalar paths everywhere, including the one-job-at-a-
+    time reduction of the LayerNorm and bias gradients."""
+    m = syn.Model(65, 16, 30, 3, 2, 120, True)
+    w = syn.Workload("odd_f32", m, 3, 16, "f32", "uniform")
+    say("odd width f32 3x16, C=30")
+    named = syn.init_params(m, seed=11)
+    x, y = syn.batch(w)
+    g = gpu_model(b, m, "f32", w.batch, w.seq, named)
+    loss = run_fwd_bwd(g, x, y)
+    rloss, rg = oracle_grads(oracle, m, named, x, y)
+    assert abs(loss - rloss) / abs(rloss) <= 1e-5, (loss, rloss)
+    compare_grads(gpu_named_grads(g), rg, "f32")
+    assert g.sync_status() == 0
+
+
 def test_adamw_isolated_matches_oracle(b, oracle):
     """Identical gradients on both sides: the update, m and v agree to 1e-6."""
     import torch
