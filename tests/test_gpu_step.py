@@ -270,6 +270,44 @@ def test_gpt2_124m_eval_64x1024_sampled_rows(b, oracle):
         assert np.max(np.abs(got - rr)) <= 0.1, s
 
 
+def test_gpt2_124m_accumulate_clip_adamw(b, oracle):
+    """The accumulation configuration at full size (12 x 1024, bf16), checked by
+    properties that hold at any size: two micro-steps at loss scale 1/2 added
+    into the gradients equal half the sum of the two separate gradients (every
+    backward operation is linear in the logits gradient and halving is exact);
+    the global norm of the accumulated gradients matches an fp64 norm of the
+    host copy; and the clipped AdamW update matches the oracle's update applied
+    to the same host arrays."""
+    import torch
+    w = syn.WORKLOADS["gpt2_124m_accum"]
+    say("gpt2_124m accumulate 2 micro-steps, clip 1.0, adamw")
+    named = syn.init_params(w.model)
+    xa, ya = syn.batch(w, step=0)
+    xb, yb = syn.batch(w, step=1)
+    g = gpu_model(b, w.model, "bf16", w.batch, w.seq, named)
+    run_fwd_bwd(g, xa, ya, 1.0, True)
+    ga = g.grads.detach().cpu().numpy().astype(np.float64)
+    run_fwd_bwd(g, xb, yb, 1.0, True)
+    gb = g.grads.detach().cpu().numpy().astype(np.float64)
+    run_fwd_bwd(g, xa, ya, 0.5, True)
+    run_fwd_bwd(g, xb, yb, 0.5, False)
+    gacc = g.grads.detach().cpu().numpy().astype(np.float64)
+    ref = 0.5 * (ga + gb)
+    assert np.max(np.abs(gacc - ref)) <= 1e-6 * np.max(np.abs(ref))
+    p0 = g.params.detach().cpu().numpy().astype(np.float64)
+    g.adamw_step(w.lr, w.beta1, w.beta2, w.eps, w.weight_decay, 1, clip=w.clip, want_norm=True)
+    torch.cuda.synchronize()
+    gc = gacc.copy()
+    n_ref = oracle.clip(gc, w.clip)
+    assert abs(float(g.grad_norm.item()) - n_ref) <= 1e-5 * n_ref
+    m = np.zeros_like(p0)
+    v = np.zeros_like(p0)
+    oracle.adamw(p0, gc, m, v, w.lr, w.beta1, w.beta2, w.eps, w.weight_decay, 1)
+    p1 = g.params.detach().cpu().numpy().astype(np.float64)
+    assert np.max(np.abs(p1 - p0)) <= 1e-6 * np.max(np.abs(p0)) + 1e-7
+    assert g.sync_status() == 0
+
+
 def test_determinism_bitwise(b):
     import torch
     w = syn.WORKLOADS["char_bf16"]
