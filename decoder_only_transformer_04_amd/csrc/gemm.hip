@@ -18,6 +18,10 @@
 
 #include "device.h"
 
+#ifndef G2_GEMM_SCHED
+#define G2_GEMM_SCHED 0
+#endif
+
 #ifndef G2_GEMM_IGLP
 #define G2_GEMM_IGLP -1
 #endif
@@ -322,6 +326,9 @@ __device__ __forceinline__ void mma_stage(const char* cur, f32x16 (&acc)[FM][FN]
         for (int j = 0; j < FN; ++j) bv[buf][j] = tile_frag<BN, BKC, BK>(cur + ABYTES, wn * WN + j * 32, kk, lane);
     };
     load(0, ks);
+#if G2_GEMM_SCHED
+    __builtin_amdgcn_sched_group_barrier(0x100, FM + FN, 0);  // DS reads of step 0
+#endif
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
         if (kk + 1 < KK) load((kk + 1) & 1, ks + (kk + 1) * KS);
@@ -333,6 +340,27 @@ __device__ __forceinline__ void mma_stage(const char* cur, f32x16 (&acc)[FM][FN]
                 const int q = (kk * FM + i) * FN + j;  // constant after unrolling
                 if (ND > 0 && q % EVERY == 0 && q / EVERY < ND) dma(q / EVERY);
             }
+#if G2_GEMM_SCHED
+        // Keep the next step's fragment reads ahead of this step's MFMAs. Left
+        // alone, the scheduler sinks each read to just before its first use (to
+        // shorten live ranges), which puts an LDS round trip in front of every
+        // few MFMAs; pinned here, a read has a whole step of MFMAs to land.
+        if (kk + 1 < KK) {
+#if G2_GEMM_SCHED == 1
+            __builtin_amdgcn_sched_group_barrier(0x100, FM + FN, 0);  // DS reads of step kk + 1
+            __builtin_amdgcn_sched_group_barrier(0x008, FM * FN, 0);  // MFMAs of step kk
+#else
+            // one read after each MFMA
+#pragma unroll
+            for (int q = 0; q < FM * FN; ++q) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                if (q < FM + FN) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            }
+#endif
+        } else {
+            __builtin_amdgcn_sched_group_barrier(0x008, FM * FN, 0);  // MFMAs of the last step
+        }
+#endif
     }
     if constexpr (ND > 0) {
         // any instructions the spread did not reach
@@ -791,6 +819,53 @@ static hipError_t dispatch(int dtype, const GP& p, int splits, hipStream_t s) {
     return launch_f32<AKC, BKC, EPI>(p, splits, s);
 }
 
+#ifndef G2_WG_BIG
+#define G2_WG_BIG 1
+#endif
+// 256 x 256 weight-gradient tiles (one workgroup per CU, half the operand
+// traffic per FLOP of 128 x 128) for outputs of at least 2304 x 768; smaller
+// outputs would need so many splits that the partial sums cost more than the
+// larger tile saves.
+static bool wgrad_big_tile(const GemmArgs& a) {
+    if (!G2_WG_BIG) return false;
+    return a.M % 256 == 0 && a.N % 256 == 0 && a.M * a.N >= (int64_t)2304 * 768;
+}
+
+// Weight gradient (both operands with the contraction index strided) over
+// BM x BN register-staged tiles. `slots` is how many such workgroups the GPU
+// holds at once; the contraction is split into as many 64-aligned pieces as
+// fill them (at least MINK deep each, and within the partial-sum buffer), each
+// piece writes its own fp32 partial, and one launch sums the partials in split
+// order into dW (adding to it when accumulating).
+template <int BM, int BN, int WGM, int WGN, int MINK>
+static hipError_t wgrad_split(const GemmArgs& a, const GP& p, int slots, hipStream_t s) {
+    const int64_t tiles = (int64_t)((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
+    int splits = 1;
+    if (tiles < slots) {
+        splits = (int)std::min<int64_t>(std::max<int64_t>(1, slots / tiles), a.K / MINK);
+        while (splits > 1 && (size_t)splits * a.M * a.N * 4 > a.split_bytes) --splits;
+    }
+    if (splits <= 1) return pick_tile_bf16<false, false, EPI_F32>(p, 1, s);
+    int kps = (int)(((a.K + splits - 1) / splits + 63) / 64 * 64);
+    splits = (a.K + kps - 1) / kps;
+    GP q = p;
+    q.k_per_split = kps;
+    q.C = a.split_buf;
+    q.ldc = a.N;
+    q.c_split_stride = (int64_t)a.M * a.N;
+    q.accumulate = 0;
+    hipError_t e = launch_bf16<BM, BN, false, false, EPI_F32, 64, 2, WGM, WGN, 1, false, true>(q, splits, s);
+    if (e != hipSuccess) return e;
+    const int64_t n = (int64_t)a.M * a.N;
+    if (a.N % 4 == 0 && a.ldc % 4 == 0 && ((uintptr_t)a.C & 15) == 0)
+        hipLaunchKernelGGL(splitk_reduce4_kernel, dim3((unsigned)((n / 4 + 255) / 256)), dim3(256), 0, s,
+                           (const float*)a.split_buf, splits, n, (float*)a.C, a.N, a.ldc, a.accumulate);
+    else
+        hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
+                           (const float*)a.split_buf, splits, n, (float*)a.C, a.M, a.N, a.ldc, a.accumulate);
+    return hipGetLastError();
+}
+
 hipError_t gemm(int dtype, const GemmArgs& a, hipStream_t s) {
     GP p;
     p.A = a.A; p.B = a.B; p.lda = a.lda; p.ldb = a.ldb;
@@ -824,31 +899,9 @@ hipError_t gemm(int dtype, const GemmArgs& a, hipStream_t s) {
     } else if (kc00 && a.epi == EPI_F32) {
         // weight gradients: contraction over all tokens; split K when the output
         // alone would not fill the GPU, reducing the partials in fixed order
-        int splits = 1;
-        const int64_t tiles = (int64_t)((a.M + 127) / 128) * ((a.N + 127) / 128);
-        if (dtype == GPT2_DTYPE_BF16 && a.split_buf && tiles < 256 && a.K >= 1024) {
-            splits = (int)std::min<int64_t>(std::max<int64_t>(1, 512 / tiles), a.K / 512);
-            while (splits > 1 && (size_t)splits * a.M * a.N * 4 > a.split_bytes) --splits;
-        }
-        if (splits <= 1) return dispatch<false, false, EPI_F32>(dtype, p, 1, s);
-        int kps = (int)(((a.K + splits - 1) / splits + 63) / 64 * 64);
-        splits = (a.K + kps - 1) / kps;
-        GP q = p;
-        q.k_per_split = kps;
-        q.C = a.split_buf;
-        q.ldc = a.N;
-        q.c_split_stride = (int64_t)a.M * a.N;
-        q.accumulate = 0;
-        hipError_t e = dispatch<false, false, EPI_F32>(dtype, q, splits, s);
-        if (e != hipSuccess) return e;
-        const int64_t n = (int64_t)a.M * a.N;
-        if (a.N % 4 == 0 && a.ldc % 4 == 0 && ((uintptr_t)a.C & 15) == 0)
-            hipLaunchKernelGGL(splitk_reduce4_kernel, dim3((unsigned)((n / 4 + 255) / 256)), dim3(256), 0, s,
-                               (const float*)a.split_buf, splits, n, (float*)a.C, a.N, a.ldc, a.accumulate);
-        else
-            hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
-                               (const float*)a.split_buf, splits, n, (float*)a.C, a.M, a.N, a.ldc, a.accumulate);
-        return hipGetLastError();
+        if (dtype != GPT2_DTYPE_BF16 || !a.split_buf || a.K < 1024) return dispatch<false, false, EPI_F32>(dtype, p, 1, s);
+        if (wgrad_big_tile(a)) return wgrad_split<256, 256, 2, 4, 1024>(a, p, 256, s);
+        return wgrad_split<128, 128, 2, 2, 512>(a, p, 512, s);
     }
     return hipErrorInvalidValue;
 }

@@ -66,7 +66,8 @@ size_t extra_bytes(const gpt2_config& c, const ArenaPlan& ap, size_t* idx_off, s
     *split_off = off;
     size_t C = c.n_embd, F = c.mlp_hidden;
     size_t biggest = 3 * C * C > F * C ? 3 * C * C : F * C;
-    *split_sz = ap.mode == GPT2_MODE_TRAIN && c.dtype == GPT2_DTYPE_BF16 ? biggest * 4 * 4 : 0;
+    // up to 9 fp32 partials of the largest weight (split-K weight gradients)
+    *split_sz = ap.mode == GPT2_MODE_TRAIN && c.dtype == GPT2_DTYPE_BF16 ? biggest * 4 * 9 : 0;
     off += (*split_sz + 255) / 256 * 256;
     return off - ap.total;
 }
