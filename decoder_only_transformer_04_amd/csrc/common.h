@@ -60,7 +60,11 @@ struct ArenaPlan {
     std::vector<Region> x, xmid, ln1, m1, r1, qkv, att, lse, ln2, m2, r2, fch, fcg;
     Region xL, xf, mf, rf, logits, loss_rows;
     // backward scratch
-    Region dres, dres_act, dtmp, dF, dqkv, datt, attD;
+    // dres_act / dres_act2: activation-type copies of the residual gradient,
+    // written alternately (LayerNorm-f and LN1 backward, LN2 backward) so a
+    // weight gradient reading one has a whole sub-layer to finish before the
+    // next write to it
+    Region dres, dres_act, dres_act2, dtmp, dF, dqkv, datt, attD;
     // parameter-gradient partials, one buffer per producer so that all of them
     // are reduced by one launch at the end of the backward: LayerNorm backward
     // calls in issue order (ln_f, then ln2 and ln1 of each layer from the top),

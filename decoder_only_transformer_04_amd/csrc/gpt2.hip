@@ -22,6 +22,11 @@ struct gpt2_ctx {
     ArenaPlan ap;
     gpt2_buffers bufs;
     hipStream_t stream;
+    // bf16 training: the backward's weight gradients run on a second stream of
+    // the library's own (default priority), forked from and joined back into
+    // `stream` with the events below; null when everything runs on `stream`
+    hipStream_t wstream = nullptr;
+    std::vector<hipEvent_t> wev;
     char* arena;
     bool have_dz;   // a TRAIN forward with targets wrote the logits gradient
     bool have_idx;  // token ids of the last forward saved for the embedding backward
@@ -101,6 +106,20 @@ hipEvent_t ev_get(gpt2_ctx* x) {
         hipEvent_t b_ = t_ ? ev_get(x) : nullptr;                               \
         if (a_ && b_) {                                                         \
             G2_TRY(hipEventRecord(b_, x->stream));                              \
+            x->ev_pairs.push_back({a_, b_});                                    \
+        }                                                                       \
+    } while (0)
+
+// as G2_T, for a launch on stream `st`
+#define G2_TS(label, st, expr)                                                  \
+    do {                                                                        \
+        const bool t_ = timing_on(x, label);                                    \
+        hipEvent_t a_ = t_ ? ev_get(x) : nullptr;                               \
+        if (a_) G2_TRY(hipEventRecord(a_, st));                                 \
+        G2_TRY(expr);                                                           \
+        hipEvent_t b_ = t_ ? ev_get(x) : nullptr;                               \
+        if (a_ && b_) {                                                         \
+            G2_TRY(hipEventRecord(b_, st));                                     \
             x->ev_pairs.push_back({a_, b_});                                    \
         }                                                                       \
     } while (0)
@@ -329,9 +348,23 @@ int gpt2_init(gpt2_ctx** out, const gpt2_config* cfg, const gpt2_buffers* bufs, 
         delete x;
         return GPT2_EHIP;
     }
+    if (x->ap.mode == GPT2_MODE_TRAIN && x->cfg.dtype == GPT2_DTYPE_BF16) {
+        // fork/join events of one backward pass: 4 forks and 4 marks per layer, 2 for the head
+        const size_t nev = 8 * (size_t)x->cfg.n_layer + 2;
+        bool ok = hipStreamCreateWithFlags(&x->wstream, hipStreamNonBlocking) == hipSuccess;
+        for (size_t i = 0; ok && i < nev; ++i) {
+            hipEvent_t e = nullptr;
+            ok = hipEventCreateWithFlags(&e, hipEventDisableTiming) == hipSuccess;
+            if (ok) x->wev.push_back(e);
+        }
+        if (!ok) {
+            gpt2_destroy(x);
+            return GPT2_EHIP;
+        }
+    }
     int r = gpt2_refresh_weights(x);
     if (r) {
-        delete x;
+        gpt2_destroy(x);
         return r;
     }
     *out = x;
@@ -347,7 +380,10 @@ int gpt2_refresh_weights(gpt2_ctx* x) {
 
 void gpt2_destroy(gpt2_ctx* x) {
     if (!x) return;
+    if (x->wstream) (void)hipStreamSynchronize(x->wstream);
     for (hipEvent_t e : x->ev_pool) (void)hipEventDestroy(e);
+    for (hipEvent_t e : x->wev) (void)hipEventDestroy(e);
+    if (x->wstream) (void)hipStreamDestroy(x->wstream);
     delete x;
 }
 
@@ -424,16 +460,45 @@ int gpt2_backward(gpt2_ctx* x, float loss_scale, int32_t zero_grads) {
     const size_t sbytes = x->split.bytes;
     const float alpha = loss_scale / (float)M;  // d(mean loss)/dlogits = (softmax - onehot) / (B*T)
     float* dres = at<float>(x, ap.dres);
-    void* dres_act = bf ? (void*)at<char>(x, ap.dres_act) : (void*)dres;
+    // LayerNorm-f and LN1 backward write the activation copy of the residual
+    // gradient to dres_a, LN2 backward to dres_b (fp32: both are dres itself)
+    void* dres_a = bf ? (void*)at<char>(x, ap.dres_act) : (void*)dres;
+    void* dres_b = bf ? (void*)at<char>(x, ap.dres_act2) : (void*)dres;
     float* dtmp = at<float>(x, ap.dtmp);
     // every LayerNorm backward and bias leaves its column-sum partials in a buffer
     // of its own; run_colsum_jobs reduces them all at the end
     const ParamLayout& pl = x->pl;
 
+    // Weight gradients go to the second stream `ws` when there is one: each is
+    // forked after the launch producing its operands (fork) and marked when
+    // done (mark); the main stream waits for a mark (join) before overwriting
+    // an operand that weight gradient reads. They run in the order launched, so
+    // the split-K partial buffer they share is never in use twice at once.
+    hipStream_t ws = x->wstream ? x->wstream : s;
+    enum { EV_FORK = 0, EV_MARK = 1 };
+    auto ev = [&](int slot, int which) { return x->wev[2 * slot + which]; };
+    auto fork = [&](int slot) -> hipError_t {
+        if (!x->wstream) return hipSuccess;
+        hipError_t e = hipEventRecord(ev(slot, EV_FORK), s);
+        return e != hipSuccess ? e : hipStreamWaitEvent(ws, ev(slot, EV_FORK), 0);
+    };
+    auto mark = [&](int slot) -> hipError_t {
+        return x->wstream ? hipEventRecord(ev(slot, EV_MARK), ws) : hipSuccess;
+    };
+    auto join = [&](int slot) -> hipError_t {
+        return x->wstream ? hipStreamWaitEvent(s, ev(slot, EV_MARK), 0) : hipSuccess;
+    };
+    // slots: 4 per layer (fc2, fc, proj, qkv weight gradients), then the head
+    auto slot = [&](int l, int which) { return 4 * l + which; };
+    enum { W_FC2 = 0, W_FC = 1, W_PROJ = 2, W_QKV = 3 };
+    const int slot_head = 4 * c.n_layer;
+
     // head: dxf = alpha dz . wte ; dwte (=|+=) alpha dz^T . xf
     G2_T("gemm.dgrad.head", linear_dgrad(dt, s, EPI_F32, M, Vp, C, at<char>(x, ap.logits), Vp, wptr(x, pl.wte), dtmp, nullptr, alpha));
-    G2_T("gemm.wgrad.head", linear_wgrad(dt, s, M, Vp, C, at<char>(x, ap.logits), Vp, at<char>(x, ap.xf), gf(x, pl.wte), acc, alpha, sb,
-                        sbytes));
+    G2_TRY(fork(slot_head));
+    G2_TS("gemm.wgrad.head", ws, linear_wgrad(dt, ws, M, Vp, C, at<char>(x, ap.logits), Vp, at<char>(x, ap.xf), gf(x, pl.wte), acc,
+                                          alpha, sb, sbytes));
+    G2_TRY(mark(slot_head));
     // Each LayerNorm backward also sums the columns of the residual gradient it
     // leaves behind, which is the bias gradient of the linear layer writing into
     // the residual stream just before it: fc2 of the layer below for ln_f and
@@ -441,34 +506,44 @@ int gpt2_backward(gpt2_ctx* x, float loss_scale, int32_t zero_grads) {
     const int Ltop = c.n_layer - 1;
     float* b_fc2_top = gf(x, pl.layer[Ltop].b_fc2);
     G2_T("ln.bwd", layernorm_bwd(dt, dtmp, at<float>(x, ap.xL), at<float>(x, ap.mf), at<float>(x, ap.rf), pf(x, pl.lnf_g),
-                         dres, bf ? dres_act : nullptr, at<float>(x, ap.ln_part[0]), ap.ln_part_rows, M, C, 0,
+                         dres, bf ? dres_a : nullptr, at<float>(x, ap.ln_part[0]), ap.ln_part_rows, M, C, 0,
                          b_fc2_top != nullptr, s));
     for (int l = c.n_layer - 1; l >= 0; --l) {
         const LayerW& w = pl.layer[l];
         const int k = c.n_layer - 1 - l;
+        const bool above = l + 1 < c.n_layer;  // a layer above has weight gradients in flight
         float* bpart_fc = at<float>(x, ap.bias_part[2 * l]);
         float* bpart_qkv = at<float>(x, ap.bias_part[2 * l + 1]);
         // x_out = x_mid + fc2(gelu(fc(ln2(x_mid))))
+        G2_TRY(fork(slot(l, W_FC2)));
+        G2_TS("gemm.wgrad.fc2", ws, linear_wgrad(dt, ws, M, C, F, dres_a, C, at<char>(x, ap.fcg[l]), gf(x, w.w_fc2), acc, 1.0f, sb,
+                                             sbytes));
+        G2_TRY(mark(slot(l, W_FC2)));
         // bf16: the GELU-derivative epilogue also leaves per-64-row column sums of
         // dF, the partials of the fc bias gradient (bias_part has (M + 63) / 64 rows)
         const bool fuse_bfc = bf && w.b_fc >= 0;
-        G2_T("gemm.dgrad.fc2", linear_dgrad(dt, s, EPI_GELU_BWD, M, C, F, dres_act, C, wptr(x, w.w_fc2), at<char>(x, ap.dF),
+        if (above) G2_TRY(join(slot(l + 1, W_FC)));  // dF is read by the fc weight gradient above
+        G2_T("gemm.dgrad.fc2", linear_dgrad(dt, s, EPI_GELU_BWD, M, C, F, dres_a, C, wptr(x, w.w_fc2), at<char>(x, ap.dF),
                             at<char>(x, ap.fch[l]), 1.0f, fuse_bfc ? bpart_fc : nullptr));
-        G2_T("gemm.wgrad.fc2", linear_wgrad(dt, s, M, C, F, dres_act, C, at<char>(x, ap.fcg[l]), gf(x, w.w_fc2), acc, 1.0f, sb, sbytes));
+        G2_TRY(fork(slot(l, W_FC)));
+        G2_TS("gemm.wgrad.fc", ws, linear_wgrad(dt, ws, M, F, C, at<char>(x, ap.dF), F, at<char>(x, ap.ln2[l]), gf(x, w.w_fc), acc,
+                                            1.0f, sb, sbytes));
+        G2_TRY(mark(slot(l, W_FC)));
         G2_T("gemm.dgrad.fc", linear_dgrad(dt, s, EPI_F32, M, F, C, at<char>(x, ap.dF), F, wptr(x, w.w_fc), dtmp, nullptr, 1.0f));
-        G2_T("gemm.wgrad.fc", linear_wgrad(dt, s, M, F, C, at<char>(x, ap.dF), F, at<char>(x, ap.ln2[l]), gf(x, w.w_fc), acc, 1.0f, sb,
-                            sbytes));
         if (!fuse_bfc && w.b_fc >= 0)
             G2_T("bias", bias_partials(dt, at<char>(x, ap.dF), M, F, bpart_fc, ap.bias_part_rows, s));
         float* b_proj = gf(x, w.b_proj);
+        if (above) G2_TRY(join(slot(l + 1, W_PROJ)));  // dres_b is read by the projection weight gradient above
         G2_T("ln.bwd", layernorm_bwd(dt, dtmp, at<float>(x, ap.xmid[l]), at<float>(x, ap.m2[l]), at<float>(x, ap.r2[l]),
-                             pf(x, w.ln2_g), dres, bf ? dres_act : nullptr, at<float>(x, ap.ln_part[1 + 2 * k]),
+                             pf(x, w.ln2_g), dres, bf ? dres_b : nullptr, at<float>(x, ap.ln_part[1 + 2 * k]),
                              ap.ln_part_rows, M, C, 1, b_proj != nullptr, s));
         // x_mid = x_in + proj(attn(ln1(x_in)))
-        G2_T("gemm.dgrad.proj", linear_dgrad(dt, s, EPI_STORE, M, C, C, dres_act, C, wptr(x, w.w_proj), at<char>(x, ap.datt), nullptr,
+        G2_TRY(fork(slot(l, W_PROJ)));
+        G2_TS("gemm.wgrad.proj", ws, linear_wgrad(dt, ws, M, C, C, dres_b, C, at<char>(x, ap.att[l]), gf(x, w.w_proj), acc, 1.0f,
+                                              sb, sbytes));
+        G2_TRY(mark(slot(l, W_PROJ)));
+        G2_T("gemm.dgrad.proj", linear_dgrad(dt, s, EPI_STORE, M, C, C, dres_b, C, wptr(x, w.w_proj), at<char>(x, ap.datt), nullptr,
                             1.0f));
-        G2_T("gemm.wgrad.proj", linear_wgrad(dt, s, M, C, C, dres_act, C, at<char>(x, ap.att[l]), gf(x, w.w_proj), acc, 1.0f, sb,
-                            sbytes));
         {
             const char* qkv_l = at<char>(x, ap.qkv[l]);
             const char* att_l = at<char>(x, ap.att[l]);
@@ -476,6 +551,7 @@ int gpt2_backward(gpt2_ctx* x, float loss_scale, int32_t zero_grads) {
             char* datt = at<char>(x, ap.datt);
             char* dqkv = at<char>(x, ap.dqkv);
             float* attD = at<float>(x, ap.attD);
+            if (above) G2_TRY(join(slot(l + 1, W_QKV)));  // dqkv is read by the qkv weight gradient above
             if (attention_bwd_staged(dt, C, H)) {
                 G2_T("attn.bwd.dq", attention_bwd(dt, ap.B, T, C, H, qkv_l, att_l, lse_l, datt, dqkv, attD, s, ATT_BWD_DQ));
                 G2_T("attn.bwd.dkdv",
@@ -484,17 +560,23 @@ int gpt2_backward(gpt2_ctx* x, float loss_scale, int32_t zero_grads) {
                 G2_T("attn.bwd", attention_bwd(dt, ap.B, T, C, H, qkv_l, att_l, lse_l, datt, dqkv, attD, s));
             }
         }
+        G2_TRY(fork(slot(l, W_QKV)));
+        G2_TS("gemm.wgrad.qkv", ws, linear_wgrad(dt, ws, M, 3 * C, C, at<char>(x, ap.dqkv), 3 * C, at<char>(x, ap.ln1[l]),
+                                             gf(x, w.w_qkv), acc, 1.0f, sb, sbytes));
+        G2_TRY(mark(slot(l, W_QKV)));
         G2_T("gemm.dgrad.qkv", linear_dgrad(dt, s, EPI_F32, M, 3 * C, C, at<char>(x, ap.dqkv), 3 * C, wptr(x, w.w_qkv), dtmp, nullptr,
                             1.0f));
-        G2_T("gemm.wgrad.qkv", linear_wgrad(dt, s, M, 3 * C, C, at<char>(x, ap.dqkv), 3 * C, at<char>(x, ap.ln1[l]), gf(x, w.w_qkv), acc,
-                            1.0f, sb, sbytes));
         if (w.b_qkv >= 0)
             G2_T("bias", bias_partials(dt, at<char>(x, ap.dqkv), M, 3 * C, bpart_qkv, ap.bias_part_rows, s));
         float* b_fc2_below = l > 0 ? gf(x, pl.layer[l - 1].b_fc2) : nullptr;
+        G2_TRY(join(slot(l, W_FC2)));  // dres_a is read by this layer's fc2 weight gradient
         G2_T("ln.bwd", layernorm_bwd(dt, dtmp, at<float>(x, ap.x[l]), at<float>(x, ap.m1[l]), at<float>(x, ap.r1[l]),
-                             pf(x, w.ln1_g), dres, bf ? dres_act : nullptr, at<float>(x, ap.ln_part[2 + 2 * k]),
+                             pf(x, w.ln1_g), dres, bf ? dres_a : nullptr, at<float>(x, ap.ln_part[2 + 2 * k]),
                              ap.ln_part_rows, M, C, 1, b_fc2_below != nullptr, s));
     }
+    // every weight gradient has finished (the stream runs them in order and this
+    // is the last one): the embedding backward adds into dwte after the head's
+    G2_TRY(join(slot(0, W_QKV)));
     // embedding: dwte[idx[m]] += dres[m] (after the head's contribution), dwpe[t] (=|+=) sum_b dres[b,t]
     G2_T("embed.bwd", encoder_bwd(at<int32_t>(x, x->idx_save), dres, gf(x, pl.wte), gf(x, pl.wpe), M, T, C, c.vocab,
                                   at<int32_t>(x, ap.enc_count), at<int32_t>(x, ap.enc_start),

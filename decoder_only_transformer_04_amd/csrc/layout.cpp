@@ -128,6 +128,7 @@ ArenaPlan make_arena_plan(const gpt2_config& c, const ParamLayout& pl, int B, in
     if (train) {
         a.dres = take(M * C * 4);
         a.dres_act = take(M * C * ab);
+        a.dres_act2 = take(M * C * ab);
         a.dtmp = take(M * C * 4);
         a.dF = take(M * F * ab);
         a.dqkv = take(M * 3 * C * ab);
