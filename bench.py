@@ -78,6 +78,14 @@ LABELS = ["gemm.fwd.qkv", "gemm.fwd.proj", "gemm.fwd.fc", "gemm.fwd.fc2", "gemm.
           "bias", "embed.fwd", "embed.bwd", "gradnorm", "adamw"]
 
 
+# Labels whose launches run with no other work of the step beside them: the
+# forward pass, the head's input gradient, the optimizer. The rest of the
+# backward overlaps the weight gradients, which run on the library's second
+# stream, so a per-launch duration there covers a kernel and its neighbour
+# sharing the GPU; the roofline kernel is the largest of these labels.
+SOLO = {"gemm.fwd.qkv", "gemm.fwd.proj", "gemm.fwd.fc", "gemm.fwd.fc2", "gemm.fwd.head", "gemm.dgrad.head",
+        "attn.fwd", "ln.fwd", "ce", "loss", "embed.fwd", "gradnorm", "adamw"}
+
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_gpt2_124m_12x1024.json")
 
 
@@ -187,7 +195,7 @@ def main():
     if args.roofline_kernel:
         dominant = args.roofline_kernel
     elif breakdown:
-        dominant = max((l for l in breakdown if kernel_work(l, w)[0]), key=lambda l: breakdown[l])
+        dominant = max((l for l in breakdown if kernel_work(l, w)[0] and l in SOLO), key=lambda l: breakdown[l])
     else:
         dominant = "gemm.fwd.head"
     if kernel_work(dominant, w)[0] is None:

@@ -37,7 +37,7 @@ LABELS = {
     "gemm.fwd.head": (r"gemm_bf16_kernel<256, 256, 64, true, true, 0,", "all"),
     "gemm.fwd.fc2": (r"gemm_bf16_kernel<192, 192, 64, true, true, 2,", "all"),
     "gemm.fwd.fc": (r"gemm_bf16_kernel<128, 128, 64, true, true, 1, 2, 4, 2,", "all"),
-    "gemm.wgrad.head": (r"gemm_bf16_kernel<256, 256, 64, false, false, 3,", "all"),
+    "gemm.wgrad.head": (r"gemm_bf16_kernel<256, 256, 64, false, false, 3,", "longest"),
     "attn.fwd": (r"attn_fwd_d64", "all"),
     "attn.bwd.dq": (r"attn_bwd_dq_d64", "all"),
     "attn.bwd.dkdv": (r"attn_bwd_dkdv_d64", "all"),

@@ -574,9 +574,8 @@ int gpt2_backward(gpt2_ctx* x, float loss_scale, int32_t zero_grads) {
                              pf(x, w.ln1_g), dres, bf ? dres_a : nullptr, at<float>(x, ap.ln_part[2 + 2 * k]),
                              ap.ln_part_rows, M, C, 1, b_fc2_below != nullptr, s));
     }
-    // every weight gradient has finished (the stream runs them in order and this
-    // is the last one): the embedding backward adds into dwte after the head's
-    G2_TRY(join(slot(0, W_QKV)));
+    // the embedding backward adds into dwte after the head's weight gradient
+    G2_TRY(join(slot_head));
     // embedding: dwte[idx[m]] += dres[m] (after the head's contribution), dwpe[t] (=|+=) sum_b dres[b,t]
     G2_T("embed.bwd", encoder_bwd(at<int32_t>(x, x->idx_save), dres, gf(x, pl.wte), gf(x, pl.wpe), M, T, C, c.vocab,
                                   at<int32_t>(x, ap.enc_count), at<int32_t>(x, ap.enc_start),
@@ -585,6 +584,9 @@ int gpt2_backward(gpt2_ctx* x, float loss_scale, int32_t zero_grads) {
                                   acc, s));
     // LayerNorm and bias parameter gradients: every column sum of the pass
     G2_T("colsum", run_colsum_jobs(x, acc, s));
+    // the pass ends when every weight gradient has (the second stream runs them
+    // in order, the qkv one of layer 0 last)
+    G2_TRY(join(slot(0, W_QKV)));
     return GPT2_OK;
 }
 
