@@ -17,13 +17,14 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "liboracle.so")
 
 KIND_NAMES = ["wte", "wpe", "ln1_g", "ln1_b", "w_qkv", "b_qkv", "w_proj", "b_proj",
-              "ln2_g", "ln2_b", "w_fc", "b_fc", "w_fc2", "b_fc2", "lnf_g", "lnf_b"]
+              "ln2_g", "ln2_b", "w_fc", "b_fc", "w_fc2", "b_fc2", "lnf_g", "lnf_b", "lm_head"]
+GELU_ERF, UNTIED = 1, 2  # variant bits: exact erf GELU, separate lm_head
 
 
 class OracleCfg(ct.Structure):
     _fields_ = [("vocab", ct.c_int32), ("block_size", ct.c_int32), ("n_embd", ct.c_int32),
                 ("n_head", ct.c_int32), ("n_layer", ct.c_int32), ("mlp_hidden", ct.c_int32),
-                ("bias", ct.c_int32), ("_pad", ct.c_int32), ("ln_eps", ct.c_double)]
+                ("bias", ct.c_int32), ("variant", ct.c_int32), ("ln_eps", ct.c_double)]
 
 
 _lib = None
@@ -50,7 +51,7 @@ def lib():
             getattr(L, f"oracle_layernorm_bwd_{suf}").argtypes = [i64, ct.c_int, P, P, P, P, P, P, P, P]
             getattr(L, f"oracle_linear_{suf}").argtypes = [i64, ct.c_int, ct.c_int, P, P, P, P]
             getattr(L, f"oracle_linear_bwd_{suf}").argtypes = [i64, ct.c_int, ct.c_int, P, P, P, P, P, P]
-            getattr(L, f"oracle_gelu_{suf}").argtypes = [i64, P, P, P]
+            getattr(L, f"oracle_gelu_{suf}").argtypes = [i64, P, P, P, ct.c_int]
             getattr(L, f"oracle_head_attention_{suf}").argtypes = [ct.c_int, ct.c_int, P, P, P, P, P]
             getattr(L, f"oracle_attention_{suf}").argtypes = [ct.c_int] * 4 + [P, P]
             getattr(L, f"oracle_attention_bwd_{suf}").argtypes = [ct.c_int] * 4 + [P, P, P]
@@ -82,8 +83,10 @@ def _dt(dtype):
     raise TypeError(dtype)
 
 
-def make_cfg(vocab, block_size, n_embd, n_head, n_layer, mlp_hidden, bias, ln_eps=1e-5):
-    return OracleCfg(vocab, block_size, n_embd, n_head, n_layer, mlp_hidden, int(bias), 0, ln_eps)
+def make_cfg(vocab, block_size, n_embd, n_head, n_layer, mlp_hidden, bias, ln_eps=1e-5, gelu_erf=False,
+             untied=False):
+    variant = (GELU_ERF if gelu_erf else 0) | (UNTIED if untied else 0)
+    return OracleCfg(vocab, block_size, n_embd, n_head, n_layer, mlp_hidden, int(bias), variant, ln_eps)
 
 
 def set_threads(n: int) -> None:
@@ -196,11 +199,12 @@ def linear_bwd(dY, X, W, with_bias=True):
     return dX, dW, db
 
 
-def gelu(u):
+def gelu(u, erf_form=False):
+    """GELU and its derivative: the tanh approximation, or the exact erf form."""
     u = np.ascontiguousarray(u)
     y = np.empty_like(u)
     dy = np.empty_like(u)
-    getattr(lib(), f"oracle_gelu_{_dt(u.dtype)}")(u.size, _p(u), _p(y), _p(dy))
+    getattr(lib(), f"oracle_gelu_{_dt(u.dtype)}")(u.size, _p(u), _p(y), _p(dy), int(bool(erf_form)))
     return y, dy
 
 

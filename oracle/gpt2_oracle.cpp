@@ -39,24 +39,29 @@ typedef struct {
     int32_t n_layer;     // L
     int32_t mlp_hidden;  // F (4C in every config on the pages)
     int32_t bias;        // 1: Linear layers carry biases
-    int32_t _pad;
+    int32_t variant;     // bit 0: exact erf GELU; bit 1: untied lm_head (ORACLE_* below)
     double ln_eps;       // LayerNorm epsilon
 } oracle_cfg;
 }
+
+// The minigpt page's literal model differs from the GPT-2 readings in two ways
+// the oracle can follow on request: nn.GELU() with its default exact erf form,
+// and an lm_head Linear of its own instead of the tied embedding.
+enum { ORACLE_GELU_ERF = 1, ORACLE_UNTIED = 2 };
 
 namespace {
 
 // Tensor kinds of the oracle's own canonical layout.
 enum Kind {
     K_WTE = 0, K_WPE, K_LN1_G, K_LN1_B, K_W_QKV, K_B_QKV, K_W_PROJ, K_B_PROJ,
-    K_LN2_G, K_LN2_B, K_W_FC, K_B_FC, K_W_FC2, K_B_FC2, K_LNF_G, K_LNF_B
+    K_LN2_G, K_LN2_B, K_W_FC, K_B_FC, K_W_FC2, K_B_FC2, K_LNF_G, K_LNF_B, K_LM_HEAD
 };
 
 struct LayerOff {
     size_t ln1_g, ln1_b, w_qkv, b_qkv, w_proj, b_proj, ln2_g, ln2_b, w_fc, b_fc, w_fc2, b_fc2;
 };
 struct Layout {
-    size_t wte, wpe, lnf_g, lnf_b, total;
+    size_t wte, wpe, lnf_g, lnf_b, lm_head, total;
     std::vector<LayerOff> layer;
 };
 static const size_t NONE = (size_t)-1;
@@ -65,7 +70,9 @@ static const size_t NONE = (size_t)-1;
 // registers them (token embedding, position embedding, blocks, ln_f), with the
 // three per-head Q/K/V Linears of a block fused into one [3C, C] matrix whose
 // rows are [Q heads 0..H-1 | K heads | V heads] (the fused QKV concatenation
-// the karpathy page asks about). The head is tied to wte and has no tensor.
+// the karpathy page asks about). The head is tied to wte and has no tensor of
+// its own, unless the untied variant asks for minigpt's separate lm_head [V, C]
+// (registered last, after ln_f, as in minigpt.py).
 static Layout make_layout(const oracle_cfg& c) {
     Layout lo;
     size_t o = 0;
@@ -84,13 +91,15 @@ static Layout make_layout(const oracle_cfg& c) {
         lo.layer.push_back(L);
     }
     lo.lnf_g = take(C); lo.lnf_b = take(C);
+    lo.lm_head = (c.variant & ORACLE_UNTIED) ? take(V * C) : lo.wte;
     lo.total = o;
     return lo;
 }
 
 static bool cfg_ok(const oracle_cfg& c) {
     return c.vocab > 0 && c.block_size > 0 && c.n_embd > 0 && c.n_head > 0 &&
-           c.n_layer >= 0 && c.mlp_hidden > 0 && c.n_embd % c.n_head == 0;
+           c.n_layer >= 0 && c.mlp_hidden > 0 && c.n_embd % c.n_head == 0 &&
+           (c.variant & ~(ORACLE_GELU_ERF | ORACLE_UNTIED)) == 0;
 }
 
 // ---------------------------------------------------------------- LayerNorm
@@ -207,14 +216,23 @@ void linear_bwd(int64_t M, int N, int K, const R* dY, const R* X, const R* W,
 // ---------------------------------------------------------------- GELU
 // The tanh approximation of GELU that the karpathy page says GPT-2 uses
 // (Hendrycks & Gimpel): 0.5 u (1 + tanh(sqrt(2/pi) (u + 0.044715 u^3))).
+// With erf_form, the exact definition nn.GELU() computes by default in
+// minigpt.py: u Phi(u) = 0.5 u (1 + erf(u / sqrt 2)), whose derivative is
+// Phi(u) + u phi(u) with phi the standard normal density.
 template <class R>
-R gelu(R u) {
+R gelu(R u, bool erf_form = false) {
+    if (erf_form) return (R)0.5 * u * ((R)1 + std::erf(u * (R)0.7071067811865476));
     const R k0 = (R)0.7978845608028654;  // sqrt(2/pi)
     const R k1 = (R)0.044715;
     return (R)0.5 * u * ((R)1 + std::tanh(k0 * (u + k1 * u * u * u)));
 }
 template <class R>
-R gelu_grad(R u) {
+R gelu_grad(R u, bool erf_form = false) {
+    if (erf_form) {
+        const R Phi = (R)0.5 * ((R)1 + std::erf(u * (R)0.7071067811865476));
+        const R phi = (R)0.3989422804014327 * std::exp((R)-0.5 * u * u);  // 1/sqrt(2 pi)
+        return Phi + u * phi;
+    }
     const R k0 = (R)0.7978845608028654;
     const R k1 = (R)0.044715;
     R w = k0 * (u + k1 * u * u * u);
@@ -374,6 +392,7 @@ double model_step(const oracle_cfg& cf, int B, int T, const R* p, const int32_t*
     const int C = cf.n_embd, H = cf.n_head, F = cf.mlp_hidden, V = cf.vocab, L = cf.n_layer;
     const int64_t M = (int64_t)B * T;
     const size_t MC = (size_t)M * C;
+    const bool erf_gelu = (cf.variant & ORACLE_GELU_ERF) != 0;
     Acts<R> a;
     auto vec = [](size_t n) { return std::vector<R>(n); };
 
@@ -407,7 +426,7 @@ double model_step(const oracle_cfg& cf, int B, int T, const R* p, const int32_t*
         linear_fwd<R>(M, F, C, h2.data(), p + W.w_fc, W.b_fc == NONE ? nullptr : p + W.b_fc, u.data());
         auto gg = vec((size_t)M * F);
 #pragma omp parallel for schedule(static)
-        for (int64_t i = 0; i < M * F; ++i) gg[i] = gelu<R>(u[i]);
+        for (int64_t i = 0; i < M * F; ++i) gg[i] = gelu<R>(u[i], erf_gelu);
         auto mo = vec(MC);
         linear_fwd<R>(M, C, F, gg.data(), p + W.w_fc2, W.b_fc2 == NONE ? nullptr : p + W.b_fc2, mo.data());
         for (size_t i = 0; i < MC; ++i) x[i] += mo[i];
@@ -418,12 +437,13 @@ double model_step(const oracle_cfg& cf, int B, int T, const R* p, const int32_t*
             a.u.push_back(std::move(u)); a.g.push_back(std::move(gg));
         }
     }
-    // 3) final LayerNorm and the tied head: logits = ln_f(x) . wte^T
+    // 3) final LayerNorm and the head: logits = ln_f(x) . lm_head^T (lm_head is
+    //    wte itself when tied)
     a.xL = x;
     a.lnf = vec(MC); a.mf = vec(M); a.rf = vec(M);
     layernorm_fwd<R>(M, C, x.data(), p + lo.lnf_g, p + lo.lnf_b, cf.ln_eps, a.lnf.data(), a.mf.data(), a.rf.data());
     a.logits = vec((size_t)M * V);
-    linear_fwd<R>(M, V, C, a.lnf.data(), p + lo.wte, nullptr, a.logits.data());
+    linear_fwd<R>(M, V, C, a.lnf.data(), p + lo.lm_head, nullptr, a.logits.data());
     if (logits_out) std::memcpy(logits_out, a.logits.data(), sizeof(R) * (size_t)M * V);
     if (!tgt) return NAN;
 
@@ -442,7 +462,7 @@ double model_step(const oracle_cfg& cf, int B, int T, const R* p, const int32_t*
     // 5) backward, layer by layer in reverse
     R* gp = grads;
     auto dxf = vec(MC);
-    linear_bwd<R>(M, V, C, dz.data(), a.lnf.data(), p + lo.wte, dxf.data(), gp + lo.wte, nullptr);
+    linear_bwd<R>(M, V, C, dz.data(), a.lnf.data(), p + lo.lm_head, dxf.data(), gp + lo.lm_head, nullptr);
     dz.clear(); dz.shrink_to_fit();
     std::vector<R> dx(MC, (R)0);  // gradient of the residual stream
     layernorm_bwd<R>(M, C, dxf.data(), a.xL.data(), a.mf.data(), a.rf.data(), p + lo.lnf_g, dx.data(),
@@ -455,7 +475,7 @@ double model_step(const oracle_cfg& cf, int B, int T, const R* p, const int32_t*
                       W.b_fc2 == NONE ? nullptr : gp + W.b_fc2);
         auto& u = a.u[l];
 #pragma omp parallel for schedule(static)
-        for (int64_t i = 0; i < M * F; ++i) dg[i] *= gelu_grad<R>(u[i]);
+        for (int64_t i = 0; i < M * F; ++i) dg[i] *= gelu_grad<R>(u[i], erf_gelu);
         auto dh2 = vec(MC);
         linear_bwd<R>(M, F, C, dg.data(), a.ln2[l].data(), p + W.w_fc, dh2.data(), gp + W.w_fc,
                       W.b_fc == NONE ? nullptr : gp + W.b_fc);
@@ -529,7 +549,7 @@ extern "C" {
 void oracle_set_threads(int n) { if (n > 0) omp_set_num_threads(n); }
 int oracle_max_threads(void) { return omp_get_max_threads(); }
 
-// Number of parameters of the oracle's compact layout (tied head counted once).
+// Number of parameters of the oracle's compact layout (a tied head counted once).
 int64_t oracle_n_params(const oracle_cfg* c) {
     if (!c || !cfg_ok(*c)) return -1;
     return (int64_t)make_layout(*c).total;
@@ -559,6 +579,7 @@ int oracle_param_table(const oracle_cfg* c, int64_t* out, int cap) {
         put(K_W_FC2, l, L.w_fc2, C, F); put(K_B_FC2, l, L.b_fc2, 1, C);
     }
     put(K_LNF_G, -1, lo.lnf_g, 1, C); put(K_LNF_B, -1, lo.lnf_b, 1, C);
+    if (c->variant & ORACLE_UNTIED) put(K_LM_HEAD, -1, lo.lm_head, V, C);
     return n;
 }
 
@@ -592,10 +613,10 @@ ORACLE_STEP(f64, double)
                                  R* dX, R* dW, R* db) {                                            \
         linear_bwd<R>(M, N, K, dY, X, W, dX, dW, db);                                              \
     }                                                                                              \
-    void oracle_gelu_##SUF(int64_t n, const R* u, R* y, R* dy) {                                   \
+    void oracle_gelu_##SUF(int64_t n, const R* u, R* y, R* dy, int erf_form) {                     \
         for (int64_t i = 0; i < n; ++i) {                                                          \
-            if (y) y[i] = gelu<R>(u[i]);                                                           \
-            if (dy) dy[i] = gelu_grad<R>(u[i]);                                                    \
+            if (y) y[i] = gelu<R>(u[i], erf_form != 0);                                            \
+            if (dy) dy[i] = gelu_grad<R>(u[i], erf_form != 0);                                     \
         }                                                                                          \
     }                                                                                              \
     void oracle_head_attention_##SUF(int T, int d, const R* q, const R* k, const R* v, R* out,     \

@@ -13,6 +13,8 @@ OpenWebText / Shakespeare, which are not available):
   gpt2_124m  V50257 T1024 C768 H12 L12 F3072, bias, B12, Zipf s=1.05,     bf16
   gpt2_124m_accum  as gpt2_124m, 40 micro-batches per optimiser step
   gpt2_124m_eval   as gpt2_124m, B64, forward + loss only
+  tiny_f32_literal, char_bf16_literal  as tiny_f32 / char_bf16 with the minigpt
+                   page's literal model: exact-erf GELU and an lm_head of its own
 """
 from __future__ import annotations
 
@@ -32,6 +34,8 @@ class Model:
     mlp_hidden: int
     bias: bool
     ln_eps: float = 1e-5
+    gelu_erf: bool = False  # exact erf GELU (nn.GELU() default) instead of the tanh form
+    untied: bool = False    # separate lm_head [V, C] instead of the head tied to wte
 
 
 @dataclasses.dataclass(frozen=True)
@@ -66,6 +70,11 @@ WORKLOADS = {
                                 accum=40, clip=1.0, cosine=True),
     "gpt2_124m_eval": Workload("gpt2_124m_eval", GPT2_124M, 64, 1024, "bf16", "zipf", zipf_s=1.05,
                                train=False),
+    "tiny_f32_literal": Workload("tiny_f32_literal", Model(65, 64, 128, 4, 4, 512, False, gelu_erf=True, untied=True),
+                                 4, 64, "f32", "uniform"),
+    "char_bf16_literal": Workload("char_bf16_literal",
+                                  Model(65, 256, 384, 6, 6, 1536, False, gelu_erf=True, untied=True), 64, 256,
+                                  "bf16", "zipf", zipf_s=1.1, steps=10),
 }
 
 PARAM_SEED = 1234
@@ -73,7 +82,8 @@ DATA_SEED = 5678
 
 
 def tensor_shapes(m: Model):
-    """Named parameter tensors in module order, with shapes (head tied to wte)."""
+    """Named parameter tensors in module order, with shapes (the head is tied to
+    wte unless the model is untied, then lm_head comes last, after ln_f)."""
     C, F = m.n_embd, m.mlp_hidden
     out = [("wte", (m.vocab, C)), ("wpe", (m.block_size, C))]
     for l in range(m.n_layer):
@@ -91,6 +101,8 @@ def tensor_shapes(m: Model):
         if m.bias:
             out.append((p + "b_fc2", (C,)))
     out += [("lnf_g", (C,)), ("lnf_b", (C,))]
+    if m.untied:
+        out.append(("lm_head", (m.vocab, C)))
     return out
 
 

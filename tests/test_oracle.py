@@ -3,7 +3,8 @@
 - whole-model gradients against central finite differences (double);
 - the whole model against an independent torch-CPU autograd model built from
   library primitives (F.layer_norm, F.linear, scaled_dot_product_attention,
-  F.gelu(approximate="tanh"), F.cross_entropy) in float64;
+  F.gelu(approximate="tanh"), F.cross_entropy) in float64, also for the minigpt
+  page's literal variants (exact erf GELU, a separate lm_head);
 - closed forms and invariants: initial loss ~ ln V, LayerNorm moments, softmax
   rows, the causal mask, the worked softmax example printed on the minigpt page,
   GELU identities, AdamW's first step, the LR schedule, clipping, parameter counts.
@@ -20,7 +21,8 @@ GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
 
 def ocfg(o, m: syn.Model):
-    return o.make_cfg(m.vocab, m.block_size, m.n_embd, m.n_head, m.n_layer, m.mlp_hidden, m.bias, m.ln_eps)
+    return o.make_cfg(m.vocab, m.block_size, m.n_embd, m.n_head, m.n_layer, m.mlp_hidden, m.bias, m.ln_eps,
+                      gelu_erf=m.gelu_erf, untied=m.untied)
 
 
 def rand_named(m: syn.Model, seed, std=0.3):
@@ -38,6 +40,9 @@ def rand_named(m: syn.Model, seed, std=0.3):
 
 TINY = syn.Model(vocab=11, block_size=8, n_embd=16, n_head=2, n_layer=2, mlp_hidden=64, bias=True)
 TINY_NB = syn.Model(vocab=11, block_size=8, n_embd=16, n_head=2, n_layer=2, mlp_hidden=64, bias=False)
+# the minigpt page's literal model: exact erf GELU, lm_head of its own
+TINY_LIT = syn.Model(vocab=11, block_size=8, n_embd=16, n_head=2, n_layer=2, mlp_hidden=64, bias=True,
+                     gelu_erf=True, untied=True)
 
 
 def tiny_batch(m, B, T, seed):
@@ -48,7 +53,7 @@ def tiny_batch(m, B, T, seed):
 
 
 # ----------------------------------------------------------------- finite differences
-@pytest.mark.parametrize("model", [TINY, TINY_NB], ids=["bias", "nobias"])
+@pytest.mark.parametrize("model", [TINY, TINY_NB, TINY_LIT], ids=["bias", "nobias", "erf_untied"])
 def test_gradients_match_finite_differences(oracle, model):
     cfg = ocfg(oracle, model)
     B, T = 2, 8
@@ -117,16 +122,18 @@ def torch_model_loss(named, m: syn.Model, x, y, scale=1.0):
         att = att.transpose(1, 2).reshape(B, T, C)
         h = h + F.linear(att, q("w_proj"), q("b_proj"))
         a2 = F.layer_norm(h, (C,), q("ln2_g"), q("ln2_b"), eps=m.ln_eps)
-        h = h + F.linear(F.gelu(F.linear(a2, q("w_fc"), q("b_fc")), approximate="tanh"), q("w_fc2"), q("b_fc2"))
+        gelu = F.gelu(F.linear(a2, q("w_fc"), q("b_fc")), approximate="none" if m.gelu_erf else "tanh")
+        h = h + F.linear(gelu, q("w_fc2"), q("b_fc2"))
     hf = F.layer_norm(h, (C,), P["lnf_g"], P["lnf_b"], eps=m.ln_eps)
-    logits = hf @ P["wte"].T
+    logits = hf @ (P["lm_head"] if m.untied else P["wte"]).T
     loss = F.cross_entropy(logits.view(-1, m.vocab), torch.tensor(y, dtype=torch.long).view(-1))
     (loss * scale).backward()
     return float(loss.detach()), {k: v.grad.numpy() for k, v in P.items()}
 
 
-@pytest.mark.parametrize("model", [TINY, TINY_NB, syn.Model(13, 16, 24, 3, 3, 96, True)],
-                         ids=["bias", "nobias", "h3"])
+@pytest.mark.parametrize("model", [TINY, TINY_NB, syn.Model(13, 16, 24, 3, 3, 96, True), TINY_LIT,
+                                   syn.Model(13, 16, 24, 3, 3, 96, False, untied=True)],
+                         ids=["bias", "nobias", "h3", "erf_untied", "untied_tanh"])
 def test_oracle_matches_independent_torch_model(oracle, model):
     cfg = ocfg(oracle, model)
     B, T = 3, model.block_size
@@ -342,6 +349,30 @@ def test_gelu_identities(oracle):
     np.testing.assert_allclose(dy, (yp - ym) / (2 * h), atol=1e-8)
 
 
+def test_erf_gelu_identities(oracle):
+    from scipy.stats import norm
+    u = np.linspace(-8, 8, 4001)
+    y, dy = oracle.gelu(u, erf_form=True)
+    assert y[2000] == 0.0                                       # GELU(0) = 0
+    np.testing.assert_allclose(y - y[::-1], u, atol=1e-14)      # Phi(u) + Phi(-u) = 1
+    np.testing.assert_allclose(y, u * norm.cdf(u), rtol=1e-13, atol=1e-15)  # u Phi(u), Phi from scipy
+    np.testing.assert_allclose(dy, norm.cdf(u) + u * norm.pdf(u), rtol=1e-12, atol=1e-15)
+    h = 1e-6
+    yp, _ = oracle.gelu(u + h, erf_form=True)
+    ym, _ = oracle.gelu(u - h, erf_form=True)
+    np.testing.assert_allclose(dy, (yp - ym) / (2 * h), atol=1e-8)
+    t, _ = oracle.gelu(u)                                       # the tanh form stays within 5e-4 of it
+    assert 0 < np.max(np.abs(t - y)) < 5e-4
+
+
+def test_erf_gelu_matches_torch_exact_gelu(oracle):
+    import torch
+    u = np.linspace(-10, 10, 2001)
+    y, _ = oracle.gelu(u, erf_form=True)
+    ref = torch.nn.functional.gelu(torch.tensor(u), approximate="none").numpy()
+    np.testing.assert_allclose(y, ref, rtol=1e-14, atol=1e-15)
+
+
 def test_gelu_matches_torch_tanh_gelu(oracle):
     import torch
     u = np.linspace(-10, 10, 2001)
@@ -446,7 +477,7 @@ def read_counts():
     return out
 
 
-@pytest.mark.parametrize("wname", ["tiny_f32", "char_bf16", "gpt2_124m"])
+@pytest.mark.parametrize("wname", ["tiny_f32", "char_bf16", "gpt2_124m", "tiny_f32_literal"])
 def test_param_counts(oracle, wname):
     import torch.nn as nn
     counts = read_counts()
@@ -459,6 +490,8 @@ def test_param_counts(oracle, wname):
         mods += [nn.LayerNorm(m.n_embd), nn.LayerNorm(m.n_embd),
                  nn.Linear(m.n_embd, 3 * m.n_embd, bias=m.bias), nn.Linear(m.n_embd, m.n_embd, bias=m.bias),
                  nn.Linear(m.n_embd, m.mlp_hidden, bias=m.bias), nn.Linear(m.mlp_hidden, m.n_embd, bias=m.bias)]
+    if m.untied:
+        mods.append(nn.Linear(m.n_embd, m.vocab, bias=False))
     assert n == sum(p.numel() for mod in mods for p in mod.parameters())
     if wname == "gpt2_124m":
         assert abs(n - counts["page_approx_124m"]) / counts["page_approx_124m"] < 0.005
