@@ -31,7 +31,7 @@ EXPORTS = [
 class Config(ct.Structure):
     _fields_ = [("vocab", ct.c_int32), ("block_size", ct.c_int32), ("n_embd", ct.c_int32), ("n_head", ct.c_int32),
                 ("n_layer", ct.c_int32), ("mlp_hidden", ct.c_int32), ("bias", ct.c_int32), ("dtype", ct.c_int32),
-                ("ln_eps", ct.c_float)]
+                ("ln_eps", ct.c_float), ("gelu_erf", ct.c_int32), ("untied_head", ct.c_int32)]
 
 
 class TensorDesc(ct.Structure):
@@ -106,8 +106,10 @@ def check(code: int, what: str) -> int:
     return code
 
 
-def make_config(vocab, block_size, n_embd, n_head, n_layer, mlp_hidden, bias, dtype, ln_eps=1e-5) -> Config:
-    return Config(vocab, block_size, n_embd, n_head, n_layer, mlp_hidden, int(bias), int(dtype), ln_eps)
+def make_config(vocab, block_size, n_embd, n_head, n_layer, mlp_hidden, bias, dtype, ln_eps=1e-5, gelu_erf=False,
+                untied_head=False) -> Config:
+    return Config(vocab, block_size, n_embd, n_head, n_layer, mlp_hidden, int(bias), int(dtype), ln_eps,
+                  int(bool(gelu_erf)), int(bool(untied_head)))
 
 
 def query_sizes(cfg: Config, B: int, T: int, mode: int):

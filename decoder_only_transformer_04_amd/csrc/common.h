@@ -34,6 +34,7 @@ struct LayerW {
 
 struct ParamLayout {
     int64_t wte, wpe, lnf_g, lnf_b;
+    int64_t lm_head;  // the head's weight: wte's offset when tied
     std::vector<LayerW> layer;
     std::vector<TensorDesc> tensors;
     int64_t n_flat;   // total elements incl. padding (multiple of kParamAlign)
@@ -110,6 +111,7 @@ struct GemmArgs {
     void* C2; int64_t ldc2;
     const void* R; int64_t ldr;
     int accumulate;
+    int gelu_erf;  // EPI_GELU: exact erf form instead of the tanh approximation
     void* split_buf; size_t split_bytes;  // fp32 scratch for split-K partials (nullable)
     // EPI_GELU_BWD only (nullable): column sums of the output over each 64-row
     // block, written to colsum_part[(m / 64) * N + n] (the bias gradient's partials)

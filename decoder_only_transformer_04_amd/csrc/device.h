@@ -64,6 +64,14 @@ __device__ __forceinline__ void gelu_tanh_and_grad(float u, float& g, float& dg)
     dg = sg + 2.0f * u * sg * (1.0f - sg) * k0 * (1.0f + 3.0f * k1 * u * u);
 }
 
+// The exact GELU u Phi(u), Phi(u) = 0.5 (1 + erf(u / sqrt 2)), and its derivative
+// Phi(u) + u phi(u) with phi(u) = exp(-u^2 / 2) / sqrt(2 pi).
+__device__ __forceinline__ void gelu_erf_and_grad(float u, float& g, float& dg) {
+    const float Phi = 0.5f * (1.0f + erff(u * 0.70710678118654752f));
+    g = u * Phi;
+    dg = Phi + u * 0.39894228040143268f * __expf(-0.5f * u * u);
+}
+
 // Two gfx950 LDS transpose loads (ds_read_b64_tr_b16) 'gap' bytes apart, packed
 // into one 8 x bf16 MFMA operand. In each 16-lane group, lane j addresses row
 // j/4 and 4 consecutive 16-bit columns 4(j%4)..; lane i of the group receives

@@ -45,6 +45,7 @@ struct GP {
     const void* R;
     int64_t ldr;
     int accumulate;
+    int gelu_erf;  // EPI_GELU: exact erf form
     float* cpart;  // GELU_BWD: per-64-row column sums of the output (nullable)
 };
 
@@ -56,7 +57,8 @@ __device__ __forceinline__ void epi_apply(const GP& p, int64_t m, int n, float v
         Act<T>::st((T*)p.C, m * p.ldc + n, p.alpha * v + bias);
     } else if constexpr (EPI == EPI_GELU) {
         float g, dg;
-        gelu_tanh_and_grad(v + bias, g, dg);
+        if (p.gelu_erf) gelu_erf_and_grad(v + bias, g, dg);
+        else gelu_tanh_and_grad(v + bias, g, dg);
         Act<T>::st((T*)p.C, m * p.ldc + n, dg);
         Act<T>::st((T*)p.C2, m * p.ldc2 + n, g);
     } else if constexpr (EPI == EPI_RESID) {
@@ -113,8 +115,13 @@ __device__ __forceinline__ void epi_apply8(const GP& p, int64_t m, int n, const 
         *(uint4*)((bf16_t*)p.C + m * p.ldc + n) = pack8(o);
     } else if constexpr (EPI == EPI_GELU) {
         float gl[8];
+        if (p.gelu_erf) {
 #pragma unroll
-        for (int k = 0; k < 8; ++k) gelu_tanh_and_grad(v[k] + bv[k], gl[k], o[k]);
+            for (int k = 0; k < 8; ++k) gelu_erf_and_grad(v[k] + bv[k], gl[k], o[k]);
+        } else {
+#pragma unroll
+            for (int k = 0; k < 8; ++k) gelu_tanh_and_grad(v[k] + bv[k], gl[k], o[k]);
+        }
         *(uint4*)((bf16_t*)p.C + m * p.ldc + n) = pack8(o);
         *(uint4*)((bf16_t*)p.C2 + m * p.ldc2 + n) = pack8(gl);
     } else if constexpr (EPI == EPI_RESID) {
@@ -875,6 +882,7 @@ hipError_t gemm(int dtype, const GemmArgs& a, hipStream_t s) {
     p.C = a.C; p.ldc = a.ldc; p.c_split_stride = 0;
     p.C2 = a.C2; p.ldc2 = a.ldc2; p.R = a.R; p.ldr = a.ldr;
     p.accumulate = a.accumulate;
+    p.gelu_erf = a.gelu_erf;
     p.cpart = a.epi == EPI_GELU_BWD ? a.colsum_part : nullptr;
     if (a.M <= 0 || a.N <= 0) return hipSuccess;
     if (a.K <= 0) {

@@ -212,6 +212,7 @@ hipError_t linear_fwd(gpt2_ctx* x, int epi, int64_t M, int N, int K, const void*
     a.C = Y; a.ldc = (epi == EPI_RESID || epi == EPI_F32) ? N : N;
     a.C2 = Y2; a.ldc2 = N;
     a.R = R; a.ldr = N;
+    a.gelu_erf = x->cfg.gelu_erf;
     return gemm(x->cfg.dtype, a, x->stream);
 }
 
@@ -428,8 +429,8 @@ int gpt2_forward(gpt2_ctx* x, const int32_t* d_idx, const int32_t* d_targets, fl
     }
     G2_T("ln.fwd", layernorm_fwd(dt, at<float>(x, ap.xL), pf(x, x->pl.lnf_g), pf(x, x->pl.lnf_b), c.ln_eps,
                          at<char>(x, ap.xf), at<float>(x, ap.mf), at<float>(x, ap.rf), M, C, s));
-    // tied head over the padded vocabulary (padded rows of wte are zero)
-    G2_T("gemm.fwd.head", linear_fwd(x, EPI_STORE, M, Vp, C, at<char>(x, ap.xf), wptr(x, x->pl.wte), nullptr, at<char>(x, ap.logits),
+    // head (wte itself when tied) over the padded vocabulary (padded rows are zero)
+    G2_T("gemm.fwd.head", linear_fwd(x, EPI_STORE, M, Vp, C, at<char>(x, ap.xf), wptr(x, x->pl.lm_head), nullptr, at<char>(x, ap.logits),
                       nullptr, nullptr));
     if (d_targets || d_argmax) {
         const bool grad = train && d_targets;
@@ -493,10 +494,11 @@ int gpt2_backward(gpt2_ctx* x, float loss_scale, int32_t zero_grads) {
     enum { W_FC2 = 0, W_FC = 1, W_PROJ = 2, W_QKV = 3 };
     const int slot_head = 4 * c.n_layer;
 
-    // head: dxf = alpha dz . wte ; dwte (=|+=) alpha dz^T . xf
-    G2_T("gemm.dgrad.head", linear_dgrad(dt, s, EPI_F32, M, Vp, C, at<char>(x, ap.logits), Vp, wptr(x, pl.wte), dtmp, nullptr, alpha));
+    // head: dxf = alpha dz . W_head ; dW_head (=|+=) alpha dz^T . xf, W_head = wte when tied
+    G2_T("gemm.dgrad.head", linear_dgrad(dt, s, EPI_F32, M, Vp, C, at<char>(x, ap.logits), Vp, wptr(x, pl.lm_head), dtmp, nullptr,
+                            alpha));
     G2_TRY(fork(slot_head));
-    G2_TS("gemm.wgrad.head", ws, linear_wgrad(dt, ws, M, Vp, C, at<char>(x, ap.logits), Vp, at<char>(x, ap.xf), gf(x, pl.wte), acc,
+    G2_TS("gemm.wgrad.head", ws, linear_wgrad(dt, ws, M, Vp, C, at<char>(x, ap.logits), Vp, at<char>(x, ap.xf), gf(x, pl.lm_head), acc,
                                           alpha, sb, sbytes));
     G2_TRY(mark(slot_head));
     // Each LayerNorm backward also sums the columns of the residual gradient it
@@ -574,8 +576,10 @@ int gpt2_backward(gpt2_ctx* x, float loss_scale, int32_t zero_grads) {
                              pf(x, w.ln1_g), dres, bf ? dres_a : nullptr, at<float>(x, ap.ln_part[2 + 2 * k]),
                              ap.ln_part_rows, M, C, 1, b_fc2_below != nullptr, s));
     }
-    // the embedding backward adds into dwte after the head's weight gradient
+    // the embedding backward adds into dwte after the head's weight gradient;
+    // untied, nothing else writes dwte, so an overwriting pass clears it first
     G2_TRY(join(slot_head));
+    if (c.untied_head && !acc) G2_TRY(fill_zero(gf(x, pl.wte), (size_t)pl.vocab_pad * C * 4, s));
     // embedding: dwte[idx[m]] += dres[m] (after the head's contribution), dwpe[t] (=|+=) sum_b dres[b,t]
     G2_T("embed.bwd", encoder_bwd(at<int32_t>(x, x->idx_save), dres, gf(x, pl.wte), gf(x, pl.wpe), M, T, C, c.vocab,
                                   at<int32_t>(x, ap.enc_count), at<int32_t>(x, ap.enc_start),

@@ -19,6 +19,7 @@ int validate_config(const gpt2_config* c) {
     if (c->bias != 0 && c->bias != 1) return GPT2_EINVAL;
     if (c->dtype != GPT2_DTYPE_F32 && c->dtype != GPT2_DTYPE_BF16) return GPT2_EINVAL;
     if (!(c->ln_eps > 0.0f) || !std::isfinite(c->ln_eps)) return GPT2_EINVAL;
+    if ((c->gelu_erf != 0 && c->gelu_erf != 1) || (c->untied_head != 0 && c->untied_head != 1)) return GPT2_EINVAL;
     const int d = c->n_embd / c->n_head;
     if (d > 128) return GPT2_EINVAL;
     if (c->dtype == GPT2_DTYPE_BF16) {
@@ -52,7 +53,7 @@ ParamLayout make_param_layout(const gpt2_config& c) {
         return t.offset;
     };
     // the embedding table keeps its rows padded to a multiple of kVocabPad (zero
-    // rows), so the tied head's GEMMs see whole tiles; padded logits are ignored
+    // rows), so the head's GEMMs see whole tiles; padded logits are ignored
     pl.wte = take("wte", -1, 1, V, C, pl.vocab_pad);
     pl.wpe = take("wpe", -1, 1, T, C, T);
     for (int l = 0; l < c.n_layer; ++l) {
@@ -74,6 +75,8 @@ ParamLayout make_param_layout(const gpt2_config& c) {
     }
     pl.lnf_g = take("lnf_g", -1, 0, 1, C, 1);
     pl.lnf_b = take("lnf_b", -1, 0, 1, C, 1);
+    // untied: the head's own weight, rows padded like wte's; tied: wte itself
+    pl.lm_head = c.untied_head ? take("lm_head", -1, 1, V, C, pl.vocab_pad) : pl.wte;
     pl.n_flat = off;
     pl.n_real = n_real;
     return pl;

@@ -69,6 +69,17 @@ typedef struct gpt2_config {
     int32_t bias;        /* 1: Linear layers carry biases (LM head never does) */
     int32_t dtype;       /* GPT2_DTYPE_* */
     float ln_eps;        /* LayerNorm epsilon (1e-5, the nn.LayerNorm default) */
+    /* The minigpt page's literal model (its section 二, minigpt.py) differs from the
+     * GPT-2 readings in two switches; both 0 is GPT-2:
+     * gelu_erf    1: the MLP activation is nn.GELU()'s exact form u Phi(u)
+     *                (0: the tanh approximation the karpathy page's GELU section
+     *                says GPT-2 uses);
+     * untied_head 1: the LM head has a weight of its own, tensor "lm_head" [V, C]
+     *                placed after lnf_b (minigpt's lm_head Linear, no bias); wte
+     *                then gets only the embedding's gradient
+     *                (0: the head reuses wte). Other values are GPT2_EINVAL. */
+    int32_t gelu_erf;
+    int32_t untied_head;
 } gpt2_config;
 
 /* One named parameter tensor in the flat buffers. */

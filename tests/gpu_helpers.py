@@ -49,12 +49,14 @@ def cosine(a, r) -> float:
 
 
 def ocfg(o, m: syn.Model):
-    return o.make_cfg(m.vocab, m.block_size, m.n_embd, m.n_head, m.n_layer, m.mlp_hidden, m.bias, m.ln_eps)
+    return o.make_cfg(m.vocab, m.block_size, m.n_embd, m.n_head, m.n_layer, m.mlp_hidden, m.bias, m.ln_eps,
+                      gelu_erf=m.gelu_erf, untied=m.untied)
 
 
 def gcfg(b, m: syn.Model, dtype: str):
     return b.make_config(m.vocab, m.block_size, m.n_embd, m.n_head, m.n_layer, m.mlp_hidden, m.bias,
-                         b.DTYPE_F32 if dtype == "f32" else b.DTYPE_BF16, m.ln_eps)
+                         b.DTYPE_F32 if dtype == "f32" else b.DTYPE_BF16, m.ln_eps, gelu_erf=m.gelu_erf,
+                         untied_head=m.untied)
 
 
 def gpu_model(b, m: syn.Model, dtype: str, B: int, T: int, named: dict, mode=None):

@@ -27,7 +27,8 @@ def b():
 
 def cfg_of(b, m: syn.Model, dtype):
     return b.make_config(m.vocab, m.block_size, m.n_embd, m.n_head, m.n_layer, m.mlp_hidden, m.bias,
-                         b.DTYPE_F32 if dtype == "f32" else b.DTYPE_BF16, m.ln_eps)
+                         b.DTYPE_F32 if dtype == "f32" else b.DTYPE_BF16, m.ln_eps, gelu_erf=m.gelu_erf,
+                         untied_head=m.untied)
 
 
 def header_functions():
@@ -48,7 +49,7 @@ def test_library_exports_every_header_symbol(b):
         assert hasattr(b.lib(), n)
 
 
-@pytest.mark.parametrize("wname", ["tiny_f32", "char_bf16", "gpt2_124m"])
+@pytest.mark.parametrize("wname", ["tiny_f32", "char_bf16", "gpt2_124m", "tiny_f32_literal", "char_bf16_literal"])
 def test_param_table_matches_model_shapes(b, wname):
     w = syn.WORKLOADS[wname]
     cfg = cfg_of(b, w.model, w.dtype)
@@ -101,6 +102,12 @@ def test_invalid_configs_rejected(b):
     assert b.lib().gpt2_query_sizes(ct.byref(big_head), 1, 64, 0, None, None) == b.GPT2_EINVAL
     neg_eps = b.make_config(65, 64, 128, 4, 4, 512, 0, b.DTYPE_F32, -1.0)
     assert b.lib().gpt2_query_sizes(ct.byref(neg_eps), 1, 64, 0, None, None) == b.GPT2_EINVAL
+    # the literal-model switches take 0 or 1 only
+    for kw in ({"gelu_erf": 2}, {"untied_head": -1}):
+        c = b.make_config(65, 64, 128, 4, 4, 512, 0, b.DTYPE_F32)
+        for k, v in kw.items():
+            setattr(c, k, v)
+        assert b.lib().gpt2_query_sizes(ct.byref(c), 1, 64, 0, None, None) == b.GPT2_EINVAL
     # shorter sequences than block_size are valid
     assert b.lib().gpt2_query_sizes(ct.byref(ok), 3, 37, 0, None, None) == 0
 

@@ -101,6 +101,46 @@ def test_odd_width_f32_step_matches_oracle(b, oracle):
     assert g.sync_status() == 0
 
 
+def test_literal_f32_step_matches_oracle(b, oracle):
+    """The minigpt page's literal model (exact erf GELU, lm_head of its own): one
+    fp32 step against the oracle, then a second zeroing pass on another batch,
+    whose wte gradient (the embedding's scatter only, when untied) must not keep
+    anything of the first."""
+    w = syn.WORKLOADS["tiny_f32_literal"]
+    say("tiny_f32_literal full step")
+    named = syn.init_params(w.model)
+    g = gpu_model(b, w.model, "f32", w.batch, w.seq, named)
+    for step in (0, 1):
+        x, y = syn.batch(w, step=step)
+        loss = run_fwd_bwd(g, x, y, zero=True)
+        rloss, rg = oracle_grads(oracle, w.model, named, x, y)
+        assert abs(loss - rloss) / abs(rloss) <= 1e-5, (step, loss, rloss)
+        gg = gpu_named_grads(g)
+        compare_grads(gg, rg, "f32")
+        assert np.all(gg["lm_head"] != 0) and np.max(np.abs(gg["lm_head"] - gg["wte"])) > 0
+    assert g.sync_status() == 0
+
+
+def test_literal_bf16_steps(b, oracle):
+    """The literal char-level model in bf16: three steps, loss within 2e-2 and every
+    gradient (lm_head included) at cosine >= 0.999 against the oracle evaluated at
+    the GPU's parameters."""
+    w = syn.WORKLOADS["char_bf16_literal"]
+    B, T = 4, w.seq
+    named = syn.init_params(w.model)
+    g = gpu_model(b, w.model, "bf16", B, T, named)
+    for step in range(3):
+        say(f"char_bf16_literal step {step}")
+        x, y = syn.batch(w, step=step, B=B, T=T)
+        gpn = gpu_named_params(g)
+        loss = run_fwd_bwd(g, x, y)
+        rloss, rg = oracle_grads(oracle, w.model, gpn, x, y, dtype=np.float32)
+        assert abs(loss - rloss) <= 2e-2, (step, loss, rloss)
+        compare_grads(gpu_named_grads(g), rg, "bf16")
+        g.adamw_step(w.lr, w.beta1, w.beta2, w.eps, w.weight_decay, step + 1)
+    assert g.sync_status() == 0
+
+
 def test_adamw_isolated_matches_oracle(b, oracle):
     """Identical gradients on both sides: the update, m and v agree to 1e-6."""
     import torch
