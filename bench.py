@@ -28,8 +28,11 @@ PEAK_HBM = 8.0e12      # MI355X HBM3E, bytes/s
 
 def flops_per_token(m: syn.Model, T: int) -> int:
     """6 N per trained token plus causal attention (6 L C (T+1)): the score and
-    value products, forward and backward, over the j <= i half of each row."""
-    return 6 * syn.n_params_exact(m) + 6 * m.n_layer * m.n_embd * (T + 1)
+    value products, forward and backward, over the j <= i half of each row.
+    N counts every parameter once (a tied head's products are wte's); an untied
+    model's wte is only looked up, so it is left out of N."""
+    n = syn.n_params_exact(m) - (m.vocab * m.n_embd if m.untied else 0)
+    return 6 * n + 6 * m.n_layer * m.n_embd * (T + 1)
 
 
 def kernel_work(label: str, w: syn.Workload):
@@ -116,7 +119,8 @@ def cpu_baseline(w: syn.Workload, named: dict, seq: int):
         from oracle import build
         build.build()
     m = w.model
-    cfg = o.make_cfg(m.vocab, m.block_size, m.n_embd, m.n_head, m.n_layer, m.mlp_hidden, m.bias, m.ln_eps)
+    cfg = o.make_cfg(m.vocab, m.block_size, m.n_embd, m.n_head, m.n_layer, m.mlp_hidden, m.bias, m.ln_eps,
+                     gelu_erf=m.gelu_erf, untied=m.untied)
     p = o.pack(cfg, named, np.float32)
     g = np.zeros_like(p)
     x, y = syn.batch(w, step=0, B=1, T=seq)
@@ -140,7 +144,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="gpt2_124m", choices=["gpt2_124m"])
+    ap.add_argument("--workload", default="gpt2_124m", choices=["gpt2_124m", "gpt2_124m_literal"],
+                    help="gpt2_124m_literal: the same model with exact erf GELU and an untied lm_head")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seq", type=int, default=1024, help="tokens in the oracle's timed sample")
     ap.add_argument("--no-breakdown", action="store_true", help="skip the per-kernel-class timing pass")
@@ -159,7 +164,7 @@ def main():
     w = syn.WORKLOADS[args.workload]
     m = w.model
     cfg = b.make_config(m.vocab, m.block_size, m.n_embd, m.n_head, m.n_layer, m.mlp_hidden, m.bias, b.DTYPE_BF16,
-                        m.ln_eps)
+                        m.ln_eps, gelu_erf=m.gelu_erf, untied_head=m.untied)
     named = syn.init_params(m)
     g = b.Model(cfg, w.batch, w.seq, b.MODE_TRAIN)
     g.load_named(named)
@@ -253,8 +258,10 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic (Zipf s=1.05 token ids, N(0,0.02) init, seeds 1234/5678)",
-        "config": {"workload": "gpt2_124m: V50257 T1024 C768 H12 L12 F3072, biases, tied head; "
-                               "micro-batch 12 x 1024, one fwd+bwd+AdamW per step",
+        "config": {"workload": ("gpt2_124m: V50257 T1024 C768 H12 L12 F3072, biases, tied head; "
+                                "micro-batch 12 x 1024, one fwd+bwd+AdamW per step") if not m.untied else
+                               ("gpt2_124m_literal: V50257 T1024 C768 H12 L12 F3072, biases, exact erf GELU, "
+                                "untied lm_head; micro-batch 12 x 1024, one fwd+bwd+AdamW per step"),
                    "global_batch": w.batch, "seq_len": w.seq, "parallelism": "none (1 GPU)"},
         "mfu": round(mfu, 4),
         "flops_per_token": fpt,

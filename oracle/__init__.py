@@ -148,6 +148,52 @@ def step(cfg: OracleCfg, B: int, T: int, params_flat: np.ndarray, idx: np.ndarra
     return loss, logits, rows
 
 
+# ---------------------------------------------------------------- generation
+# The generate loop of the minigpt page (section 二, MiniGPT.generate; walkthrough
+# 3.8) written out: crop the sequence to its last block_size tokens, run the whole
+# forward, take the last position's logits, divide by the temperature, softmax,
+# draw one token, append. The draw: torch.multinomial's internal procedure is not
+# on the pages, so a draw is inverse-CDF sampling with a uniform number u in [0, 1)
+# supplied by the caller (one per sequence and step): the token is the smallest k
+# whose cumulative probability, summed in index order, exceeds u.
+def next_token_probs(cfg: OracleCfg, params_flat: np.ndarray, ctx: np.ndarray, temperature: float) -> np.ndarray:
+    """[B, V] float64 probabilities of the next token after each row of ``ctx``
+    ([B, n] int32, n >= 1), with the crop to the last block_size tokens."""
+    ctx = np.asarray(ctx, dtype=np.int32)
+    B, n = ctx.shape
+    win = ctx[:, max(0, n - cfg.block_size):]
+    T = win.shape[1]
+    _, logits, _ = step(cfg, B, T, params_flat, win, None, want_logits=True)
+    z = logits.reshape(B, T, cfg.vocab)[:, -1, :].astype(np.float64) / temperature
+    z -= z.max(axis=1, keepdims=True)
+    e = np.exp(z)
+    return e / e.sum(axis=1, keepdims=True)
+
+
+def sample_inverse_cdf(probs: np.ndarray, u: np.ndarray) -> np.ndarray:
+    """Per row, the smallest k with sum_{j<=k} p_j > u (the last token with p > 0
+    if rounding leaves the total below u)."""
+    out = np.empty(probs.shape[0], dtype=np.int32)
+    for r in range(probs.shape[0]):
+        c = np.cumsum(probs[r])
+        k = int(np.searchsorted(c, u[r], side="right"))
+        if k >= probs.shape[1]:
+            k = int(np.nonzero(probs[r] > 0)[0][-1])
+        out[r] = k
+    return out
+
+
+def generate(cfg: OracleCfg, params_flat: np.ndarray, prompt: np.ndarray, n_new: int, temperature: float,
+             uniforms: np.ndarray) -> np.ndarray:
+    """[B, T0 + n_new] int32: the prompt followed by n_new drawn tokens, the i-th
+    new token of row b drawn with uniforms[b, i]."""
+    seq = np.asarray(prompt, dtype=np.int32)
+    for i in range(n_new):
+        p = next_token_probs(cfg, params_flat, seq, temperature)
+        seq = np.concatenate([seq, sample_inverse_cdf(p, uniforms[:, i])[:, None]], axis=1)
+    return seq
+
+
 # ---------------------------------------------------------------- unit functions
 def layernorm(x, g, b, eps=1e-5):
     x = np.ascontiguousarray(x)

@@ -13,8 +13,9 @@ OpenWebText / Shakespeare, which are not available):
   gpt2_124m  V50257 T1024 C768 H12 L12 F3072, bias, B12, Zipf s=1.05,     bf16
   gpt2_124m_accum  as gpt2_124m, 40 micro-batches per optimiser step
   gpt2_124m_eval   as gpt2_124m, B64, forward + loss only
-  tiny_f32_literal, char_bf16_literal  as tiny_f32 / char_bf16 with the minigpt
-                   page's literal model: exact-erf GELU and an lm_head of its own
+  tiny_f32_literal, char_bf16_literal, gpt2_124m_literal  as tiny_f32 / char_bf16 /
+                   gpt2_124m with the minigpt page's literal model: exact-erf GELU
+                   and an lm_head of its own
 """
 from __future__ import annotations
 
@@ -70,6 +71,8 @@ WORKLOADS = {
                                 accum=40, clip=1.0, cosine=True),
     "gpt2_124m_eval": Workload("gpt2_124m_eval", GPT2_124M, 64, 1024, "bf16", "zipf", zipf_s=1.05,
                                train=False),
+    "gpt2_124m_literal": Workload("gpt2_124m_literal", dataclasses.replace(GPT2_124M, gelu_erf=True, untied=True), 12,
+                                  1024, "bf16", "zipf", zipf_s=1.05),
     "tiny_f32_literal": Workload("tiny_f32_literal", Model(65, 64, 128, 4, 4, 512, False, gelu_erf=True, untied=True),
                                  4, 64, "f32", "uniform"),
     "char_bf16_literal": Workload("char_bf16_literal",

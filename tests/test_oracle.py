@@ -126,6 +126,8 @@ def torch_model_loss(named, m: syn.Model, x, y, scale=1.0):
         h = h + F.linear(gelu, q("w_fc2"), q("b_fc2"))
     hf = F.layer_norm(h, (C,), P["lnf_g"], P["lnf_b"], eps=m.ln_eps)
     logits = hf @ (P["lm_head"] if m.untied else P["wte"]).T
+    if y is None:
+        return logits.detach().numpy()
     loss = F.cross_entropy(logits.view(-1, m.vocab), torch.tensor(y, dtype=torch.long).view(-1))
     (loss * scale).backward()
     return float(loss.detach()), {k: v.grad.numpy() for k, v in P.items()}
@@ -495,6 +497,59 @@ def test_param_counts(oracle, wname):
     assert n == sum(p.numel() for mod in mods for p in mod.parameters())
     if wname == "gpt2_124m":
         assert abs(n - counts["page_approx_124m"]) / counts["page_approx_124m"] < 0.005
+
+
+# ----------------------------------------------------------------- generation
+def test_inverse_cdf_sampling_boundaries(oracle):
+    # dyadic probabilities, so the cumulative sums 0.125 | 0.375 | 0.75 | 1 are exact
+    p = np.array([[0.125, 0.25, 0.375, 0.25]] * 7)
+    u = np.array([0.0, 0.124, 0.125, 0.374, 0.375, 0.75, 0.9999])
+    # the smallest k whose cumulative probability exceeds u
+    assert list(oracle.sample_inverse_cdf(p, u)) == [0, 0, 1, 1, 2, 3, 3]
+    q = np.array([[0.0, 0.5, 0.0, 0.5]] * 3)
+    assert list(oracle.sample_inverse_cdf(q, np.array([0.0, 0.49, 0.5]))) == [1, 1, 3]  # p = 0 never drawn
+
+
+def test_inverse_cdf_sampling_frequencies(oracle):
+    from scipy.stats import chisquare
+    rng = np.random.default_rng(8)
+    p = rng.dirichlet(np.ones(12))
+    n = 60000
+    draws = oracle.sample_inverse_cdf(np.broadcast_to(p, (n, 12)), rng.random(n))
+    counts = np.bincount(draws, minlength=12)
+    assert chisquare(counts, p * n).pvalue > 1e-3
+
+
+def test_next_token_probs_match_torch_softmax_and_crop(oracle):
+    import torch
+    m = TINY
+    cfg = ocfg(oracle, m)
+    named = rand_named(m, 21)
+    p = oracle.pack(cfg, named, np.float64)
+    rng = np.random.default_rng(22)
+    ctx = rng.integers(0, m.vocab, size=(3, 5)).astype(np.int32)
+    probs = oracle.next_token_probs(cfg, p, ctx, temperature=0.7)
+    z = torch.tensor(torch_model_loss(named, m, ctx, None)[:, -1, :] / 0.7)
+    np.testing.assert_allclose(probs, torch.softmax(z, dim=-1).numpy(), rtol=1e-12, atol=1e-15)
+    np.testing.assert_allclose(probs.sum(axis=1), 1.0, rtol=1e-14)
+    # the model sees only the last block_size tokens: anything before them is cropped away
+    full = rng.integers(0, m.vocab, size=(3, m.block_size)).astype(np.int32)
+    longer = np.concatenate([rng.integers(0, m.vocab, size=(3, 4)).astype(np.int32), full], axis=1)
+    np.testing.assert_array_equal(oracle.next_token_probs(cfg, p, longer, 1.0),
+                                  oracle.next_token_probs(cfg, p, full, 1.0))
+
+
+def test_low_temperature_generation_is_greedy(oracle):
+    m = TINY
+    cfg = ocfg(oracle, m)
+    p = oracle.pack(cfg, rand_named(m, 23), np.float64)
+    prompt = np.array([[1, 2], [3, 4]], dtype=np.int32)
+    u = np.random.default_rng(24).random((2, 12))
+    seq = oracle.generate(cfg, p, prompt, 12, 1e-6, u)      # crosses block_size = 8
+    assert seq.shape == (2, 14) and np.array_equal(seq[:, :2], prompt)
+    for i in range(2, 14):
+        probs = oracle.next_token_probs(cfg, p, seq[:, :i], 1.0)
+        assert np.array_equal(seq[:, i], probs.argmax(axis=1)), i
 
 
 # ----------------------------------------------------------------- synthetic inputs
