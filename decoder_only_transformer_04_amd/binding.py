@@ -15,13 +15,13 @@ LIB_PATH = os.path.join(HERE, "libgpt2mi.so")
 
 GPT2_OK, GPT2_EINVAL, GPT2_ENOSPC, GPT2_EHIP, GPT2_EDEVICE, GPT2_ESTATE = 0, -1, -2, -3, -4, -5
 DTYPE_F32, DTYPE_BF16 = 0, 1
-MODE_TRAIN, MODE_EVAL = 0, 1
+MODE_TRAIN, MODE_EVAL, MODE_GENERATE = 0, 1, 2
 DECAY_ALL, DECAY_MATRICES = 0, 1
 STATUS_TOKEN_RANGE, STATUS_NONFINITE_LOSS, STATUS_NONFINITE_GNORM = 1, 2, 4
 
 EXPORTS = [
     "gpt2_query_sizes", "gpt2_num_params", "gpt2_param_table", "gpt2_lr_cosine", "gpt2_strerror", "gpt2_init",
-    "gpt2_refresh_weights", "gpt2_forward", "gpt2_backward", "gpt2_adamw_step", "gpt2_sync_status",
+    "gpt2_refresh_weights", "gpt2_forward", "gpt2_backward", "gpt2_adamw_step", "gpt2_generate", "gpt2_sync_status",
     "gpt2_clear_status", "gpt2_arena_tensor", "gpt2_destroy", "gpt2_op_linear_fwd", "gpt2_op_linear_bwd",
     "gpt2_op_layernorm_fwd", "gpt2_op_layernorm_bwd", "gpt2_op_attention_fwd", "gpt2_op_attention_bwd",
     "gpt2_op_cross_entropy", "gpt2_timing_begin", "gpt2_timing_end",
@@ -73,6 +73,7 @@ def lib():
             "gpt2_forward": (ct.c_int, [P, P, P, P, P]),
             "gpt2_backward": (ct.c_int, [P, f32, i32]),
             "gpt2_adamw_step": (ct.c_int, [P, f32, f32, f32, f32, f32, i32, f32, i32, P]),
+            "gpt2_generate": (ct.c_int, [P, P, i32, i32, f32, P, P]),
             "gpt2_sync_status": (ct.c_int, [P, ct.POINTER(ct.c_uint32)]),
             "gpt2_clear_status": (ct.c_int, [P]),
             "gpt2_arena_tensor": (ct.c_int, [P, ct.c_char_p, i32, sz, ct.POINTER(i32), ct.POINTER(i64),
@@ -224,6 +225,13 @@ class Model:
                    decay_mode=DECAY_ALL, want_norm=False) -> None:
         check(lib().gpt2_adamw_step(self.ctx, lr, beta1, beta2, eps, weight_decay, int(t), clip, decay_mode,
                                     _ptr(self.grad_norm) if want_norm else None), "gpt2_adamw_step")
+
+    def generate(self, prompt, n_new: int, temperature: float, uniforms, out) -> None:
+        """prompt: int32 [B, T0] (cuda); uniforms: fp32 [B, n_new] (cuda); out:
+        int32 [B, T0 + n_new] (cuda), written on the context's stream."""
+        T0 = int(prompt.shape[1])
+        check(lib().gpt2_generate(self.ctx, _ptr(prompt), T0, int(n_new), float(temperature), _ptr(uniforms),
+                                  _ptr(out)), "gpt2_generate")
 
     def sync_status(self) -> int:
         bits = ct.c_uint32()

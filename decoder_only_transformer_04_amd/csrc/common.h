@@ -60,6 +60,9 @@ struct ArenaPlan {
     // forward activations, per layer (eval mode: one slot reused)
     std::vector<Region> x, xmid, ln1, m1, r1, qkv, att, lse, ln2, m2, r2, fch, fcg;
     Region xL, xf, mf, rf, logits, loss_rows;
+    // generation: per-layer key and value caches [B, block_size, C] (activation
+    // type); logits are fp32 [B, Vp] there, for the sampler
+    std::vector<Region> kc, vc;
     // backward scratch
     // dres_act / dres_act2: activation-type copies of the residual gradient,
     // written alternately (LayerNorm-f and LN1 backward, LN2 backward) so a
@@ -174,6 +177,21 @@ hipError_t encoder_bwd(const int32_t* idx, const float* dres, float* dwte, float
                        int32_t* nseg_total, float* seg_part, int accumulate_wpe, hipStream_t s);
 hipError_t cast_f32_bf16(const float* src, bf16_t* dst, int64_t n, hipStream_t s);
 hipError_t fill_zero(void* p, size_t bytes, hipStream_t s);
+
+// --------------------------------------------------------------- generation
+constexpr int kGenMaxCache = 8192;  // longest key/value cache (block_size) gpt2_generate takes
+// x[b] = wte[seq[b * seq_ld + col]] + wpe[pos] for B rows (fp32 tables); an id
+// outside [0, V) sets GPT2_STATUS_TOKEN_RANGE and embeds token 0
+hipError_t gen_embed(const int32_t* seq, int64_t seq_ld, int col, const float* wte, const float* wpe, int pos,
+                     float* x, int B, int C, int V, uint32_t* status, hipStream_t s);
+// per (b, h): store this step's key and value (qkv [B, 3C]) at position pos of
+// the caches [B, Tc, C], then out[b, h] = softmax_j(q . k_j / sqrt(d)) v_j over j <= pos
+hipError_t gen_attention(int dtype, const void* qkv, void* kc, void* vc, int Tc, int pos, void* out, int B, int C,
+                         int H, hipStream_t s);
+// per row b: the smallest k whose cumulative softmax(logits[b, :V] / temperature)
+// probability exceeds u[b * u_ld + ucol]; written to seq[b * seq_ld + col]
+hipError_t gen_sample(const float* logits, int Vp, int V, float temperature, const float* u, int64_t u_ld, int ucol,
+                      int32_t* seq, int64_t seq_ld, int col, int B, hipStream_t s);
 hipError_t grad_norm(const float* g, int64_t n, double* part, int nblocks, float clip, float* norm_out,
                      float* coef_out, float* user_norm, uint32_t* status, hipStream_t s);
 hipError_t adamw(float* p, const float* g, float* m, float* v, bf16_t* p16, int64_t n, float lr, float b1,

@@ -1,0 +1,191 @@
+// Autoregressive generation, one position of B sequences per step, the loop of
+// MiniGPT.generate on the minigpt page (section 二; walkthrough 3.8): crop to the
+// last block_size tokens, forward, last position's logits over the temperature,
+// softmax, one draw, append. The forward of one position reuses the training
+// step's LayerNorm and GEMM kernels with M = B rows; what is new here is
+//  - the embedding of one position (gen_embed),
+//  - attention of the new query over a cache of the keys and values of the
+//    window so far (gen_attention), which also appends this position's k and v,
+//  - the draw (gen_sample): the smallest token whose cumulative probability, in
+//    index order, exceeds a caller-supplied uniform number u in [0, 1).
+#include <cfloat>
+
+#include "device.h"
+
+namespace g2 {
+namespace {
+
+__global__ void gen_embed_kernel(const int32_t* seq, int64_t seq_ld, int col, const float* wte, const float* wpe,
+                                 int pos, float* x, int C, int V, uint32_t* status) {
+    const int b = blockIdx.x;
+    int tok = seq[(int64_t)b * seq_ld + col];
+    if (tok < 0 || tok >= V) {
+        if (threadIdx.x == 0) atomicOr(status, (uint32_t)GPT2_STATUS_TOKEN_RANGE);
+        tok = 0;
+    }
+    const float* te = wte + (int64_t)tok * C;
+    const float* pe = wpe + (int64_t)pos * C;
+    float* xr = x + (int64_t)b * C;
+    for (int c = threadIdx.x; c < C; c += blockDim.x) xr[c] = te[c] + pe[c];
+}
+
+constexpr int kAttThreads = 256;
+
+// One workgroup per (sequence b, head h); d = C / H <= 128, pos < Tc <= kGenMaxCache.
+// Scores go to LDS (one float per cached position), then max, exponentials and
+// their sum; the output sums p_j v_j with each thread owning one dimension of
+// one of 256 / d interleaved slices of the positions, reduced in fixed order.
+template <class T>
+__global__ __launch_bounds__(kAttThreads) void gen_attn_kernel(const T* qkv, T* kc, T* vc, int Tc, int pos, T* out,
+                                                               int C, int H, float scale) {
+    extern __shared__ float sm[];  // scores[Tc] | q[d] | partial outputs[kAttThreads] | reduction[kAttThreads]
+    const int b = blockIdx.x / H, h = blockIdx.x % H;
+    const int d = C / H;
+    const int tid = threadIdx.x;
+    float* sc = sm;
+    float* q = sm + Tc;
+    float* part = q + d;
+    float* red = part + kAttThreads;
+    const T* row = qkv + (int64_t)b * 3 * C;
+    T* kb = kc + (int64_t)b * Tc * C + h * d;
+    T* vb = vc + (int64_t)b * Tc * C + h * d;
+    // this position's query, and its key and value appended to the caches
+    for (int c = tid; c < d; c += kAttThreads) {
+        q[c] = Act<T>::ld(row, h * d + c);
+        kb[(int64_t)pos * C + c] = row[C + h * d + c];
+        vb[(int64_t)pos * C + c] = row[2 * C + h * d + c];
+    }
+    __syncthreads();  // the appended k and v are visible to the whole workgroup
+    // scores of the positions j <= pos (causal: the new query sees the window so far)
+    float mx = -FLT_MAX;
+    for (int j = tid; j <= pos; j += kAttThreads) {
+        const T* kr = kb + (int64_t)j * C;
+        float s = 0.0f;
+        for (int c = 0; c < d; ++c) s = fmaf(q[c], Act<T>::ld(kr, c), s);
+        s *= scale;
+        sc[j] = s;
+        mx = fmaxf(mx, s);
+    }
+    red[tid] = mx;
+    __syncthreads();
+    for (int w = kAttThreads / 2; w > 0; w >>= 1) {
+        if (tid < w) red[tid] = fmaxf(red[tid], red[tid + w]);
+        __syncthreads();
+    }
+    mx = red[0];
+    __syncthreads();
+    float sum = 0.0f;
+    for (int j = tid; j <= pos; j += kAttThreads) {
+        const float e = __expf(sc[j] - mx);
+        sc[j] = e;
+        sum += e;
+    }
+    red[tid] = sum;
+    __syncthreads();
+    for (int w = kAttThreads / 2; w > 0; w >>= 1) {
+        if (tid < w) red[tid] += red[tid + w];
+        __syncthreads();
+    }
+    const float inv = 1.0f / red[0];
+    // out[c] = sum_j p_j v_j[c]: slice `sl` of the positions (j = sl, sl + ns, ...)
+    const int ns = kAttThreads / d;  // d <= 128, so ns >= 2
+    const int c = tid % d, sl = tid / d;
+    float acc = 0.0f;
+    if (sl < ns)
+        for (int j = sl; j <= pos; j += ns) acc = fmaf(sc[j], Act<T>::ld(vb + (int64_t)j * C, c), acc);
+    part[tid] = acc;
+    __syncthreads();
+    if (tid < d) {
+        float o = 0.0f;
+        for (int k = 0; k < ns; ++k) o += part[k * d + tid];
+        Act<T>::st(out, (int64_t)b * C + h * d + tid, o * inv);
+    }
+}
+
+constexpr int kSampleThreads = 1024;
+
+// One workgroup per row. Thread t owns the contiguous chunk [t * ch, (t + 1) * ch)
+// of the vocabulary; chunk sums of exp((z - max) / temperature) are scanned in
+// index order, and the thread whose chunk holds u * total walks it to the first
+// token whose running sum exceeds it.
+__global__ __launch_bounds__(kSampleThreads) void gen_sample_kernel(const float* logits, int Vp, int V,
+                                                                    float inv_temp, const float* u, int64_t u_ld,
+                                                                    int ucol, int32_t* seq, int64_t seq_ld, int col) {
+    __shared__ float red[kSampleThreads];
+    __shared__ float scan[kSampleThreads + 1];
+    __shared__ int pick;
+    const int b = blockIdx.x, tid = threadIdx.x;
+    const float* z = logits + (int64_t)b * Vp;
+    const int ch = (V + kSampleThreads - 1) / kSampleThreads;
+    const int lo = min(V, tid * ch), hi = min(V, lo + ch);
+    float mx = -FLT_MAX;
+    for (int k = lo; k < hi; ++k) mx = fmaxf(mx, z[k]);
+    red[tid] = mx;
+    if (tid == 0) pick = -1;
+    __syncthreads();
+    for (int w = kSampleThreads / 2; w > 0; w >>= 1) {
+        if (tid < w) red[tid] = fmaxf(red[tid], red[tid + w]);
+        __syncthreads();
+    }
+    mx = red[0];
+    float s = 0.0f;
+    for (int k = lo; k < hi; ++k) s += __expf((z[k] - mx) * inv_temp);
+    scan[tid + 1] = s;
+    __syncthreads();
+    if (tid == 0) {  // exclusive prefix of the chunk sums, in index order
+        scan[0] = 0.0f;
+        for (int t = 1; t <= kSampleThreads; ++t) scan[t] += scan[t - 1];
+    }
+    __syncthreads();
+    const float target = u[(int64_t)b * u_ld + ucol] * scan[kSampleThreads];
+    if (target >= scan[tid] && target < scan[tid + 1]) {
+        float run = scan[tid];
+        int k = lo;
+        for (; k < hi; ++k) {
+            run += __expf((z[k] - mx) * inv_temp);
+            if (run > target) break;
+        }
+        atomicMax(&pick, min(k, hi - 1));  // one chunk holds the target; max keeps it unique
+    }
+    __syncthreads();
+    if (tid == 0) {
+        int k = pick;
+        if (k < 0) {  // u * total at or past the rounded total: the last token with p > 0
+            k = V - 1;
+            while (k > 0 && __expf((z[k] - mx) * inv_temp) == 0.0f) --k;
+        }
+        seq[(int64_t)b * seq_ld + col] = k;
+    }
+}
+
+}  // namespace
+
+hipError_t gen_embed(const int32_t* seq, int64_t seq_ld, int col, const float* wte, const float* wpe, int pos,
+                     float* x, int B, int C, int V, uint32_t* status, hipStream_t s) {
+    hipLaunchKernelGGL(gen_embed_kernel, dim3(B), dim3(256), 0, s, seq, seq_ld, col, wte, wpe, pos, x, C, V, status);
+    return hipGetLastError();
+}
+
+hipError_t gen_attention(int dtype, const void* qkv, void* kc, void* vc, int Tc, int pos, void* out, int B, int C,
+                         int H, hipStream_t s) {
+    const int d = C / H;
+    if (d > 128 || pos < 0 || pos >= Tc || Tc > kGenMaxCache) return hipErrorInvalidValue;
+    const size_t lds = (size_t)(Tc + d + 2 * kAttThreads) * sizeof(float);
+    const float scale = 1.0f / sqrtf((float)d);
+    if (dtype == GPT2_DTYPE_BF16)
+        hipLaunchKernelGGL(gen_attn_kernel<bf16_t>, dim3(B * H), dim3(kAttThreads), lds, s, (const bf16_t*)qkv,
+                           (bf16_t*)kc, (bf16_t*)vc, Tc, pos, (bf16_t*)out, C, H, scale);
+    else
+        hipLaunchKernelGGL(gen_attn_kernel<float>, dim3(B * H), dim3(kAttThreads), lds, s, (const float*)qkv,
+                           (float*)kc, (float*)vc, Tc, pos, (float*)out, C, H, scale);
+    return hipGetLastError();
+}
+
+hipError_t gen_sample(const float* logits, int Vp, int V, float temperature, const float* u, int64_t u_ld, int ucol,
+                      int32_t* seq, int64_t seq_ld, int col, int B, hipStream_t s) {
+    hipLaunchKernelGGL(gen_sample_kernel, dim3(B), dim3(kSampleThreads), 0, s, logits, Vp, V, 1.0f / temperature, u,
+                       u_ld, ucol, seq, seq_ld, col);
+    return hipGetLastError();
+}
+
+}  // namespace g2

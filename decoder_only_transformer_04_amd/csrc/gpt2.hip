@@ -58,7 +58,10 @@ int check_batch(const gpt2_config* c, int32_t B, int32_t T, int32_t mode) {
     int e = validate_config(c);
     if (e) return e;
     if (B < 1 || T < 1 || T > c->block_size) return GPT2_EINVAL;  // T <= block_size, the forward's assert
-    if (mode != GPT2_MODE_TRAIN && mode != GPT2_MODE_EVAL) return GPT2_EINVAL;
+    if (mode != GPT2_MODE_TRAIN && mode != GPT2_MODE_EVAL && mode != GPT2_MODE_GENERATE) return GPT2_EINVAL;
+    // generation caches every position of the window; its attention keeps one
+    // score per cached position in LDS
+    if (mode == GPT2_MODE_GENERATE && (T != c->block_size || T > kGenMaxCache)) return GPT2_EINVAL;
     if ((int64_t)B * T > (int64_t)1 << 30) return GPT2_EINVAL;
     return GPT2_OK;
 }
@@ -390,6 +393,7 @@ void gpt2_destroy(gpt2_ctx* x) {
 
 int gpt2_forward(gpt2_ctx* x, const int32_t* d_idx, const int32_t* d_targets, float* d_loss, int32_t* d_argmax) {
     if (!x || !d_idx) return GPT2_EINVAL;
+    if (x->ap.mode == GPT2_MODE_GENERATE) return GPT2_ESTATE;
     const gpt2_config& c = x->cfg;
     const ArenaPlan& ap = x->ap;
     const int M = ap.M, T = ap.T, C = c.n_embd, F = c.mlp_hidden, H = c.n_head;
@@ -621,6 +625,80 @@ int gpt2_adamw_step(gpt2_ctx* x, float lr, float beta1, float beta2, float eps, 
     const uint8_t* tab = decay_mode == GPT2_DECAY_MATRICES ? at<uint8_t>(x, ap.decay_tab) : nullptr;
     G2_T("adamw", adamw(x->bufs.params, x->bufs.grads, x->bufs.adam_m, x->bufs.adam_v, p16, x->pl.n_flat, lr, beta1, beta2, eps,
                  decay_mul, (float)bc1, (float)bc2, tab, sc + SLOT_COEF, s));
+    return GPT2_OK;
+}
+
+// One position of the B sequences through the model (generation): the token in
+// column `col` of each row of seq at model position `pos`, its keys and values
+// appended to the caches at `pos`; with `head`, the final LayerNorm and the head
+// leave fp32 logits [B, Vp] for the sampler.
+static int gen_position(gpt2_ctx* x, const int32_t* seq, int64_t seq_ld, int col, int pos, bool head) {
+    const gpt2_config& c = x->cfg;
+    const ArenaPlan& ap = x->ap;
+    const int B = ap.B, C = c.n_embd, F = c.mlp_hidden, H = c.n_head;
+    const int Vp = (int)x->pl.vocab_pad;
+    const int dt = c.dtype;
+    hipStream_t s = x->stream;
+    float* xr = at<float>(x, ap.x[0]);
+    float* xmid = at<float>(x, ap.xmid[0]);
+    G2_T("gen.embed", gen_embed(seq, seq_ld, col, pf(x, x->pl.wte), pf(x, x->pl.wpe), pos, xr, B, C, c.vocab,
+                                status_ptr(x), s));
+    for (int l = 0; l < c.n_layer; ++l) {
+        const LayerW& w = x->pl.layer[l];
+        G2_T("gen.ln", layernorm_fwd(dt, xr, pf(x, w.ln1_g), pf(x, w.ln1_b), c.ln_eps, at<char>(x, ap.ln1[0]),
+                                     at<float>(x, ap.m1[0]), at<float>(x, ap.r1[0]), B, C, s));
+        G2_T("gen.gemm", linear_fwd(x, EPI_STORE, B, 3 * C, C, at<char>(x, ap.ln1[0]), wptr(x, w.w_qkv), pf(x, w.b_qkv),
+                                    at<char>(x, ap.qkv[0]), nullptr, nullptr));
+        G2_T("gen.attn", gen_attention(dt, at<char>(x, ap.qkv[0]), at<char>(x, ap.kc[l]), at<char>(x, ap.vc[l]), ap.T, pos,
+                                       at<char>(x, ap.att[0]), B, C, H, s));
+        G2_T("gen.gemm", linear_fwd(x, EPI_RESID, B, C, C, at<char>(x, ap.att[0]), wptr(x, w.w_proj), pf(x, w.b_proj), xmid,
+                                    nullptr, xr));
+        G2_T("gen.ln", layernorm_fwd(dt, xmid, pf(x, w.ln2_g), pf(x, w.ln2_b), c.ln_eps, at<char>(x, ap.ln2[0]),
+                                     at<float>(x, ap.m2[0]), at<float>(x, ap.r2[0]), B, C, s));
+        G2_T("gen.gemm", linear_fwd(x, EPI_GELU, B, F, C, at<char>(x, ap.ln2[0]), wptr(x, w.w_fc), pf(x, w.b_fc),
+                                    at<char>(x, ap.fch[0]), at<char>(x, ap.fcg[0]), nullptr));
+        G2_T("gen.gemm", linear_fwd(x, EPI_RESID, B, C, F, at<char>(x, ap.fcg[0]), wptr(x, w.w_fc2), pf(x, w.b_fc2), xr,
+                                    nullptr, xmid));
+    }
+    if (!head) return GPT2_OK;
+    G2_T("gen.ln", layernorm_fwd(dt, xr, pf(x, x->pl.lnf_g), pf(x, x->pl.lnf_b), c.ln_eps, at<char>(x, ap.xf),
+                                 at<float>(x, ap.mf), at<float>(x, ap.rf), B, C, s));
+    G2_T("gen.head", linear_fwd(x, EPI_F32, B, Vp, C, at<char>(x, ap.xf), wptr(x, x->pl.lm_head), nullptr,
+                                at<float>(x, ap.logits), nullptr, nullptr));
+    return GPT2_OK;
+}
+
+int gpt2_generate(gpt2_ctx* x, const int32_t* d_prompt, int32_t T0, int32_t n_new, float temperature,
+                  const float* d_uniform, int32_t* d_out) {
+    if (!x || !d_prompt || !d_out || T0 < 1 || n_new < 0 || (n_new > 0 && !d_uniform)) return GPT2_EINVAL;
+    if (!(temperature > 0.0f) || !std::isfinite(temperature)) return GPT2_EINVAL;
+    if (x->ap.mode != GPT2_MODE_GENERATE) return GPT2_ESTATE;
+    if ((int64_t)T0 + n_new > INT32_MAX) return GPT2_EINVAL;
+    const int B = x->ap.B, bs = x->cfg.block_size, Vp = (int)x->pl.vocab_pad;
+    const int64_t len = (int64_t)T0 + n_new;  // row length of d_out
+    hipStream_t s = x->stream;
+    G2_TRY(hipMemcpy2DAsync(d_out, len * 4, d_prompt, (size_t)T0 * 4, (size_t)T0 * 4, B, hipMemcpyDeviceToDevice, s));
+    // The caches hold the window that starts at sequence column w_cached, with
+    // `filled` positions so far. While the sequence fits in block_size the window
+    // only grows, one position per new token; past it the window slides, every
+    // position of the model moves, and the window is run again from its start.
+    int w_cached = -1, filled = 0;
+    for (int i = 0; i < n_new; ++i) {
+        const int n = T0 + i;  // tokens so far
+        const int w0 = n > bs ? n - bs : 0;
+        if (w0 != w_cached) {
+            w_cached = w0;
+            filled = 0;
+        }
+        while (w0 + filled < n) {
+            const int col = w0 + filled;
+            const int e = gen_position(x, d_out, len, col, filled, col == n - 1);
+            if (e) return e;
+            ++filled;
+        }
+        G2_T("gen.sample", gen_sample(at<float>(x, x->ap.logits), Vp, x->cfg.vocab, temperature, d_uniform, n_new, i,
+                                      d_out, len, n, B, s));
+    }
     return GPT2_OK;
 }
 

@@ -84,7 +84,9 @@ ParamLayout make_param_layout(const gpt2_config& c) {
 
 ArenaPlan make_arena_plan(const gpt2_config& c, const ParamLayout& pl, int B, int T, int mode) {
     ArenaPlan a;
-    a.M = B * T;
+    const bool gen = mode == GPT2_MODE_GENERATE;
+    // generation runs one position of B sequences at a time; T is the cache length
+    a.M = gen ? B : B * T;
     a.B = B;
     a.T = T;
     a.mode = mode;
@@ -114,7 +116,7 @@ ArenaPlan make_arena_plan(const gpt2_config& c, const ParamLayout& pl, int B, in
         a.r1.push_back(take(M * 4));
         a.qkv.push_back(take(M * 3 * C * ab));
         a.att.push_back(take(M * C * ab));
-        a.lse.push_back(take((size_t)B * H * T * 4));
+        a.lse.push_back(take((size_t)B * H * (gen ? 1 : T) * 4));
         a.xmid.push_back(take(M * C * 4));
         a.ln2.push_back(take(M * C * ab));
         a.m2.push_back(take(M * 4));
@@ -126,7 +128,12 @@ ArenaPlan make_arena_plan(const gpt2_config& c, const ParamLayout& pl, int B, in
     a.xf = take(M * C * ab);
     a.mf = take(M * 4);
     a.rf = take(M * 4);
-    a.logits = take(M * Vp * ab);
+    a.logits = take(M * Vp * (gen ? 4 : ab));
+    if (gen)
+        for (int l = 0; l < c.n_layer; ++l) {
+            a.kc.push_back(take((size_t)B * T * C * ab));
+            a.vc.push_back(take((size_t)B * T * C * ab));
+        }
     a.loss_rows = take(M * 4);
     if (train) {
         a.dres = take(M * C * 4);

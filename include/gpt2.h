@@ -51,6 +51,8 @@ extern "C" {
 
 #define GPT2_MODE_TRAIN 0  /* forward keeps what backward needs */
 #define GPT2_MODE_EVAL 1   /* forward and loss only; smaller arena */
+#define GPT2_MODE_GENERATE 2  /* gpt2_generate only: key/value caches of block_size positions
+                                 for B sequences (T must equal block_size) */
 
 #define GPT2_STATUS_TOKEN_RANGE 1u      /* an input or target id was outside [0, V) */
 #define GPT2_STATUS_NONFINITE_LOSS 2u   /* the mean loss was NaN or Inf */
@@ -165,6 +167,23 @@ int gpt2_backward(gpt2_ctx* ctx, float loss_scale, int32_t zero_grads);
  * flat buffers, and the low-precision weight copies are refreshed. */
 int gpt2_adamw_step(gpt2_ctx* ctx, float lr, float beta1, float beta2, float eps, float weight_decay,
                     int32_t t, float clip, int32_t decay_mode, float* d_grad_norm);
+
+/* Autoregressive generation (MiniGPT.generate on the minigpt page, section 二 and
+ * walkthrough 3.8) for a context made with GPT2_MODE_GENERATE (B sequences, T =
+ * block_size). d_prompt: device int32 [B, T0], T0 >= 1. d_out: device int32
+ * [B, T0 + n_new], receives the prompt followed by n_new drawn tokens. Each new
+ * token: crop the sequence to its last block_size tokens, run the model, take
+ * the last position's logits over `temperature` (> 0), softmax, and draw: the
+ * token is the smallest k whose cumulative probability (index order) exceeds
+ * u = d_uniform[b * n_new + i] (device fp32 [B, n_new], u in [0, 1); the pages
+ * leave multinomial's procedure open, this is inverse-CDF sampling with the
+ * caller's random numbers; u at or above the rounded total gives the last token
+ * with nonzero probability). Keys and values of the window are cached; once the
+ * sequence is longer than block_size the window slides and is recomputed from
+ * its start each step. An id outside [0, V) sets GPT2_STATUS_TOKEN_RANGE.
+ * Enqueue-only on the context's stream; GPT2_ESTATE for other modes. */
+int gpt2_generate(gpt2_ctx* ctx, const int32_t* d_prompt, int32_t T0, int32_t n_new, float temperature,
+                  const float* d_uniform, int32_t* d_out);
 
 /* Synchronises the stream and reads the sticky status word into *bits (nullable).
  * Returns GPT2_EDEVICE if any bit is set, else GPT2_OK. gpt2_clear_status resets it. */
