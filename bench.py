@@ -139,6 +139,75 @@ def cpu_baseline(w: syn.Workload, named: dict, seq: int):
                       f"{syn.n_params_exact(m)} parameters ({t2 - t1:.2f} s)"}
 
 
+def bench_generate(args, b):
+    """Generation with the key/value cache: B sequences, a Zipf prompt of P tokens,
+    N new tokens at temperature 1. A position step runs B rows through the model;
+    P + N - 1 steps feed the prompt and every new token but the last, and the N
+    steps that end a feed also run the head and the sampler. Throughput is new
+    tokens per second (B N / time, prompt included in the time) and position
+    rows per second. The roofline is HBM: one position step reads every weight
+    once (bf16 copy), so its algorithmic bytes are 2 bytes per flat-buffer element
+    (without the head's on steps that skip it), timed per label."""
+    import numpy as np
+    import torch
+    w = syn.WORKLOADS[args.workload]
+    m = w.model
+    B, P, N = args.gen_batch, args.gen_prompt, args.gen_new
+    if P + N > m.block_size:
+        sys.exit("prompt + new tokens must fit in block_size for this measurement (no window slide)")
+    cfg = b.make_config(m.vocab, m.block_size, m.n_embd, m.n_head, m.n_layer, m.mlp_hidden, m.bias, b.DTYPE_BF16,
+                        m.ln_eps, gelu_erf=m.gelu_erf, untied_head=m.untied)
+    g = b.Model(cfg, B, m.block_size, b.MODE_GENERATE)
+    g.load_named(syn.init_params(m))
+    g.init()
+    rng = np.random.default_rng(syn.DATA_SEED)
+    prompt = torch.from_numpy(syn.draw_tokens(rng, m.vocab, B * P, "zipf", w.zipf_s).reshape(B, P)).cuda()
+    u = torch.from_numpy(rng.random((B, N)).astype(np.float32)).cuda()
+    out = torch.empty((B, P + N), dtype=torch.int32, device="cuda")
+    g.generate(prompt, N, 1.0, u, out)  # warm-up
+    torch.cuda.synchronize()
+    labels = ["gen.embed", "gen.ln", "gen.gemm", "gen.attn", "gen.head", "gen.sample"]
+    breakdown = {}
+    for lab in labels:
+        g.timing_begin(lab)
+        g.generate(prompt, N, 1.0, u, out)
+        ms, n = g.timing_end()
+        breakdown[lab] = {"ms": round(ms, 4), "launches": n}
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = max(1, args.steps // 5)
+    ev0.record()
+    for _ in range(reps):
+        g.generate(prompt, N, 1.0, u, out)
+    ev1.record()
+    torch.cuda.synchronize()
+    sec = ev0.elapsed_time(ev1) / 1e3 / reps
+    status = g.sync_status()
+    steps = P + N - 1
+    n_head = sum(int(np.prod(d["shape"])) for d in g.table if d["name"] == ("lm_head" if m.untied else "wte"))
+    n_body = g.n_flat - g.vocab_pad * m.n_embd * (2 if m.untied else 1)  # layer and LN weights (+ wpe)
+    gemm_ms = breakdown["gen.gemm"]["ms"] / breakdown["gen.gemm"]["launches"] * 4 * m.n_layer  # per step
+    body_bytes = 2 * (n_body - m.block_size * m.n_embd)
+    head_ms = breakdown["gen.head"]["ms"] / max(1, breakdown["gen.head"]["launches"])
+    head_bytes = 2 * g.vocab_pad * m.n_embd
+    out_line = {
+        "metric": "GPT-2 124M generation, new tokens/sec with the key/value cache (bf16 weights)",
+        "value": round(B * N / sec, 1), "unit": "tokens/s", "n_gpus": 1, "higher_is_better": True,
+        "dtype": "bf16", "data": "synthetic (Zipf s=1.05 prompts, N(0,0.02) init, uniform draws)",
+        "config": {"workload": f"{w.name}: B={B} sequences, prompt {P}, {N} new tokens, temperature 1",
+                   "batch": B, "prompt": P, "new_tokens": N},
+        "ms_per_generate": round(sec * 1e3, 3), "position_rows_per_s": round(B * steps / sec, 1),
+        "status": status,
+        "roofline": {"bound": "hbm", "kernel": "gen.gemm (the four layer products of one position step)",
+                     "achieved": round(body_bytes / (gemm_ms / 1e3) / 1e9, 2), "peak": PEAK_HBM / 1e9,
+                     "unit": "GB/s", "frac": round(body_bytes / (gemm_ms / 1e3) / PEAK_HBM, 4), "traffic": None,
+                     "bytes_per_step": body_bytes, "ms_per_step": round(gemm_ms, 4)},
+        "head_roofline": {"achieved": round(head_bytes / (head_ms / 1e3) / 1e9, 2), "unit": "GB/s",
+                          "ms_per_launch": round(head_ms, 4), "bytes": head_bytes},
+        "breakdown": breakdown,
+    }
+    print(json.dumps(out_line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -151,6 +220,11 @@ def main():
     ap.add_argument("--no-breakdown", action="store_true", help="skip the per-kernel-class timing pass")
     ap.add_argument("--roofline-kernel", default=None, help="timing label for the roofline (default: the "
                     "label with the largest time in the breakdown pass)")
+    ap.add_argument("--generate", action="store_true", help="measure generation instead of the training step "
+                    "(prints its own JSON line)")
+    ap.add_argument("--gen-batch", type=int, default=12)
+    ap.add_argument("--gen-prompt", type=int, default=32)
+    ap.add_argument("--gen-new", type=int, default=64)
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -161,6 +235,9 @@ def main():
     import torch
     from decoder_only_transformer_04_amd import binding as b
 
+    if args.generate:
+        bench_generate(args, b)
+        return
     w = syn.WORKLOADS[args.workload]
     m = w.model
     cfg = b.make_config(m.vocab, m.block_size, m.n_embd, m.n_head, m.n_layer, m.mlp_hidden, m.bias, b.DTYPE_BF16,

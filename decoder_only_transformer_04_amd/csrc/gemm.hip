@@ -710,6 +710,99 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GP p) {
         }
 }
 
+// ------------------------------------------------------------------ skinny products
+// Y = X W^T with at most kSkinnyRows rows of X, both contraction-contiguous
+// (generation runs one position of a few sequences at a time). Tiles of 128+
+// rows would leave all but a few CUs idle; here every wave owns one output
+// column n, streams row n of W once with 16-byte loads (8 bf16 or 4 fp32 per
+// lane), and keeps one partial sum per row of X, whose rows come through LDS in
+// kSkinnyChunk-wide pieces of the contraction. A wave reduction leaves the M
+// sums of column n; the tiled kernel's epilogues finish them. Summation order is
+// fixed. (Reading X straight from the caches instead, several columns per wave,
+// measured slower.)
+constexpr int kSkinnyRows = 16;
+constexpr int kSkinnyWaves = 4;
+constexpr int kSkinnyChunk = 1024;
+
+template <int E>
+__device__ __forceinline__ void skinny_unpack(uint4 v, float (&o)[E]) {
+    if constexpr (E == 8) {
+        unpack8(v, o);
+    } else {
+        o[0] = __uint_as_float(v.x); o[1] = __uint_as_float(v.y);
+        o[2] = __uint_as_float(v.z); o[3] = __uint_as_float(v.w);
+    }
+}
+
+template <int EPI, class T>
+__global__ __launch_bounds__(64 * kSkinnyWaves) void gemm_skinny_kernel(GP p) {
+    constexpr int E = 16 / sizeof(T);  // elements per 16-byte load
+    __shared__ __attribute__((aligned(16))) T xs[kSkinnyRows * kSkinnyChunk];
+    const int M = (int)p.M, K = p.K, N = p.N;
+    const T* X = (const T*)p.A;
+    const T* W = (const T*)p.B;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int n = blockIdx.x * kSkinnyWaves + wave;
+    const T* wr = W + (int64_t)min(n, N - 1) * p.ldb;
+    float acc[kSkinnyRows];
+#pragma unroll
+    for (int m = 0; m < kSkinnyRows; ++m) acc[m] = 0.0f;
+    for (int kc = 0; kc < K; kc += kSkinnyChunk) {
+        const int kn = min(kSkinnyChunk, K - kc);
+        __syncthreads();  // the previous chunk is no longer read
+        for (int i = threadIdx.x * E; i < M * kn; i += 64 * kSkinnyWaves * E) {
+            const int m = i / kn, k = i - m * kn;  // kn is a multiple of E
+            *(uint4*)(xs + m * kSkinnyChunk + k) = *(const uint4*)(X + (int64_t)m * p.lda + kc + k);
+        }
+        __syncthreads();
+        for (int k = lane * E; k < kn; k += 64 * E) {
+            float w[E];
+            skinny_unpack<E>(*(const uint4*)(wr + kc + k), w);
+#pragma unroll
+            for (int m = 0; m < kSkinnyRows; ++m) {
+                if (m < M) {
+                    float x[E];
+                    skinny_unpack<E>(*(const uint4*)(xs + m * kSkinnyChunk + k), x);
+#pragma unroll
+                    for (int e = 0; e < E; ++e) acc[m] = fmaf(w[e], x[e], acc[m]);
+                }
+            }
+        }
+    }
+    // every lane ends with the column's M sums; lane m finishes row m
+    float v = 0.0f;
+#pragma unroll
+    for (int m = 0; m < kSkinnyRows; ++m) {
+        if (m < M) {
+            float a = acc[m];
+#pragma unroll
+            for (int off = 32; off > 0; off >>= 1) a += __shfl_xor(a, off, 64);
+            if (lane == m) v = a;
+        }
+    }
+    if (n < N && lane < M) epi_apply<EPI, T>(p, lane, n, v);
+}
+
+template <int EPI>
+static hipError_t launch_skinny(int dtype, const GP& p, hipStream_t s) {
+    const dim3 grid((unsigned)((p.N + kSkinnyWaves - 1) / kSkinnyWaves));
+    if (dtype == GPT2_DTYPE_BF16)
+        hipLaunchKernelGGL((gemm_skinny_kernel<EPI, bf16_t>), grid, dim3(64 * kSkinnyWaves), 0, s, p);
+    else
+        hipLaunchKernelGGL((gemm_skinny_kernel<EPI, float>), grid, dim3(64 * kSkinnyWaves), 0, s, p);
+    return hipGetLastError();
+}
+
+// forward products the skinny kernel takes: few rows, 16-byte aligned rows of X and W
+static bool skinny_ok(int dtype, const GemmArgs& a) {
+    const int E = dtype == GPT2_DTYPE_BF16 ? 8 : 4;
+    const int eb = dtype == GPT2_DTYPE_BF16 ? 2 : 4;
+    // (vocabulary-wide outputs keep the tiled kernel, measured faster there)
+    return a.M <= kSkinnyRows && a.N < 8192 && a.K > 0 && a.K % E == 0 && a.lda % E == 0 && a.ldb % E == 0 &&
+           ((uintptr_t)a.A % 16) == 0 && ((uintptr_t)a.B % 16) == 0 && (a.epi == EPI_STORE || a.epi == EPI_GELU ||
+           a.epi == EPI_RESID || a.epi == EPI_F32) && eb > 0;
+}
+
 // ------------------------------------------------------------------ split-K reduction
 // out[i] = sum_s part[s][i] (in s order) (+ out[i] if accumulate)
 __global__ void splitk_reduce_kernel(const float* part, int splits, int64_t n, float* out, int64_t rows,
@@ -891,6 +984,14 @@ hipError_t gemm(int dtype, const GemmArgs& a, hipStream_t s) {
         p.K = 0;
     }
     const bool kc11 = a.a_kc && a.b_kc, kc10 = a.a_kc && !a.b_kc, kc00 = !a.a_kc && !a.b_kc;
+    if (kc11 && skinny_ok(dtype, a)) {
+        switch (a.epi) {
+            case EPI_STORE: return launch_skinny<EPI_STORE>(dtype, p, s);
+            case EPI_GELU: return launch_skinny<EPI_GELU>(dtype, p, s);
+            case EPI_RESID: return launch_skinny<EPI_RESID>(dtype, p, s);
+            case EPI_F32: return launch_skinny<EPI_F32>(dtype, p, s);
+        }
+    }
     if (kc11) {
         switch (a.epi) {
             case EPI_STORE: return dispatch<true, true, EPI_STORE>(dtype, p, 1, s);
