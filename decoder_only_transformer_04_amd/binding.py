@@ -17,14 +17,15 @@ GPT2_OK, GPT2_EINVAL, GPT2_ENOSPC, GPT2_EHIP, GPT2_EDEVICE, GPT2_ESTATE = 0, -1,
 DTYPE_F32, DTYPE_BF16 = 0, 1
 MODE_TRAIN, MODE_EVAL, MODE_GENERATE = 0, 1, 2
 DECAY_ALL, DECAY_MATRICES = 0, 1
-STATUS_TOKEN_RANGE, STATUS_NONFINITE_LOSS, STATUS_NONFINITE_GNORM = 1, 2, 4
+STATUS_TOKEN_RANGE, STATUS_NONFINITE_LOSS, STATUS_NONFINITE_GNORM, STATUS_WINDOW_RANGE = 1, 2, 4, 8
 
 EXPORTS = [
     "gpt2_query_sizes", "gpt2_num_params", "gpt2_param_table", "gpt2_lr_cosine", "gpt2_strerror", "gpt2_init",
     "gpt2_refresh_weights", "gpt2_forward", "gpt2_backward", "gpt2_adamw_step", "gpt2_generate", "gpt2_sync_status",
     "gpt2_clear_status", "gpt2_arena_tensor", "gpt2_destroy", "gpt2_op_linear_fwd", "gpt2_op_linear_bwd",
     "gpt2_op_layernorm_fwd", "gpt2_op_layernorm_bwd", "gpt2_op_attention_fwd", "gpt2_op_attention_bwd",
-    "gpt2_op_cross_entropy", "gpt2_timing_begin", "gpt2_timing_end",
+    "gpt2_op_cross_entropy", "gpt2_timing_begin", "gpt2_timing_end", "gpt2_char_vocab", "gpt2_char_encode",
+    "gpt2_char_decode", "gpt2_split_point", "gpt2_batch_windows",
 ]
 
 
@@ -59,6 +60,10 @@ def lib():
     if _lib is None:
         if not os.path.exists(LIB_PATH):
             raise RuntimeError(f"{LIB_PATH} is missing: build it first (python -m decoder_only_transformer_04_amd.build)")
+        # torch first: it loads the HIP runtime it was built with, and the library
+        # then binds to that one; loaded the other way round, the process can end up
+        # with two runtimes, and the library's sees no device
+        import torch  # noqa: F401
         L = ct.CDLL(LIB_PATH)
         P, i32, i64, f32, f64 = ct.c_void_p, ct.c_int32, ct.c_int64, ct.c_float, ct.c_double
         sz = ct.POINTER(ct.c_size_t)
@@ -74,6 +79,11 @@ def lib():
             "gpt2_backward": (ct.c_int, [P, f32, i32]),
             "gpt2_adamw_step": (ct.c_int, [P, f32, f32, f32, f32, f32, i32, f32, i32, P]),
             "gpt2_generate": (ct.c_int, [P, P, i32, i32, f32, P, P]),
+            "gpt2_char_vocab": (i32, [P, i64, P]),
+            "gpt2_char_encode": (ct.c_int, [P, i64, P, i32, P]),
+            "gpt2_char_decode": (ct.c_int, [P, i64, P, i32, P]),
+            "gpt2_split_point": (i64, [i64, f64]),
+            "gpt2_batch_windows": (ct.c_int, [P, i64, P, i32, i32, P, P, P, P]),
             "gpt2_sync_status": (ct.c_int, [P, ct.POINTER(ct.c_uint32)]),
             "gpt2_clear_status": (ct.c_int, [P]),
             "gpt2_arena_tensor": (ct.c_int, [P, ct.c_char_p, i32, sz, ct.POINTER(i32), ct.POINTER(i64),
@@ -135,6 +145,42 @@ def param_table(cfg: Config):
         out.append({"name": name, "layer": d.layer, "decay": d.decay, "offset": int(d.offset), "shape": shape,
                     "reserved": int(d.reserved)})
     return out
+
+
+# ------------------------------------------------------------------ character-level data
+def char_vocab(text: bytes) -> list:
+    buf = (ct.c_uint8 * 256)()
+    v = check(int(lib().gpt2_char_vocab(text, len(text), buf)), "gpt2_char_vocab")
+    return list(buf[:v])
+
+
+def char_encode(text: bytes, vocab: list):
+    import numpy as np
+    ids = np.empty(len(text), dtype=np.int32)
+    ch = (ct.c_uint8 * 256)(*vocab)
+    check(lib().gpt2_char_encode(text, len(text), ch, len(vocab), ids.ctypes.data_as(ct.c_void_p)),
+          "gpt2_char_encode")
+    return ids
+
+
+def char_decode(ids, vocab: list) -> bytes:
+    import numpy as np
+    ids = np.ascontiguousarray(ids, dtype=np.int32)
+    out = ct.create_string_buffer(max(1, ids.size))
+    ch = (ct.c_uint8 * 256)(*vocab)
+    check(lib().gpt2_char_decode(ids.ctypes.data_as(ct.c_void_p), ids.size, ch, len(vocab), out), "gpt2_char_decode")
+    return out.raw[:ids.size]
+
+
+def split_point(n: int, ratio: float = 0.9) -> int:
+    return check(int(lib().gpt2_split_point(int(n), float(ratio))), "gpt2_split_point")
+
+
+def batch_windows(data, offsets, x, y, status=None, stream=None) -> None:
+    """data: int32 [n] (cuda); offsets: int64 [B] (cuda); x, y: int32 [B, T] (cuda)."""
+    B, T = x.shape
+    check(lib().gpt2_batch_windows(_ptr(data), data.numel(), _ptr(offsets), B, T, _ptr(x), _ptr(y), _ptr(status),
+                                   _s(stream)), "gpt2_batch_windows")
 
 
 def lr_cosine(it, max_lr=6e-4, min_lr=6e-5, warmup=2000, max_iters=600000) -> float:

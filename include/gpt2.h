@@ -57,6 +57,7 @@ extern "C" {
 #define GPT2_STATUS_TOKEN_RANGE 1u      /* an input or target id was outside [0, V) */
 #define GPT2_STATUS_NONFINITE_LOSS 2u   /* the mean loss was NaN or Inf */
 #define GPT2_STATUS_NONFINITE_GNORM 4u  /* the global gradient norm was NaN or Inf */
+#define GPT2_STATUS_WINDOW_RANGE 8u     /* gpt2_batch_windows: a window start outside [0, n - T - 1] */
 
 /* ------------------------------------------------------------------ types */
 /* Model shape (GPTConfig of the minigpt page, section 3.1; the 124M values of
@@ -184,6 +185,29 @@ int gpt2_adamw_step(gpt2_ctx* ctx, float lr, float beta1, float beta2, float eps
  * Enqueue-only on the context's stream; GPT2_ESTATE for other modes. */
 int gpt2_generate(gpt2_ctx* ctx, const int32_t* d_prompt, int32_t T0, int32_t n_new, float temperature,
                   const float* d_uniform, int32_t* d_out);
+
+/* ------------------------------------------------------------------ character-level data
+ * prepare_data and get_batch of minigpt.py (the minigpt page, section 二; walkthrough
+ * 3.2). A character is one byte of the text (the same as the page's str for ASCII).
+ *
+ * gpt2_char_vocab: the sorted distinct bytes of text[0, n) into chars[256]; returns
+ *   the vocabulary size (GPT2_EINVAL on null pointers). Host only.
+ * gpt2_char_encode / gpt2_char_decode: ids[i] = position of text[i] in chars[0,
+ *   vocab), and back; GPT2_EINVAL on a byte outside the vocabulary or an id outside
+ *   [0, vocab). Host only.
+ * gpt2_split_point: int(ratio * n), the end of the training split (ratio in [0, 1]).
+ * gpt2_batch_windows: device int32 token stream d_data[0, n), device int64 window
+ *   starts d_offsets[B] (get_batch draws them from [0, n - T - 1); the caller
+ *   supplies them) -> device int32 d_x[B, T] = d_data[off_b + t], d_y[B, T] =
+ *   d_data[off_b + t + 1]. A start outside [0, n - T - 1] zeroes its rows and sets
+ *   GPT2_STATUS_WINDOW_RANGE in *d_status (device uint32, nullable). Enqueued on
+ *   hip_stream; the caller owns every buffer. */
+int32_t gpt2_char_vocab(const uint8_t* text, int64_t n, uint8_t* chars);
+int gpt2_char_encode(const uint8_t* text, int64_t n, const uint8_t* chars, int32_t vocab, int32_t* ids);
+int gpt2_char_decode(const int32_t* ids, int64_t n, const uint8_t* chars, int32_t vocab, uint8_t* text);
+int64_t gpt2_split_point(int64_t n, double ratio);
+int gpt2_batch_windows(const int32_t* d_data, int64_t n, const int64_t* d_offsets, int32_t B, int32_t T,
+                       int32_t* d_x, int32_t* d_y, uint32_t* d_status, void* hip_stream);
 
 /* Synchronises the stream and reads the sticky status word into *bits (nullable).
  * Returns GPT2_EDEVICE if any bit is set, else GPT2_OK. gpt2_clear_status resets it. */
