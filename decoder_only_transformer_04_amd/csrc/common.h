@@ -90,7 +90,8 @@ enum ScalarSlot {
     SLOT_COEF = 1,     // float clip coefficient for AdamW
     SLOT_NORM = 2,     // float gradient norm
     SLOT_LOSS = 3,     // float mean loss (when the caller passes no loss pointer)
-    SLOT_NSEG = 4      // int32 number of token segments (embedding backward)
+    SLOT_NSEG = 4,     // int32 number of token segments (embedding backward)
+    SLOT_GEN = 5       // int32 [3]: generation step state (column, position, prompt length)
 };
 
 // --------------------------------------------------------------- GEMM
@@ -115,6 +116,11 @@ struct GemmArgs {
     const void* R; int64_t ldr;
     int accumulate;
     int gelu_erf;  // EPI_GELU: exact erf form instead of the tanh approximation
+    // few-row products (at most 16 rows, K <= 1024, EPI_STORE or EPI_GELU): when
+    // ln_g is set, A is fp32 and the operand is its LayerNorm with ln_g, ln_b, ln_eps
+    const float* ln_g;
+    const float* ln_b;
+    float ln_eps;
     void* split_buf; size_t split_bytes;  // fp32 scratch for split-K partials (nullable)
     // EPI_GELU_BWD only (nullable): column sums of the output over each 64-row
     // block, written to colsum_part[(m / 64) * N + n] (the bias gradient's partials)
@@ -180,18 +186,23 @@ hipError_t fill_zero(void* p, size_t bytes, hipStream_t s);
 
 // --------------------------------------------------------------- generation
 constexpr int kGenMaxCache = 8192;  // longest key/value cache (block_size) gpt2_generate takes
+// The step's position is device state cp[3] = {col: sequence column of the token
+// fed, pos: its model position, T0: prompt length}, set by gen_set and moved on by
+// one by gen_advance, so a captured step replays unchanged.
+hipError_t gen_set(int32_t* cp, int col, int pos, int T0, hipStream_t s);
+hipError_t gen_advance(int32_t* cp, hipStream_t s);
 // x[b] = wte[seq[b * seq_ld + col]] + wpe[pos] for B rows (fp32 tables); an id
 // outside [0, V) sets GPT2_STATUS_TOKEN_RANGE and embeds token 0
-hipError_t gen_embed(const int32_t* seq, int64_t seq_ld, int col, const float* wte, const float* wpe, int pos,
+hipError_t gen_embed(const int32_t* seq, int64_t seq_ld, const int32_t* cp, const float* wte, const float* wpe,
                      float* x, int B, int C, int V, uint32_t* status, hipStream_t s);
 // per (b, h): store this step's key and value (qkv [B, 3C]) at position pos of
 // the caches [B, Tc, C], then out[b, h] = softmax_j(q . k_j / sqrt(d)) v_j over j <= pos
-hipError_t gen_attention(int dtype, const void* qkv, void* kc, void* vc, int Tc, int pos, void* out, int B, int C,
-                         int H, hipStream_t s);
+hipError_t gen_attention(int dtype, const void* qkv, void* kc, void* vc, int Tc, const int32_t* cp, void* out, int B,
+                         int C, int H, hipStream_t s);
 // per row b: the smallest k whose cumulative softmax(logits[b, :V] / temperature)
-// probability exceeds u[b * u_ld + ucol]; written to seq[b * seq_ld + col]
-hipError_t gen_sample(const float* logits, int Vp, int V, float temperature, const float* u, int64_t u_ld, int ucol,
-                      int32_t* seq, int64_t seq_ld, int col, int B, hipStream_t s);
+// probability exceeds u[b * u_ld + (col + 1 - T0)]; written to seq[b * seq_ld + col + 1]
+hipError_t gen_sample(const float* logits, int Vp, int V, float temperature, const float* u, int64_t u_ld,
+                      const int32_t* cp, int32_t* seq, int64_t seq_ld, int B, hipStream_t s);
 hipError_t grad_norm(const float* g, int64_t n, double* part, int nblocks, float clip, float* norm_out,
                      float* coef_out, float* user_norm, uint32_t* status, hipStream_t s);
 hipError_t adamw(float* p, const float* g, float* m, float* v, bf16_t* p16, int64_t n, float lr, float b1,

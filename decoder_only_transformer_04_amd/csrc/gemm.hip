@@ -47,6 +47,9 @@ struct GP {
     int accumulate;
     int gelu_erf;  // EPI_GELU: exact erf form
     float* cpart;  // GELU_BWD: per-64-row column sums of the output (nullable)
+    const float* ln_g;  // skinny products: A is fp32 and the operand is its LayerNorm (nullable)
+    const float* ln_b;
+    float ln_eps;
 };
 
 // ------------------------------------------------------------------ epilogue
@@ -734,12 +737,15 @@ __device__ __forceinline__ void skinny_unpack(uint4 v, float (&o)[E]) {
     }
 }
 
-template <int EPI, class T>
+// LNX: X is the fp32 residual stream and the product's operand is its
+// LayerNorm (gain p.ln_g, bias p.ln_b, epsilon p.ln_eps, biased variance, the
+// same two-pass statistics as the LayerNorm kernel), formed while staging; the
+// contraction then fits one chunk (K <= kSkinnyChunk).
+template <int EPI, class T, bool LNX>
 __global__ __launch_bounds__(64 * kSkinnyWaves) void gemm_skinny_kernel(GP p) {
     constexpr int E = 16 / sizeof(T);  // elements per 16-byte load
     __shared__ __attribute__((aligned(16))) T xs[kSkinnyRows * kSkinnyChunk];
     const int M = (int)p.M, K = p.K, N = p.N;
-    const T* X = (const T*)p.A;
     const T* W = (const T*)p.B;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int n = blockIdx.x * kSkinnyWaves + wave;
@@ -747,24 +753,109 @@ __global__ __launch_bounds__(64 * kSkinnyWaves) void gemm_skinny_kernel(GP p) {
     float acc[kSkinnyRows];
 #pragma unroll
     for (int m = 0; m < kSkinnyRows; ++m) acc[m] = 0.0f;
+    // Loads are issued all together before their results are used (the weight
+    // row's piece first, then every 16-byte piece of X this thread stages), so a
+    // chunk costs about one memory round trip rather than one per piece.
+    constexpr int NWR = kSkinnyChunk / (64 * E);                               // weight pieces per lane
+    constexpr int NXR = kSkinnyRows * kSkinnyChunk / (64 * kSkinnyWaves * E);  // X pieces per thread
     for (int kc = 0; kc < K; kc += kSkinnyChunk) {
         const int kn = min(kSkinnyChunk, K - kc);
-        __syncthreads();  // the previous chunk is no longer read
-        for (int i = threadIdx.x * E; i < M * kn; i += 64 * kSkinnyWaves * E) {
-            const int m = i / kn, k = i - m * kn;  // kn is a multiple of E
-            *(uint4*)(xs + m * kSkinnyChunk + k) = *(const uint4*)(X + (int64_t)m * p.lda + kc + k);
+        uint4 wv[NWR];
+#pragma unroll
+        for (int r = 0; r < NWR; ++r) {
+            const int k = (lane + 64 * r) * E;
+            wv[r] = k < kn ? *(const uint4*)(wr + kc + k) : make_uint4(0, 0, 0, 0);
         }
-        __syncthreads();
-        for (int k = lane * E; k < kn; k += 64 * E) {
-            float w[E];
-            skinny_unpack<E>(*(const uint4*)(wr + kc + k), w);
+        if constexpr (LNX) {
+            // wave w normalises rows w, w + 4, w + 8, w + 12: every row's float4
+            // pieces are loaded up front (one round trip), then mean, variance
+            // about it and the normalised row come from registers
+            constexpr int RPW = kSkinnyRows / kSkinnyWaves;  // rows per wave
+            constexpr int NJ = kSkinnyChunk / 256;           // float4 pieces per lane per row
+            const float4* Xf = (const float4*)p.A;
+            const int K4 = K / 4;
+            float4 v[RPW][NJ];
 #pragma unroll
-            for (int m = 0; m < kSkinnyRows; ++m) {
-                if (m < M) {
-                    float x[E];
-                    skinny_unpack<E>(*(const uint4*)(xs + m * kSkinnyChunk + k), x);
+            for (int ri = 0; ri < RPW; ++ri) {
+                const int m = wave + kSkinnyWaves * ri;
 #pragma unroll
-                    for (int e = 0; e < E; ++e) acc[m] = fmaf(w[e], x[e], acc[m]);
+                for (int j = 0; j < NJ; ++j) {
+                    const int c4 = lane + 64 * j;
+                    v[ri][j] = m < M && c4 < K4 ? Xf[(int64_t)m * (p.lda / 4) + c4] : make_float4(0.f, 0.f, 0.f, 0.f);
+                }
+            }
+#pragma unroll
+            for (int ri = 0; ri < RPW; ++ri) {
+                const int m = wave + kSkinnyWaves * ri;
+                if (m >= M) continue;  // uniform across the wave
+                float sum = 0.0f;
+#pragma unroll
+                for (int j = 0; j < NJ; ++j) sum += (v[ri][j].x + v[ri][j].y) + (v[ri][j].z + v[ri][j].w);
+#pragma unroll
+                for (int off = 32; off > 0; off >>= 1) sum += __shfl_xor(sum, off, 64);
+                const float mu = sum / (float)K;
+                float q = 0.0f;
+#pragma unroll
+                for (int j = 0; j < NJ; ++j) {
+                    if (lane + 64 * j < K4) {
+                        const float a = v[ri][j].x - mu, b = v[ri][j].y - mu, c = v[ri][j].z - mu, d = v[ri][j].w - mu;
+                        q += (a * a + b * b) + (c * c + d * d);
+                    }
+                }
+#pragma unroll
+                for (int off = 32; off > 0; off >>= 1) q += __shfl_xor(q, off, 64);
+                const float rs = 1.0f / sqrtf(q / (float)K + p.ln_eps);
+#pragma unroll
+                for (int j = 0; j < NJ; ++j) {
+                    const int c4 = lane + 64 * j;
+                    if (c4 < K4) {
+                        const float4 gg = ((const float4*)p.ln_g)[c4], bb = ((const float4*)p.ln_b)[c4];
+                        const int o = m * kSkinnyChunk + 4 * c4;
+                        Act<T>::st(xs, o + 0, (v[ri][j].x - mu) * rs * gg.x + bb.x);
+                        Act<T>::st(xs, o + 1, (v[ri][j].y - mu) * rs * gg.y + bb.y);
+                        Act<T>::st(xs, o + 2, (v[ri][j].z - mu) * rs * gg.z + bb.z);
+                        Act<T>::st(xs, o + 3, (v[ri][j].w - mu) * rs * gg.w + bb.w);
+                    }
+                }
+            }
+            __syncthreads();
+        } else {
+            const T* X = (const T*)p.A;
+            uint4 xv[NXR];
+#pragma unroll
+            for (int r = 0; r < NXR; ++r) {
+                const int i = (threadIdx.x + 64 * kSkinnyWaves * r) * E;
+                xv[r] = make_uint4(0, 0, 0, 0);
+                if (i < M * kn) {
+                    const int m = i / kn, k = i - m * kn;  // kn is a multiple of E
+                    xv[r] = *(const uint4*)(X + (int64_t)m * p.lda + kc + k);
+                }
+            }
+            __syncthreads();  // the previous chunk is no longer read
+#pragma unroll
+            for (int r = 0; r < NXR; ++r) {
+                const int i = (threadIdx.x + 64 * kSkinnyWaves * r) * E;
+                if (i < M * kn) {
+                    const int m = i / kn, k = i - m * kn;
+                    *(uint4*)(xs + m * kSkinnyChunk + k) = xv[r];
+                }
+            }
+            __syncthreads();
+        }
+#pragma unroll
+        for (int r = 0; r < NWR; ++r) {
+            const int k = (lane + 64 * r) * E;
+            if (k < kn) {
+                float w[E];
+                skinny_unpack<E>(wv[r], w);
+#pragma unroll
+                for (int m = 0; m < kSkinnyRows; ++m) {
+                    if (m < M) {
+                        float xx[E];
+                        skinny_unpack<E>(*(const uint4*)(xs + m * kSkinnyChunk + k), xx);
+#pragma unroll
+                        for (int e = 0; e < E; ++e) acc[m] = fmaf(w[e], xx[e], acc[m]);
+                    }
                 }
             }
         }
@@ -783,13 +874,13 @@ __global__ __launch_bounds__(64 * kSkinnyWaves) void gemm_skinny_kernel(GP p) {
     if (n < N && lane < M) epi_apply<EPI, T>(p, lane, n, v);
 }
 
-template <int EPI>
+template <int EPI, bool LNX>
 static hipError_t launch_skinny(int dtype, const GP& p, hipStream_t s) {
     const dim3 grid((unsigned)((p.N + kSkinnyWaves - 1) / kSkinnyWaves));
     if (dtype == GPT2_DTYPE_BF16)
-        hipLaunchKernelGGL((gemm_skinny_kernel<EPI, bf16_t>), grid, dim3(64 * kSkinnyWaves), 0, s, p);
+        hipLaunchKernelGGL((gemm_skinny_kernel<EPI, bf16_t, LNX>), grid, dim3(64 * kSkinnyWaves), 0, s, p);
     else
-        hipLaunchKernelGGL((gemm_skinny_kernel<EPI, float>), grid, dim3(64 * kSkinnyWaves), 0, s, p);
+        hipLaunchKernelGGL((gemm_skinny_kernel<EPI, float, LNX>), grid, dim3(64 * kSkinnyWaves), 0, s, p);
     return hipGetLastError();
 }
 
@@ -977,6 +1068,9 @@ hipError_t gemm(int dtype, const GemmArgs& a, hipStream_t s) {
     p.accumulate = a.accumulate;
     p.gelu_erf = a.gelu_erf;
     p.cpart = a.epi == EPI_GELU_BWD ? a.colsum_part : nullptr;
+    p.ln_g = a.ln_g;
+    p.ln_b = a.ln_b;
+    p.ln_eps = a.ln_eps;
     if (a.M <= 0 || a.N <= 0) return hipSuccess;
     if (a.K <= 0) {
         // empty contraction: the product is zero
@@ -984,12 +1078,22 @@ hipError_t gemm(int dtype, const GemmArgs& a, hipStream_t s) {
         p.K = 0;
     }
     const bool kc11 = a.a_kc && a.b_kc, kc10 = a.a_kc && !a.b_kc, kc00 = !a.a_kc && !a.b_kc;
+    if (a.ln_g) {
+        // LayerNorm folded into a skinny product only (fp32 A rows, one chunk)
+        if (!kc11 || !a.ln_b || a.K > kSkinnyChunk || !skinny_ok(GPT2_DTYPE_F32, a) || (a.K % 8) != 0)
+            return hipErrorInvalidValue;
+        switch (a.epi) {
+            case EPI_STORE: return launch_skinny<EPI_STORE, true>(dtype, p, s);
+            case EPI_GELU: return launch_skinny<EPI_GELU, true>(dtype, p, s);
+            default: return hipErrorInvalidValue;
+        }
+    }
     if (kc11 && skinny_ok(dtype, a)) {
         switch (a.epi) {
-            case EPI_STORE: return launch_skinny<EPI_STORE>(dtype, p, s);
-            case EPI_GELU: return launch_skinny<EPI_GELU>(dtype, p, s);
-            case EPI_RESID: return launch_skinny<EPI_RESID>(dtype, p, s);
-            case EPI_F32: return launch_skinny<EPI_F32>(dtype, p, s);
+            case EPI_STORE: return launch_skinny<EPI_STORE, false>(dtype, p, s);
+            case EPI_GELU: return launch_skinny<EPI_GELU, false>(dtype, p, s);
+            case EPI_RESID: return launch_skinny<EPI_RESID, false>(dtype, p, s);
+            case EPI_F32: return launch_skinny<EPI_F32, false>(dtype, p, s);
         }
     }
     if (kc11) {

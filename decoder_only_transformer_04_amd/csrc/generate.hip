@@ -15,9 +15,23 @@
 namespace g2 {
 namespace {
 
-__global__ void gen_embed_kernel(const int32_t* seq, int64_t seq_ld, int col, const float* wte, const float* wpe,
-                                 int pos, float* x, int C, int V, uint32_t* status) {
+// The position of a step lives in device memory, cp[0] = sequence column of the
+// token fed, cp[1] = its model position, cp[2] = prompt length, so one captured
+// graph of a step serves every step: its last node moves the column and position on.
+__global__ void gen_set_kernel(int32_t* cp, int col, int pos, int T0) {
+    cp[0] = col;
+    cp[1] = pos;
+    cp[2] = T0;
+}
+__global__ void gen_advance_kernel(int32_t* cp) {
+    cp[0] += 1;
+    cp[1] += 1;
+}
+
+__global__ void gen_embed_kernel(const int32_t* seq, int64_t seq_ld, const int32_t* cp, const float* wte,
+                                 const float* wpe, float* x, int C, int V, uint32_t* status) {
     const int b = blockIdx.x;
+    const int col = cp[0], pos = cp[1];
     int tok = seq[(int64_t)b * seq_ld + col];
     if (tok < 0 || tok >= V) {
         if (threadIdx.x == 0) atomicOr(status, (uint32_t)GPT2_STATUS_TOKEN_RANGE);
@@ -36,9 +50,11 @@ constexpr int kAttThreads = 256;
 // their sum; the output sums p_j v_j with each thread owning one dimension of
 // one of 256 / d interleaved slices of the positions, reduced in fixed order.
 template <class T>
-__global__ __launch_bounds__(kAttThreads) void gen_attn_kernel(const T* qkv, T* kc, T* vc, int Tc, int pos, T* out,
-                                                               int C, int H, float scale) {
+__global__ __launch_bounds__(kAttThreads) void gen_attn_kernel(const T* qkv, T* kc, T* vc, int Tc, const int32_t* cp,
+                                                               T* out, int C, int H, float scale) {
     extern __shared__ float sm[];  // scores[Tc] | q[d] | partial outputs[kAttThreads] | reduction[kAttThreads]
+    const int pos = cp[1];
+    if (pos < 0 || pos >= Tc) return;  // the host keeps the window inside the cache
     const int b = blockIdx.x / H, h = blockIdx.x % H;
     const int d = C / H;
     const int tid = threadIdx.x;
@@ -110,7 +126,9 @@ constexpr int kSampleThreads = 1024;
 // token whose running sum exceeds it.
 __global__ __launch_bounds__(kSampleThreads) void gen_sample_kernel(const float* logits, int Vp, int V,
                                                                     float inv_temp, const float* u, int64_t u_ld,
-                                                                    int ucol, int32_t* seq, int64_t seq_ld, int col) {
+                                                                    const int32_t* cp, int32_t* seq, int64_t seq_ld) {
+    // the new token goes after the last one fed; it is new token number col + 1 - T0
+    const int col = cp[0] + 1, ucol = cp[0] + 1 - cp[2];
     __shared__ float red[kSampleThreads];
     __shared__ float scan[kSampleThreads + 1];
     __shared__ int pick;
@@ -130,12 +148,30 @@ __global__ __launch_bounds__(kSampleThreads) void gen_sample_kernel(const float*
     mx = red[0];
     float s = 0.0f;
     for (int k = lo; k < hi; ++k) s += __expf((z[k] - mx) * inv_temp);
-    scan[tid + 1] = s;
-    __syncthreads();
-    if (tid == 0) {  // exclusive prefix of the chunk sums, in index order
-        scan[0] = 0.0f;
-        for (int t = 1; t <= kSampleThreads; ++t) scan[t] += scan[t - 1];
+    // prefix sums of the chunk sums in index order: within each wave by shuffles,
+    // then the wave totals (one wave scans them), then each wave's offset added
+    const int lane = tid & 63, wv = tid >> 6;
+    float inc = s;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const float t = __shfl_up(inc, off, 64);
+        if (lane >= off) inc += t;
     }
+    __shared__ float wsum[kSampleThreads / 64];
+    if (lane == 63) wsum[wv] = inc;
+    __syncthreads();
+    if (wv == 0) {
+        float w = lane < kSampleThreads / 64 ? wsum[lane] : 0.0f;
+#pragma unroll
+        for (int off = 1; off < kSampleThreads / 64; off <<= 1) {
+            const float t = __shfl_up(w, off, 64);
+            if (lane >= off) w += t;
+        }
+        if (lane < kSampleThreads / 64) wsum[lane] = w;  // inclusive prefix of the wave totals
+    }
+    __syncthreads();
+    scan[tid + 1] = inc + (wv > 0 ? wsum[wv - 1] : 0.0f);
+    if (tid == 0) scan[0] = 0.0f;
     __syncthreads();
     const float target = u[(int64_t)b * u_ld + ucol] * scan[kSampleThreads];
     if (target >= scan[tid] && target < scan[tid + 1]) {
@@ -160,31 +196,41 @@ __global__ __launch_bounds__(kSampleThreads) void gen_sample_kernel(const float*
 
 }  // namespace
 
-hipError_t gen_embed(const int32_t* seq, int64_t seq_ld, int col, const float* wte, const float* wpe, int pos,
-                     float* x, int B, int C, int V, uint32_t* status, hipStream_t s) {
-    hipLaunchKernelGGL(gen_embed_kernel, dim3(B), dim3(256), 0, s, seq, seq_ld, col, wte, wpe, pos, x, C, V, status);
+hipError_t gen_set(int32_t* cp, int col, int pos, int T0, hipStream_t s) {
+    hipLaunchKernelGGL(gen_set_kernel, dim3(1), dim3(1), 0, s, cp, col, pos, T0);
     return hipGetLastError();
 }
 
-hipError_t gen_attention(int dtype, const void* qkv, void* kc, void* vc, int Tc, int pos, void* out, int B, int C,
-                         int H, hipStream_t s) {
+hipError_t gen_advance(int32_t* cp, hipStream_t s) {
+    hipLaunchKernelGGL(gen_advance_kernel, dim3(1), dim3(1), 0, s, cp);
+    return hipGetLastError();
+}
+
+hipError_t gen_embed(const int32_t* seq, int64_t seq_ld, const int32_t* cp, const float* wte, const float* wpe,
+                     float* x, int B, int C, int V, uint32_t* status, hipStream_t s) {
+    hipLaunchKernelGGL(gen_embed_kernel, dim3(B), dim3(256), 0, s, seq, seq_ld, cp, wte, wpe, x, C, V, status);
+    return hipGetLastError();
+}
+
+hipError_t gen_attention(int dtype, const void* qkv, void* kc, void* vc, int Tc, const int32_t* cp, void* out, int B,
+                         int C, int H, hipStream_t s) {
     const int d = C / H;
-    if (d > 128 || pos < 0 || pos >= Tc || Tc > kGenMaxCache) return hipErrorInvalidValue;
+    if (d > 128 || Tc > kGenMaxCache) return hipErrorInvalidValue;
     const size_t lds = (size_t)(Tc + d + 2 * kAttThreads) * sizeof(float);
     const float scale = 1.0f / sqrtf((float)d);
     if (dtype == GPT2_DTYPE_BF16)
         hipLaunchKernelGGL(gen_attn_kernel<bf16_t>, dim3(B * H), dim3(kAttThreads), lds, s, (const bf16_t*)qkv,
-                           (bf16_t*)kc, (bf16_t*)vc, Tc, pos, (bf16_t*)out, C, H, scale);
+                           (bf16_t*)kc, (bf16_t*)vc, Tc, cp, (bf16_t*)out, C, H, scale);
     else
         hipLaunchKernelGGL(gen_attn_kernel<float>, dim3(B * H), dim3(kAttThreads), lds, s, (const float*)qkv,
-                           (float*)kc, (float*)vc, Tc, pos, (float*)out, C, H, scale);
+                           (float*)kc, (float*)vc, Tc, cp, (float*)out, C, H, scale);
     return hipGetLastError();
 }
 
-hipError_t gen_sample(const float* logits, int Vp, int V, float temperature, const float* u, int64_t u_ld, int ucol,
-                      int32_t* seq, int64_t seq_ld, int col, int B, hipStream_t s) {
+hipError_t gen_sample(const float* logits, int Vp, int V, float temperature, const float* u, int64_t u_ld,
+                      const int32_t* cp, int32_t* seq, int64_t seq_ld, int B, hipStream_t s) {
     hipLaunchKernelGGL(gen_sample_kernel, dim3(B), dim3(kSampleThreads), 0, s, logits, Vp, V, 1.0f / temperature, u,
-                       u_ld, ucol, seq, seq_ld, col);
+                       u_ld, cp, seq, seq_ld);
     return hipGetLastError();
 }
 

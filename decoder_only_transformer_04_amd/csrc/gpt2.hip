@@ -27,6 +27,11 @@ struct gpt2_ctx {
     // `stream` with the events below; null when everything runs on `stream`
     hipStream_t wstream = nullptr;
     std::vector<hipEvent_t> wev;
+    // generation: capture stream and the two captured position steps (without,
+    // with the head and the draw) of the last gpt2_generate call
+    hipStream_t gstream = nullptr;
+    hipGraph_t ggraph[2] = {nullptr, nullptr};
+    hipGraphExec_t gexec[2] = {nullptr, nullptr};
     char* arena;
     bool have_dz;   // a TRAIN forward with targets wrote the logits gradient
     bool have_idx;  // token ids of the last forward saved for the embedding backward
@@ -204,9 +209,9 @@ GemmArgs gemm_args() {
     return a;
 }
 
-// Y[M,N] = X[M,K] W[N,K]^T with an epilogue
-hipError_t linear_fwd(gpt2_ctx* x, int epi, int64_t M, int N, int K, const void* X, const void* W, const float* bias,
-                      void* Y, void* Y2, const void* R) {
+// Y[M,N] = X[M,K] W[N,K]^T with an epilogue, on stream s
+hipError_t linear_fwd_on(gpt2_ctx* x, hipStream_t s, int epi, int64_t M, int N, int K, const void* X, const void* W,
+                         const float* bias, void* Y, void* Y2, const void* R) {
     GemmArgs a = gemm_args();
     a.M = M; a.N = N; a.K = K;
     a.A = X; a.lda = K; a.a_kc = true;
@@ -216,7 +221,26 @@ hipError_t linear_fwd(gpt2_ctx* x, int epi, int64_t M, int N, int K, const void*
     a.C2 = Y2; a.ldc2 = N;
     a.R = R; a.ldr = N;
     a.gelu_erf = x->cfg.gelu_erf;
-    return gemm(x->cfg.dtype, a, x->stream);
+    return gemm(x->cfg.dtype, a, s);
+}
+hipError_t linear_fwd(gpt2_ctx* x, int epi, int64_t M, int N, int K, const void* X, const void* W, const float* bias,
+                      void* Y, void* Y2, const void* R) {
+    return linear_fwd_on(x, x->stream, epi, M, N, K, X, W, bias, Y, Y2, R);
+}
+// Y = LayerNorm(X; g, b) W^T with an epilogue, X fp32, for a few rows (the
+// skinny product forms the LayerNorm while staging X)
+hipError_t linear_fwd_ln(gpt2_ctx* x, hipStream_t s, int epi, int64_t M, int N, int K, const float* X, const float* g,
+                         const float* b, const void* W, const float* bias, void* Y, void* Y2) {
+    GemmArgs a = gemm_args();
+    a.M = M; a.N = N; a.K = K;
+    a.A = X; a.lda = K; a.a_kc = true;
+    a.B = W; a.ldb = K; a.b_kc = true;
+    a.epi = epi; a.bias = bias;
+    a.C = Y; a.ldc = N;
+    a.C2 = Y2; a.ldc2 = N;
+    a.gelu_erf = x->cfg.gelu_erf;
+    a.ln_g = g; a.ln_b = b; a.ln_eps = x->cfg.ln_eps;
+    return gemm(x->cfg.dtype, a, s);
 }
 
 // dX[M,K] = dY[M,N] W[N,K] (epilogue epi, alpha), with optional GELU' operand R
@@ -366,6 +390,11 @@ int gpt2_init(gpt2_ctx** out, const gpt2_config* cfg, const gpt2_buffers* bufs, 
             return GPT2_EHIP;
         }
     }
+    if (x->ap.mode == GPT2_MODE_GENERATE &&
+        hipStreamCreateWithFlags(&x->gstream, hipStreamNonBlocking) != hipSuccess) {
+        gpt2_destroy(x);
+        return GPT2_EHIP;
+    }
     int r = gpt2_refresh_weights(x);
     if (r) {
         gpt2_destroy(x);
@@ -382,9 +411,14 @@ int gpt2_refresh_weights(gpt2_ctx* x) {
     return GPT2_OK;
 }
 
+static void gen_release(gpt2_ctx* x);
+
 void gpt2_destroy(gpt2_ctx* x) {
     if (!x) return;
     if (x->wstream) (void)hipStreamSynchronize(x->wstream);
+    if (x->gexec[0] || x->gexec[1]) (void)hipStreamSynchronize(x->stream);
+    gen_release(x);
+    if (x->gstream) (void)hipStreamDestroy(x->gstream);
     for (hipEvent_t e : x->ev_pool) (void)hipEventDestroy(e);
     for (hipEvent_t e : x->wev) (void)hipEventDestroy(e);
     if (x->wstream) (void)hipStreamDestroy(x->wstream);
@@ -628,44 +662,91 @@ int gpt2_adamw_step(gpt2_ctx* x, float lr, float beta1, float beta2, float eps, 
     return GPT2_OK;
 }
 
-// One position of the B sequences through the model (generation): the token in
-// column `col` of each row of seq at model position `pos`, its keys and values
-// appended to the caches at `pos`; with `head`, the final LayerNorm and the head
-// leave fp32 logits [B, Vp] for the sampler.
-static int gen_position(gpt2_ctx* x, const int32_t* seq, int64_t seq_ld, int col, int pos, bool head) {
+// One position of the B sequences through the model (generation), on stream s:
+// the token in column cp[0] of each row of seq at model position cp[1] (device
+// state, see gen_set), its keys and values appended to the caches; with `head`,
+// the final LayerNorm and the head leave fp32 logits [B, Vp] and the sampler
+// writes the next token. Ends by moving the state on by one position.
+static int gen_position(gpt2_ctx* x, hipStream_t s, int32_t* seq, int64_t seq_ld, bool head, float temperature,
+                        const float* u, int64_t u_ld) {
     const gpt2_config& c = x->cfg;
     const ArenaPlan& ap = x->ap;
     const int B = ap.B, C = c.n_embd, F = c.mlp_hidden, H = c.n_head;
     const int Vp = (int)x->pl.vocab_pad;
     const int dt = c.dtype;
-    hipStream_t s = x->stream;
+    int32_t* cp = at<int32_t>(x, ap.scalars) + SLOT_GEN;
     float* xr = at<float>(x, ap.x[0]);
     float* xmid = at<float>(x, ap.xmid[0]);
-    G2_T("gen.embed", gen_embed(seq, seq_ld, col, pf(x, x->pl.wte), pf(x, x->pl.wpe), pos, xr, B, C, c.vocab,
-                                status_ptr(x), s));
+    G2_TS("gen.embed", s, gen_embed(seq, seq_ld, cp, pf(x, x->pl.wte), pf(x, x->pl.wpe), xr, B, C, c.vocab,
+                                    status_ptr(x), s));
+    // the LayerNorms that feed a product fold into it when the skinny kernel
+    // takes it (few rows, C within one staging chunk)
+    const bool fuse_ln = B <= 16 && C <= 1024 && C % 8 == 0 && 3 * C < 8192 && F < 8192;
     for (int l = 0; l < c.n_layer; ++l) {
         const LayerW& w = x->pl.layer[l];
-        G2_T("gen.ln", layernorm_fwd(dt, xr, pf(x, w.ln1_g), pf(x, w.ln1_b), c.ln_eps, at<char>(x, ap.ln1[0]),
-                                     at<float>(x, ap.m1[0]), at<float>(x, ap.r1[0]), B, C, s));
-        G2_T("gen.gemm", linear_fwd(x, EPI_STORE, B, 3 * C, C, at<char>(x, ap.ln1[0]), wptr(x, w.w_qkv), pf(x, w.b_qkv),
-                                    at<char>(x, ap.qkv[0]), nullptr, nullptr));
-        G2_T("gen.attn", gen_attention(dt, at<char>(x, ap.qkv[0]), at<char>(x, ap.kc[l]), at<char>(x, ap.vc[l]), ap.T, pos,
-                                       at<char>(x, ap.att[0]), B, C, H, s));
-        G2_T("gen.gemm", linear_fwd(x, EPI_RESID, B, C, C, at<char>(x, ap.att[0]), wptr(x, w.w_proj), pf(x, w.b_proj), xmid,
-                                    nullptr, xr));
-        G2_T("gen.ln", layernorm_fwd(dt, xmid, pf(x, w.ln2_g), pf(x, w.ln2_b), c.ln_eps, at<char>(x, ap.ln2[0]),
-                                     at<float>(x, ap.m2[0]), at<float>(x, ap.r2[0]), B, C, s));
-        G2_T("gen.gemm", linear_fwd(x, EPI_GELU, B, F, C, at<char>(x, ap.ln2[0]), wptr(x, w.w_fc), pf(x, w.b_fc),
-                                    at<char>(x, ap.fch[0]), at<char>(x, ap.fcg[0]), nullptr));
-        G2_T("gen.gemm", linear_fwd(x, EPI_RESID, B, C, F, at<char>(x, ap.fcg[0]), wptr(x, w.w_fc2), pf(x, w.b_fc2), xr,
-                                    nullptr, xmid));
+        if (fuse_ln) {
+            G2_TS("gen.gemm", s, linear_fwd_ln(x, s, EPI_STORE, B, 3 * C, C, xr, pf(x, w.ln1_g), pf(x, w.ln1_b),
+                                               wptr(x, w.w_qkv), pf(x, w.b_qkv), at<char>(x, ap.qkv[0]), nullptr));
+        } else {
+            G2_TS("gen.ln", s, layernorm_fwd(dt, xr, pf(x, w.ln1_g), pf(x, w.ln1_b), c.ln_eps, at<char>(x, ap.ln1[0]),
+                                             at<float>(x, ap.m1[0]), at<float>(x, ap.r1[0]), B, C, s));
+            G2_TS("gen.gemm", s, linear_fwd_on(x, s, EPI_STORE, B, 3 * C, C, at<char>(x, ap.ln1[0]), wptr(x, w.w_qkv),
+                                               pf(x, w.b_qkv), at<char>(x, ap.qkv[0]), nullptr, nullptr));
+        }
+        G2_TS("gen.attn", s, gen_attention(dt, at<char>(x, ap.qkv[0]), at<char>(x, ap.kc[l]), at<char>(x, ap.vc[l]),
+                                           ap.T, cp, at<char>(x, ap.att[0]), B, C, H, s));
+        G2_TS("gen.gemm", s, linear_fwd_on(x, s, EPI_RESID, B, C, C, at<char>(x, ap.att[0]), wptr(x, w.w_proj),
+                                           pf(x, w.b_proj), xmid, nullptr, xr));
+        if (fuse_ln) {
+            G2_TS("gen.gemm", s, linear_fwd_ln(x, s, EPI_GELU, B, F, C, xmid, pf(x, w.ln2_g), pf(x, w.ln2_b),
+                                               wptr(x, w.w_fc), pf(x, w.b_fc), at<char>(x, ap.fch[0]),
+                                               at<char>(x, ap.fcg[0])));
+        } else {
+            G2_TS("gen.ln", s, layernorm_fwd(dt, xmid, pf(x, w.ln2_g), pf(x, w.ln2_b), c.ln_eps, at<char>(x, ap.ln2[0]),
+                                             at<float>(x, ap.m2[0]), at<float>(x, ap.r2[0]), B, C, s));
+            G2_TS("gen.gemm", s, linear_fwd_on(x, s, EPI_GELU, B, F, C, at<char>(x, ap.ln2[0]), wptr(x, w.w_fc),
+                                               pf(x, w.b_fc), at<char>(x, ap.fch[0]), at<char>(x, ap.fcg[0]), nullptr));
+        }
+        G2_TS("gen.gemm", s, linear_fwd_on(x, s, EPI_RESID, B, C, F, at<char>(x, ap.fcg[0]), wptr(x, w.w_fc2),
+                                           pf(x, w.b_fc2), xr, nullptr, xmid));
     }
-    if (!head) return GPT2_OK;
-    G2_T("gen.ln", layernorm_fwd(dt, xr, pf(x, x->pl.lnf_g), pf(x, x->pl.lnf_b), c.ln_eps, at<char>(x, ap.xf),
-                                 at<float>(x, ap.mf), at<float>(x, ap.rf), B, C, s));
-    G2_T("gen.head", linear_fwd(x, EPI_F32, B, Vp, C, at<char>(x, ap.xf), wptr(x, x->pl.lm_head), nullptr,
-                                at<float>(x, ap.logits), nullptr, nullptr));
+    if (head) {
+        G2_TS("gen.ln", s, layernorm_fwd(dt, xr, pf(x, x->pl.lnf_g), pf(x, x->pl.lnf_b), c.ln_eps, at<char>(x, ap.xf),
+                                         at<float>(x, ap.mf), at<float>(x, ap.rf), B, C, s));
+        G2_TS("gen.head", s, linear_fwd_on(x, s, EPI_F32, B, Vp, C, at<char>(x, ap.xf), wptr(x, x->pl.lm_head), nullptr,
+                                           at<float>(x, ap.logits), nullptr, nullptr));
+        G2_TS("gen.sample", s, gen_sample(at<float>(x, ap.logits), Vp, c.vocab, temperature, u, u_ld, cp, seq, seq_ld,
+                                          B, s));
+    }
+    G2_TRY(gen_advance(cp, s));
     return GPT2_OK;
+}
+
+// The two kinds of position step captured as graphs on the capture stream (a
+// step is ~85 small launches; replayed, their launch overhead mostly goes).
+static int gen_capture(gpt2_ctx* x, int32_t* seq, int64_t seq_ld, float temperature, const float* u, int64_t u_ld) {
+    for (int k = 0; k < 2; ++k) {
+        hipGraph_t g = nullptr;
+        G2_TRY(hipStreamBeginCapture(x->gstream, hipStreamCaptureModeThreadLocal));
+        const int e = gen_position(x, x->gstream, seq, seq_ld, k == 1, temperature, u, u_ld);
+        const hipError_t ee = hipStreamEndCapture(x->gstream, &g);
+        if (e || ee != hipSuccess) {
+            if (g) (void)hipGraphDestroy(g);
+            return e ? e : GPT2_EHIP;
+        }
+        x->ggraph[k] = g;
+        G2_TRY(hipGraphInstantiate(&x->gexec[k], g, nullptr, nullptr, 0));
+    }
+    return GPT2_OK;
+}
+
+static void gen_release(gpt2_ctx* x) {
+    for (int k = 0; k < 2; ++k) {
+        if (x->gexec[k]) (void)hipGraphExecDestroy(x->gexec[k]);
+        if (x->ggraph[k]) (void)hipGraphDestroy(x->ggraph[k]);
+        x->gexec[k] = nullptr;
+        x->ggraph[k] = nullptr;
+    }
 }
 
 int gpt2_generate(gpt2_ctx* x, const int32_t* d_prompt, int32_t T0, int32_t n_new, float temperature,
@@ -674,10 +755,26 @@ int gpt2_generate(gpt2_ctx* x, const int32_t* d_prompt, int32_t T0, int32_t n_ne
     if (!(temperature > 0.0f) || !std::isfinite(temperature)) return GPT2_EINVAL;
     if (x->ap.mode != GPT2_MODE_GENERATE) return GPT2_ESTATE;
     if ((int64_t)T0 + n_new > INT32_MAX) return GPT2_EINVAL;
-    const int B = x->ap.B, bs = x->cfg.block_size, Vp = (int)x->pl.vocab_pad;
+    const int B = x->ap.B, bs = x->cfg.block_size;
     const int64_t len = (int64_t)T0 + n_new;  // row length of d_out
     hipStream_t s = x->stream;
+    int32_t* cp = at<int32_t>(x, x->ap.scalars) + SLOT_GEN;
     G2_TRY(hipMemcpy2DAsync(d_out, len * 4, d_prompt, (size_t)T0 * 4, (size_t)T0 * 4, B, hipMemcpyDeviceToDevice, s));
+    if (n_new == 0) return GPT2_OK;
+    // graphs of the previous call: released once their replays have finished
+    if (x->gexec[0] || x->gexec[1]) {
+        G2_TRY(hipStreamSynchronize(s));
+        gen_release(x);
+    }
+    // per-label timing records events per launch: then the steps run unrolled
+    const bool graphs = !x->timing;
+    if (graphs) {
+        const int e = gen_capture(x, d_out, len, temperature, d_uniform, n_new);
+        if (e) {
+            gen_release(x);
+            return e;
+        }
+    }
     // The caches hold the window that starts at sequence column w_cached, with
     // `filled` positions so far. While the sequence fits in block_size the window
     // only grows, one position per new token; past it the window slides, every
@@ -689,15 +786,18 @@ int gpt2_generate(gpt2_ctx* x, const int32_t* d_prompt, int32_t T0, int32_t n_ne
         if (w0 != w_cached) {
             w_cached = w0;
             filled = 0;
+            G2_TRY(gen_set(cp, w0, 0, T0, s));
         }
         while (w0 + filled < n) {
-            const int col = w0 + filled;
-            const int e = gen_position(x, d_out, len, col, filled, col == n - 1);
-            if (e) return e;
+            const bool last = w0 + filled == n - 1;  // the step that draws token n
+            if (graphs) {
+                G2_TRY(hipGraphLaunch(x->gexec[last ? 1 : 0], s));
+            } else {
+                const int e = gen_position(x, s, d_out, len, last, temperature, d_uniform, n_new);
+                if (e) return e;
+            }
             ++filled;
         }
-        G2_T("gen.sample", gen_sample(at<float>(x, x->ap.logits), Vp, x->cfg.vocab, temperature, d_uniform, n_new, i,
-                                      d_out, len, n, B, s));
     }
     return GPT2_OK;
 }
