@@ -119,11 +119,13 @@ __global__ __launch_bounds__(kAttThreads) void gen_attn_kernel(const T* qkv, T* 
 }
 
 constexpr int kSampleThreads = 1024;
+constexpr int kSampleVec = 13;  // float4 pieces per thread: rows of up to 50k-odd logits (GPT-2: 50257)
 
 // One workgroup per row. Thread t owns the contiguous chunk [t * ch, (t + 1) * ch)
-// of the vocabulary; chunk sums of exp((z - max) / temperature) are scanned in
-// index order, and the thread whose chunk holds u * total walks it to the first
-// token whose running sum exceeds it.
+// of the vocabulary (ch a multiple of 4), loaded once into registers as float4
+// pieces; chunk sums of exp((z - max) / temperature) are scanned in index order,
+// and the thread whose chunk holds u * total walks it to the first token whose
+// running sum exceeds it.
 __global__ __launch_bounds__(kSampleThreads) void gen_sample_kernel(const float* logits, int Vp, int V,
                                                                     float inv_temp, const float* u, int64_t u_ld,
                                                                     const int32_t* cp, int32_t* seq, int64_t seq_ld) {
@@ -131,13 +133,24 @@ __global__ __launch_bounds__(kSampleThreads) void gen_sample_kernel(const float*
     const int col = cp[0] + 1, ucol = cp[0] + 1 - cp[2];
     __shared__ float red[kSampleThreads];
     __shared__ float scan[kSampleThreads + 1];
+    __shared__ float wsum[kSampleThreads / 64];
     __shared__ int pick;
     const int b = blockIdx.x, tid = threadIdx.x;
     const float* z = logits + (int64_t)b * Vp;
-    const int ch = (V + kSampleThreads - 1) / kSampleThreads;
+    const int ch = ((V + kSampleThreads - 1) / kSampleThreads + 3) / 4 * 4;
     const int lo = min(V, tid * ch), hi = min(V, lo + ch);
+    float zv[kSampleVec * 4];
+#pragma unroll
+    for (int j = 0; j < kSampleVec; ++j) {
+        const int k = lo + 4 * j;
+        // whole pieces inside the padded row (Vp is a multiple of 4); tokens >= V are not used
+        const float4 v = (4 * j < ch && k + 4 <= Vp) ? *(const float4*)(z + k) : make_float4(0.f, 0.f, 0.f, 0.f);
+        zv[4 * j] = v.x; zv[4 * j + 1] = v.y; zv[4 * j + 2] = v.z; zv[4 * j + 3] = v.w;
+    }
     float mx = -FLT_MAX;
-    for (int k = lo; k < hi; ++k) mx = fmaxf(mx, z[k]);
+#pragma unroll
+    for (int i = 0; i < kSampleVec * 4; ++i)
+        if (lo + i < hi) mx = fmaxf(mx, zv[i]);
     red[tid] = mx;
     if (tid == 0) pick = -1;
     __syncthreads();
@@ -147,7 +160,9 @@ __global__ __launch_bounds__(kSampleThreads) void gen_sample_kernel(const float*
     }
     mx = red[0];
     float s = 0.0f;
-    for (int k = lo; k < hi; ++k) s += __expf((z[k] - mx) * inv_temp);
+#pragma unroll
+    for (int i = 0; i < kSampleVec * 4; ++i)
+        if (lo + i < hi) s += __expf((zv[i] - mx) * inv_temp);
     // prefix sums of the chunk sums in index order: within each wave by shuffles,
     // then the wave totals (one wave scans them), then each wave's offset added
     const int lane = tid & 63, wv = tid >> 6;
@@ -157,7 +172,6 @@ __global__ __launch_bounds__(kSampleThreads) void gen_sample_kernel(const float*
         const float t = __shfl_up(inc, off, 64);
         if (lane >= off) inc += t;
     }
-    __shared__ float wsum[kSampleThreads / 64];
     if (lane == 63) wsum[wv] = inc;
     __syncthreads();
     if (wv == 0) {
@@ -175,13 +189,17 @@ __global__ __launch_bounds__(kSampleThreads) void gen_sample_kernel(const float*
     __syncthreads();
     const float target = u[(int64_t)b * u_ld + ucol] * scan[kSampleThreads];
     if (target >= scan[tid] && target < scan[tid + 1]) {
+        // one thread walks its chunk (the exponentials recomputed as summed above)
         float run = scan[tid];
-        int k = lo;
-        for (; k < hi; ++k) {
-            run += __expf((z[k] - mx) * inv_temp);
-            if (run > target) break;
+        int k = hi - 1;  // rounding can leave the walk just short of target: the chunk's last token
+        for (int i = lo; i < hi; ++i) {
+            run += __expf((z[i] - mx) * inv_temp);
+            if (run > target) {
+                k = i;
+                break;
+            }
         }
-        atomicMax(&pick, min(k, hi - 1));  // one chunk holds the target; max keeps it unique
+        atomicMax(&pick, k);  // one chunk holds the target; max keeps it unique
     }
     __syncthreads();
     if (tid == 0) {
@@ -229,6 +247,8 @@ hipError_t gen_attention(int dtype, const void* qkv, void* kc, void* vc, int Tc,
 
 hipError_t gen_sample(const float* logits, int Vp, int V, float temperature, const float* u, int64_t u_ld,
                       const int32_t* cp, int32_t* seq, int64_t seq_ld, int B, hipStream_t s) {
+    const int ch = ((V + kSampleThreads - 1) / kSampleThreads + 3) / 4 * 4;  // the kernel's chunk length
+    if (ch > 4 * kSampleVec || Vp % 4 != 0) return hipErrorInvalidValue;
     hipLaunchKernelGGL(gen_sample_kernel, dim3(B), dim3(kSampleThreads), 0, s, logits, Vp, V, 1.0f / temperature, u,
                        u_ld, cp, seq, seq_ld);
     return hipGetLastError();
