@@ -24,7 +24,11 @@ GELU_ERF, UNTIED = 1, 2  # variant bits: exact erf GELU, separate lm_head
 class OracleCfg(ct.Structure):
     _fields_ = [("vocab", ct.c_int32), ("block_size", ct.c_int32), ("n_embd", ct.c_int32),
                 ("n_head", ct.c_int32), ("n_layer", ct.c_int32), ("mlp_hidden", ct.c_int32),
-                ("bias", ct.c_int32), ("variant", ct.c_int32), ("ln_eps", ct.c_double)]
+                ("bias", ct.c_int32), ("variant", ct.c_int32), ("ln_eps", ct.c_double),
+                ("dropout", ct.c_double), ("seed", ct.c_uint64)]
+
+
+DROP_ATTN, DROP_PROJ, DROP_FC2 = 0, 1, 2  # dropout sites of a block
 
 
 _lib = None
@@ -64,6 +68,8 @@ def lib():
         L.oracle_lr.restype = dbl
         L.oracle_lr.argtypes = [i64, dbl, dbl, i64, i64]
         L.oracle_argmax_f32.argtypes = [i64, ct.c_int, P, P]
+        L.oracle_philox4x32_10.argtypes = [P, P, P]
+        L.oracle_dropout_keep.argtypes = [dbl, ct.c_uint64, ct.c_int, ct.c_int, ct.c_uint64, i64, P]
         L.oracle_set_threads.argtypes = [ct.c_int]
         L.oracle_max_threads.restype = ct.c_int
         _lib = L
@@ -84,9 +90,34 @@ def _dt(dtype):
 
 
 def make_cfg(vocab, block_size, n_embd, n_head, n_layer, mlp_hidden, bias, ln_eps=1e-5, gelu_erf=False,
-             untied=False):
+             untied=False, dropout=0.0, seed=0):
+    """dropout > 0: the training-mode model (step() applies dropout keyed by seed)."""
     variant = (GELU_ERF if gelu_erf else 0) | (UNTIED if untied else 0)
-    return OracleCfg(vocab, block_size, n_embd, n_head, n_layer, mlp_hidden, int(bias), variant, ln_eps)
+    return OracleCfg(vocab, block_size, n_embd, n_head, n_layer, mlp_hidden, int(bias), variant, ln_eps,
+                     float(dropout), int(seed))
+
+
+def eval_cfg(cfg: OracleCfg) -> OracleCfg:
+    """The same model in eval mode (model.eval(): no dropout)."""
+    c = OracleCfg.from_buffer_copy(cfg)
+    c.dropout = 0.0
+    return c
+
+
+def philox4x32_10(ctr, key) -> np.ndarray:
+    """Philox4x32-10 of one 4-word counter under a 2-word key (uint32)."""
+    c = np.ascontiguousarray(ctr, dtype=np.uint32)
+    k = np.ascontiguousarray(key, dtype=np.uint32)
+    out = np.zeros(4, dtype=np.uint32)
+    lib().oracle_philox4x32_10(_p(c), _p(k), _p(out))
+    return out
+
+
+def dropout_keep(p: float, seed: int, site: int, layer: int, n: int, e0: int = 0) -> np.ndarray:
+    """uint8 keep flags of elements e0 .. e0 + n - 1 of one dropout site."""
+    out = np.zeros(n, dtype=np.uint8)
+    lib().oracle_dropout_keep(float(p), int(seed), int(site), int(layer), int(e0), int(n), _p(out))
+    return out
 
 
 def set_threads(n: int) -> None:
@@ -163,7 +194,7 @@ def next_token_probs(cfg: OracleCfg, params_flat: np.ndarray, ctx: np.ndarray, t
     B, n = ctx.shape
     win = ctx[:, max(0, n - cfg.block_size):]
     T = win.shape[1]
-    _, logits, _ = step(cfg, B, T, params_flat, win, None, want_logits=True)
+    _, logits, _ = step(eval_cfg(cfg), B, T, params_flat, win, None, want_logits=True)
     z = logits.reshape(B, T, cfg.vocab)[:, -1, :].astype(np.float64) / temperature
     z -= z.max(axis=1, keepdims=True)
     e = np.exp(z)

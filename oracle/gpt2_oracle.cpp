@@ -41,15 +41,70 @@ typedef struct {
     int32_t bias;        // 1: Linear layers carry biases
     int32_t variant;     // bit 0: exact erf GELU; bit 1: untied lm_head (ORACLE_* below)
     double ln_eps;       // LayerNorm epsilon
+    double dropout;      // training-mode dropout probability p (0: none)
+    uint64_t seed;       // dropout stream key (see keep() below)
 } oracle_cfg;
 }
 
-// The minigpt page's literal model differs from the GPT-2 readings in two ways
+// The minigpt page's literal model differs from the GPT-2 readings in three ways
 // the oracle can follow on request: nn.GELU() with its default exact erf form,
-// and an lm_head Linear of its own instead of the tied embedding.
+// an lm_head Linear of its own instead of the tied embedding, and dropout
+// (cfg.dropout, three sites per block, see model_step).
 enum { ORACLE_GELU_ERF = 1, ORACLE_UNTIED = 2 };
 
+// Dropout sites of a block in minigpt.py: the attention weights after the
+// softmax (Head.forward), the attention projection's output
+// (MultiHeadAttention.forward) and the FeedForward's last Linear (its
+// nn.Dropout). Embeddings have none.
+enum { DROP_ATTN = 0, DROP_PROJ = 1, DROP_FC2 = 2 };
+
 namespace {
+
+// ---------------------------------------------------------------- dropout stream
+// Philox4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel random numbers: as easy
+// as 1, 2, 3", SC 2011): a 128-bit counter and a 64-bit key; each of ten rounds
+// multiplies words 0 and 2 by fixed 32-bit constants into 64-bit products and
+// rebuilds the four words from the product halves, the two other words and the
+// key, which is advanced by two Weyl constants between rounds.
+static void philox4x32_10(const uint32_t ctr[4], const uint32_t key[2], uint32_t out[4]) {
+    uint32_t x0 = ctr[0], x1 = ctr[1], x2 = ctr[2], x3 = ctr[3];
+    uint32_t k0 = key[0], k1 = key[1];
+    for (int round = 0; round < 10; ++round) {
+        const uint64_t p0 = (uint64_t)0xD2511F53u * x0;
+        const uint64_t p1 = (uint64_t)0xCD9E8D57u * x2;
+        const uint32_t n0 = (uint32_t)(p1 >> 32) ^ x1 ^ k0;
+        const uint32_t n1 = (uint32_t)p1;
+        const uint32_t n2 = (uint32_t)(p0 >> 32) ^ x3 ^ k1;
+        const uint32_t n3 = (uint32_t)p0;
+        x0 = n0; x1 = n1; x2 = n2; x3 = n3;
+        k0 += 0x9E3779B9u;
+        k1 += 0xBB67AE85u;
+    }
+    out[0] = x0; out[1] = x1; out[2] = x2; out[3] = x3;
+}
+
+// The keep decision for element e of a dropout site (nn.Dropout keeps each
+// element independently with probability 1 - p). The pages fix no generator;
+// the reading adopted: element e of site `site` in layer `layer` takes 16-bit
+// half (e mod 8) of Philox4x32-10 at counter (e / 8 low and high words, site,
+// layer) under key (seed low, seed high) -- halves numbered low then high
+// within words 0..3 -- and is kept when that half is at least
+// round(p * 65536). Element order: attention ((b H + h) T + i) T + j for query
+// i and key j of head h in sequence b; the residual sites m C + c.
+static uint32_t drop_threshold(double p) {
+    double t = std::floor(p * 65536.0 + 0.5);
+    return (uint32_t)std::min(t, 65536.0);
+}
+static bool keep(uint64_t seed, int site, int layer, uint64_t e, uint32_t thr) {
+    const uint64_t n = e >> 3;
+    const uint32_t ctr[4] = {(uint32_t)n, (uint32_t)(n >> 32), (uint32_t)site, (uint32_t)layer};
+    const uint32_t key[2] = {(uint32_t)seed, (uint32_t)(seed >> 32)};
+    uint32_t r[4];
+    philox4x32_10(ctr, key, r);
+    const int h = (int)(e & 7);
+    const uint32_t half = (h & 1) ? (r[h >> 1] >> 16) : (r[h >> 1] & 0xFFFFu);
+    return half >= thr;
+}
 
 // Tensor kinds of the oracle's own canonical layout.
 enum Kind {
@@ -97,6 +152,7 @@ static Layout make_layout(const oracle_cfg& c) {
 }
 
 static bool cfg_ok(const oracle_cfg& c) {
+    if (!(c.dropout >= 0.0 && c.dropout < 1.0)) return false;
     return c.vocab > 0 && c.block_size > 0 && c.n_embd > 0 && c.n_head > 0 &&
            c.n_layer >= 0 && c.mlp_hidden > 0 && c.n_embd % c.n_head == 0 &&
            (c.variant & ~(ORACLE_GELU_ERF | ORACLE_UNTIED)) == 0;
@@ -244,10 +300,12 @@ R gelu_grad(R u, bool erf_form = false) {
 // One causal head, the Head.forward of minigpt.py written out: scores
 // q_i.k_j / sqrt(d), -inf for j > i, softmax over j, out_i = sum_j P_ij v_j.
 // Rows of q, k, v, out are `stride` apart. P (T x T, may be null) receives the
-// probabilities with exact zeros above the diagonal.
+// probabilities with exact zeros above the diagonal. With `kp` (T x T keep
+// flags, may be null) the attention weights pass through dropout before they
+// weight the values: P_ij kp_ij / (1 - p), with dscale = 1 / (1 - p).
 template <class R>
 void head_fwd(int T, int d, const R* q, const R* k, const R* v, int64_t stride, R* out,
-              int64_t ostride, R* P, R* srow) {
+              int64_t ostride, R* P, R* srow, const uint8_t* kp = nullptr, R dscale = 1) {
     const R scale = (R)1 / std::sqrt((R)d);
     for (int i = 0; i < T; ++i) {
         R mx = -INFINITY;
@@ -263,8 +321,10 @@ void head_fwd(int T, int d, const R* q, const R* k, const R* v, int64_t stride, 
         for (int j = 0; j <= i; ++j) srow[j] /= sum;
         R* o = out + (int64_t)i * ostride;
         for (int c = 0; c < d; ++c) o[c] = 0;
-        for (int j = 0; j <= i; ++j)
-            for (int c = 0; c < d; ++c) o[c] += srow[j] * v[(int64_t)j * stride + c];
+        for (int j = 0; j <= i; ++j) {
+            const R w = kp ? (kp[(int64_t)i * T + j] ? srow[j] * dscale : (R)0) : srow[j];
+            for (int c = 0; c < d; ++c) o[c] += w * v[(int64_t)j * stride + c];
+        }
         if (P) {
             for (int j = 0; j < T; ++j) P[(int64_t)i * T + j] = j <= i ? srow[j] : (R)0;
         }
@@ -274,10 +334,14 @@ void head_fwd(int T, int d, const R* q, const R* k, const R* v, int64_t stride, 
 // Backward of head_fwd with P recomputed from q and k:
 //   dV_j = sum_i P_ij dO_i, dP_ij = dO_i . v_j, dS_ij = P_ij (dP_ij - sum_j' P_ij' dP_ij'),
 //   dQ_i = sum_j dS_ij k_j / sqrt(d), dK_j = sum_i dS_ij q_i / sqrt(d).
+// With dropout (kp, dscale as in head_fwd) the values are weighted by the
+// dropped weights W_ij = P_ij kp_ij dscale: dV_j = sum_i W_ij dO_i, and the
+// softmax sees dP_ij = kp_ij dscale (dO_i . v_j).
 // dq, dk, dv are overwritten.
 template <class R>
 void head_bwd(int T, int d, const R* q, const R* k, const R* v, int64_t stride, const R* dout,
-              int64_t ostride, R* dq, R* dk, R* dv, R* prow, R* dprow) {
+              int64_t ostride, R* dq, R* dk, R* dv, R* prow, R* dprow, const uint8_t* kp = nullptr,
+              R dscale = 1) {
     const R scale = (R)1 / std::sqrt((R)d);
     for (int i = 0; i < T; ++i)
         for (int c = 0; c < d; ++c) {
@@ -301,15 +365,17 @@ void head_bwd(int T, int d, const R* q, const R* k, const R* v, int64_t stride, 
         for (int j = 0; j <= i; ++j) {
             R s = 0;
             for (int c = 0; c < d; ++c) s += doi[c] * v[(int64_t)j * stride + c];
+            if (kp) s = kp[(int64_t)i * T + j] ? s * dscale : (R)0;
             dprow[j] = s;
             rowdot += prow[j] * s;
         }
         for (int j = 0; j <= i; ++j) {
             R ds = prow[j] * (dprow[j] - rowdot);
+            const R w = kp ? (kp[(int64_t)i * T + j] ? prow[j] * dscale : (R)0) : prow[j];
             for (int c = 0; c < d; ++c) {
                 dq[(int64_t)i * stride + c] += ds * k[(int64_t)j * stride + c] * scale;
                 dk[(int64_t)j * stride + c] += ds * q[(int64_t)i * stride + c] * scale;
-                dv[(int64_t)j * stride + c] += prow[j] * doi[c];
+                dv[(int64_t)j * stride + c] += w * doi[c];
             }
         }
     }
@@ -318,38 +384,73 @@ void head_bwd(int T, int d, const R* q, const R* k, const R* v, int64_t stride, 
 // Multi-head causal attention over a fused qkv [B*T, 3C] activation. Head h uses
 // columns [h*d, (h+1)*d) of each third; outputs are concatenated head 0 first
 // (torch.cat over heads in MultiHeadAttention.forward).
+// Dropout of one model step: the probability and key, and the layer whose
+// masks are wanted (p = 0: no dropout).
+struct Drop {
+    double p = 0.0;
+    uint64_t seed = 0;
+    int layer = 0;
+    bool on() const { return p > 0.0; }
+};
+// keep flags of head (b, h): kp[i T + j] for the attention site
+static void head_keep(const Drop& dr, int b, int h, int H, int T, uint8_t* kp) {
+    const uint32_t thr = drop_threshold(dr.p);
+    for (int i = 0; i < T; ++i)
+        for (int j = 0; j < T; ++j)
+            kp[(int64_t)i * T + j] = keep(dr.seed, DROP_ATTN, dr.layer,
+                                          (((uint64_t)b * H + h) * T + i) * T + j, thr);
+}
+
 template <class R>
-void attention_fwd(int B, int T, int C, int H, const R* qkv, R* out) {
+void attention_fwd(int B, int T, int C, int H, const R* qkv, R* out, const Drop& dr = Drop()) {
     const int d = C / H;
+    const R dscale = dr.on() ? (R)(1.0 / (1.0 - dr.p)) : (R)1;
 #pragma omp parallel
     {
         std::vector<R> srow(T);
+        std::vector<uint8_t> kp(dr.on() ? (size_t)T * T : 0);
 #pragma omp for schedule(dynamic)
         for (int bh = 0; bh < B * H; ++bh) {
             int b = bh / H, h = bh % H;
+            if (dr.on()) head_keep(dr, b, h, H, T, kp.data());
             const R* base = qkv + (int64_t)b * T * 3 * C;
             head_fwd<R>(T, d, base + h * d, base + C + h * d, base + 2 * C + h * d, 3 * C,
-                        out + (int64_t)b * T * C + h * d, C, nullptr, srow.data());
+                        out + (int64_t)b * T * C + h * d, C, nullptr, srow.data(),
+                        dr.on() ? kp.data() : nullptr, dscale);
         }
     }
 }
 template <class R>
-void attention_bwd(int B, int T, int C, int H, const R* qkv, const R* dout, R* dqkv) {
+void attention_bwd(int B, int T, int C, int H, const R* qkv, const R* dout, R* dqkv, const Drop& dr = Drop()) {
     const int d = C / H;
+    const R dscale = dr.on() ? (R)(1.0 / (1.0 - dr.p)) : (R)1;
 #pragma omp parallel
     {
         std::vector<R> prow(T), dprow(T);
+        std::vector<uint8_t> kp(dr.on() ? (size_t)T * T : 0);
 #pragma omp for schedule(dynamic)
         for (int bh = 0; bh < B * H; ++bh) {
             int b = bh / H, h = bh % H;
+            if (dr.on()) head_keep(dr, b, h, H, T, kp.data());
             const R* base = qkv + (int64_t)b * T * 3 * C;
             R* dbase = dqkv + (int64_t)b * T * 3 * C;
             head_bwd<R>(T, d, base + h * d, base + C + h * d, base + 2 * C + h * d, 3 * C,
                         dout + (int64_t)b * T * C + h * d, C,
                         dbase + h * d, dbase + C + h * d, dbase + 2 * C + h * d,
-                        prow.data(), dprow.data());
+                        prow.data(), dprow.data(), dr.on() ? kp.data() : nullptr, dscale);
         }
     }
+}
+
+// Residual-branch dropout in place: y[m C + c] = keep ? y / (1 - p) : 0
+// (also the backward: the same mask and scale on the incoming gradient).
+template <class R>
+void residual_dropout(const Drop& dr, int site, int64_t M, int C, R* y) {
+    if (!dr.on()) return;
+    const uint32_t thr = drop_threshold(dr.p);
+    const R dscale = (R)(1.0 / (1.0 - dr.p));
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < M * C; ++i) y[i] = keep(dr.seed, site, dr.layer, (uint64_t)i, thr) ? y[i] * dscale : (R)0;
 }
 
 // ---------------------------------------------------------------- cross-entropy
@@ -385,6 +486,8 @@ struct Acts {
 // the readings adopted for GPT-2: pre-LN blocks, fused QKV, tanh GELU, weight-tied
 // head. Returns the mean loss over B*T rows (accumulated in double), or NaN when
 // targets is null. grads are accumulated into (zero them to start fresh).
+// cf.dropout > 0 is the training-mode model (model.train()): dropout after the
+// softmax of every head, on the projection output and on the fc2 output.
 template <class R>
 double model_step(const oracle_cfg& cf, int B, int T, const R* p, const int32_t* idx,
                   const int32_t* tgt, R* grads, double loss_scale, R* logits_out, R* loss_rows_out) {
@@ -393,6 +496,9 @@ double model_step(const oracle_cfg& cf, int B, int T, const R* p, const int32_t*
     const int64_t M = (int64_t)B * T;
     const size_t MC = (size_t)M * C;
     const bool erf_gelu = (cf.variant & ORACLE_GELU_ERF) != 0;
+    Drop dr;
+    dr.p = cf.dropout;
+    dr.seed = cf.seed;
     Acts<R> a;
     auto vec = [](size_t n) { return std::vector<R>(n); };
 
@@ -414,10 +520,12 @@ double model_step(const oracle_cfg& cf, int B, int T, const R* p, const int32_t*
         layernorm_fwd<R>(M, C, x.data(), p + W.ln1_g, p + W.ln1_b, cf.ln_eps, h1.data(), m1.data(), r1.data());
         auto qkv = vec((size_t)M * 3 * C);
         linear_fwd<R>(M, 3 * C, C, h1.data(), p + W.w_qkv, W.b_qkv == NONE ? nullptr : p + W.b_qkv, qkv.data());
+        dr.layer = l;
         auto att = vec(MC);
-        attention_fwd<R>(B, T, C, H, qkv.data(), att.data());
+        attention_fwd<R>(B, T, C, H, qkv.data(), att.data(), dr);
         auto pr = vec(MC);
         linear_fwd<R>(M, C, C, att.data(), p + W.w_proj, W.b_proj == NONE ? nullptr : p + W.b_proj, pr.data());
+        residual_dropout<R>(dr, DROP_PROJ, M, C, pr.data());
         for (size_t i = 0; i < MC; ++i) x[i] += pr[i];
         a.xmid.push_back(x);
         auto h2 = vec(MC), m2 = vec(M), r2 = vec(M);
@@ -429,6 +537,7 @@ double model_step(const oracle_cfg& cf, int B, int T, const R* p, const int32_t*
         for (int64_t i = 0; i < M * F; ++i) gg[i] = gelu<R>(u[i], erf_gelu);
         auto mo = vec(MC);
         linear_fwd<R>(M, C, F, gg.data(), p + W.w_fc2, W.b_fc2 == NONE ? nullptr : p + W.b_fc2, mo.data());
+        residual_dropout<R>(dr, DROP_FC2, M, C, mo.data());
         for (size_t i = 0; i < MC; ++i) x[i] += mo[i];
         if (grads) {
             a.ln1.push_back(std::move(h1)); a.m1.push_back(std::move(m1)); a.r1.push_back(std::move(r1));
@@ -469,9 +578,12 @@ double model_step(const oracle_cfg& cf, int B, int T, const R* p, const int32_t*
                      gp + lo.lnf_g, gp + lo.lnf_b);
     for (int l = L - 1; l >= 0; --l) {
         const LayerOff& W = lo.layer[l];
-        // x_out = x_mid + fc2(gelu(fc(ln2(x_mid))))
+        dr.layer = l;
+        // x_out = x_mid + drop(fc2(gelu(fc(ln2(x_mid)))))
+        std::vector<R> dmo = dx;
+        residual_dropout<R>(dr, DROP_FC2, M, C, dmo.data());
         auto dg = vec((size_t)M * F);
-        linear_bwd<R>(M, C, F, dx.data(), a.g[l].data(), p + W.w_fc2, dg.data(), gp + W.w_fc2,
+        linear_bwd<R>(M, C, F, dmo.data(), a.g[l].data(), p + W.w_fc2, dg.data(), gp + W.w_fc2,
                       W.b_fc2 == NONE ? nullptr : gp + W.b_fc2);
         auto& u = a.u[l];
 #pragma omp parallel for schedule(static)
@@ -481,12 +593,14 @@ double model_step(const oracle_cfg& cf, int B, int T, const R* p, const int32_t*
                       W.b_fc == NONE ? nullptr : gp + W.b_fc);
         layernorm_bwd<R>(M, C, dh2.data(), a.xmid[l].data(), a.m2[l].data(), a.r2[l].data(), p + W.ln2_g,
                          dx.data(), gp + W.ln2_g, gp + W.ln2_b);
-        // x_mid = x_in + proj(attn(ln1(x_in)))
+        // x_mid = x_in + drop(proj(attn(ln1(x_in))))
+        std::vector<R> dpr = dx;
+        residual_dropout<R>(dr, DROP_PROJ, M, C, dpr.data());
         auto datt = vec(MC);
-        linear_bwd<R>(M, C, C, dx.data(), a.att[l].data(), p + W.w_proj, datt.data(), gp + W.w_proj,
+        linear_bwd<R>(M, C, C, dpr.data(), a.att[l].data(), p + W.w_proj, datt.data(), gp + W.w_proj,
                       W.b_proj == NONE ? nullptr : gp + W.b_proj);
         auto dqkv = vec((size_t)M * 3 * C);
-        attention_bwd<R>(B, T, C, H, a.qkv[l].data(), datt.data(), dqkv.data());
+        attention_bwd<R>(B, T, C, H, a.qkv[l].data(), datt.data(), dqkv.data(), dr);
         auto dh1 = vec(MC);
         linear_bwd<R>(M, 3 * C, C, dqkv.data(), a.ln1[l].data(), p + W.w_qkv, dh1.data(), gp + W.w_qkv,
                       W.b_qkv == NONE ? nullptr : gp + W.b_qkv);
@@ -652,6 +766,14 @@ double oracle_lr(int64_t it, double max_lr, double min_lr, int64_t warmup, int64
     if (it >= max_iters) return min_lr;
     double ratio = (double)(it - warmup) / (double)(max_iters - warmup);
     return min_lr + 0.5 * (1.0 + std::cos(pi * ratio)) * (max_lr - min_lr);
+}
+
+// Philox4x32-10 itself (for its known-answer vectors) and the keep flags of
+// elements e0 .. e0 + n - 1 of one dropout site (1 = kept).
+void oracle_philox4x32_10(const uint32_t* ctr, const uint32_t* key, uint32_t* out) { philox4x32_10(ctr, key, out); }
+void oracle_dropout_keep(double p, uint64_t seed, int site, int layer, uint64_t e0, int64_t n, uint8_t* out) {
+    const uint32_t thr = drop_threshold(p);
+    for (int64_t i = 0; i < n; ++i) out[i] = keep(seed, site, layer, e0 + (uint64_t)i, thr) ? 1 : 0;
 }
 
 // Row argmax with the lowest index winning ties.

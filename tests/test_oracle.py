@@ -101,7 +101,9 @@ def test_fp32_instantiation_tracks_fp64(oracle):
 
 
 # ----------------------------------------------------------------- independent torch model
-def torch_model_loss(named, m: syn.Model, x, y, scale=1.0):
+def torch_model_loss(named, m: syn.Model, x, y, scale=1.0, masks=None):
+    """masks (training-mode dropout): {(layer, site): keep flags} with the
+    attention site [B, H, T, T] and the residual sites [B, T, C], plus "p"."""
     import torch
     import torch.nn.functional as F
     P = {k: torch.tensor(v, dtype=torch.float64, requires_grad=True) for k, v in named.items()}
@@ -110,6 +112,12 @@ def torch_model_loss(named, m: syn.Model, x, y, scale=1.0):
     d = C // H
     idx = torch.tensor(x, dtype=torch.long)
     h = P["wte"][idx] + P["wpe"][:T]
+
+    def drop(t, l, site):  # nn.Dropout in training mode with a given keep mask
+        if masks is None:
+            return t
+        return t * torch.tensor(masks[(l, site)], dtype=torch.float64) / (1.0 - masks["p"])
+
     for l in range(m.n_layer):
         q = lambda s: P[f"h{l}.{s}"] if f"h{l}.{s}" in P else None
         a = F.layer_norm(h, (C,), q("ln1_g"), q("ln1_b"), eps=m.ln_eps)
@@ -118,12 +126,17 @@ def torch_model_loss(named, m: syn.Model, x, y, scale=1.0):
         qq = qq.view(B, T, H, d).transpose(1, 2)
         kk = kk.view(B, T, H, d).transpose(1, 2)
         vv = vv.view(B, T, H, d).transpose(1, 2)
-        att = F.scaled_dot_product_attention(qq, kk, vv, is_causal=True)
+        if masks is None:
+            att = F.scaled_dot_product_attention(qq, kk, vv, is_causal=True)
+        else:  # Head.forward: masked softmax of the scaled scores, dropout, weights @ v
+            wei = (qq @ kk.transpose(-2, -1)) / math.sqrt(d)
+            wei = wei.masked_fill(torch.ones(T, T, dtype=torch.bool).triu(1), float("-inf"))
+            att = drop(torch.softmax(wei, dim=-1), l, 0) @ vv
         att = att.transpose(1, 2).reshape(B, T, C)
-        h = h + F.linear(att, q("w_proj"), q("b_proj"))
+        h = h + drop(F.linear(att, q("w_proj"), q("b_proj")), l, 1)
         a2 = F.layer_norm(h, (C,), q("ln2_g"), q("ln2_b"), eps=m.ln_eps)
         gelu = F.gelu(F.linear(a2, q("w_fc"), q("b_fc")), approximate="none" if m.gelu_erf else "tanh")
-        h = h + F.linear(gelu, q("w_fc2"), q("b_fc2"))
+        h = h + drop(F.linear(gelu, q("w_fc2"), q("b_fc2")), l, 2)
     hf = F.layer_norm(h, (C,), P["lnf_g"], P["lnf_b"], eps=m.ln_eps)
     logits = hf @ (P["lm_head"] if m.untied else P["wte"]).T
     if y is None:
@@ -150,6 +163,84 @@ def test_oracle_matches_independent_torch_model(oracle, model):
     for name in og:
         r = tg[name]
         assert np.max(np.abs(og[name] - r)) <= 1e-10 * max(1.0, np.max(np.abs(r))), name
+
+
+# ----------------------------------------------------------------- dropout
+def test_philox_known_answer_vectors(oracle):
+    rows = []
+    with open(os.path.join(GOLDEN, "philox4x32_10_kat.txt")) as f:
+        for line in f:
+            if line.strip() and not line.startswith("#"):
+                rows.append([int(w, 16) for w in line.split()])
+    assert len(rows) == 3
+    for r in rows:
+        out = oracle.philox4x32_10(r[0:4], r[4:6])
+        assert [int(v) for v in out] == r[6:10], [hex(v) for v in out]
+
+
+def test_dropout_keep_rate_and_independence(oracle):
+    """Each element is kept with probability 1 - round(65536 p) / 65536 (a
+    binomial 6-sigma band over 2M draws); p = 0 keeps everything; sites, layers
+    and seeds draw different masks; a stretch equals the same stretch of a longer
+    run (element e is a function of e alone)."""
+    n = 2_000_000
+    for p in (0.1, 0.5):
+        k = oracle.dropout_keep(p, 99, oracle.DROP_ATTN, 0, n)
+        q = 1.0 - round(65536 * p) / 65536
+        assert abs(k.mean() - q) <= 6 * math.sqrt(q * (1 - q) / n), (p, k.mean())
+    assert oracle.dropout_keep(0.0, 99, oracle.DROP_PROJ, 3, 4096).all()
+    a = oracle.dropout_keep(0.5, 7, oracle.DROP_PROJ, 1, 4096)
+    for other in (oracle.dropout_keep(0.5, 7, oracle.DROP_FC2, 1, 4096),
+                  oracle.dropout_keep(0.5, 7, oracle.DROP_PROJ, 2, 4096),
+                  oracle.dropout_keep(0.5, 8, oracle.DROP_PROJ, 1, 4096)):
+        assert 0.4 < np.mean(a == other) < 0.6
+    np.testing.assert_array_equal(oracle.dropout_keep(0.5, 7, oracle.DROP_PROJ, 1, 1000, e0=1234),
+                                  oracle.dropout_keep(0.5, 7, oracle.DROP_PROJ, 1, 4096)[1234:2234])
+    # element e uses half e mod 8 of Philox at counter e / 8: low half of word 0 first
+    r = oracle.philox4x32_10([5, 0, oracle.DROP_FC2, 2], [7, 0])
+    halves = np.array([[w & 0xFFFF, w >> 16] for w in r.tolist()]).ravel()
+    np.testing.assert_array_equal(oracle.dropout_keep(0.5, 7, oracle.DROP_FC2, 2, 8, e0=40),
+                                  (halves >= 32768).astype(np.uint8))
+
+
+def dropout_masks(oracle, m: syn.Model, B, T, p, seed):
+    masks = {"p": p}
+    C, H = m.n_embd, m.n_head
+    for l in range(m.n_layer):
+        masks[(l, 0)] = oracle.dropout_keep(p, seed, oracle.DROP_ATTN, l, B * H * T * T).reshape(B, H, T, T)
+        masks[(l, 1)] = oracle.dropout_keep(p, seed, oracle.DROP_PROJ, l, B * T * C).reshape(B, T, C)
+        masks[(l, 2)] = oracle.dropout_keep(p, seed, oracle.DROP_FC2, l, B * T * C).reshape(B, T, C)
+    return masks
+
+
+@pytest.mark.parametrize("model", [TINY, TINY_LIT], ids=["gpt2", "literal"])
+def test_dropout_step_matches_torch_model(oracle, model):
+    """Training-mode dropout (p = 0.1) at the three sites of minigpt.py's block
+    -- the attention weights after the softmax, the projection output and the
+    FeedForward output -- against torch with the same keep masks: loss and every
+    gradient."""
+    p, seed = 0.1, 2024
+    cfg = oracle.make_cfg(model.vocab, model.block_size, model.n_embd, model.n_head, model.n_layer,
+                          model.mlp_hidden, model.bias, model.ln_eps, gelu_erf=model.gelu_erf,
+                          untied=model.untied, dropout=p, seed=seed)
+    B, T = 3, model.block_size
+    named = rand_named(model, 31)
+    x, y = tiny_batch(model, B, T, 32)
+    pf = oracle.pack(cfg, named, np.float64)
+    g = np.zeros_like(pf)
+    loss, _, _ = oracle.step(cfg, B, T, pf, x, y, g)
+    masks = dropout_masks(oracle, model, B, T, p, seed)
+    assert 0 < sum(int((masks[k] == 0).sum()) for k in masks if k != "p")   # something was dropped
+    tl, tg = torch_model_loss(named, model, x, y, masks=masks)
+    assert abs(loss - tl) <= 1e-12 * abs(tl)
+    og = oracle.unpack(cfg, g)
+    for name in og:
+        r = tg[name]
+        assert np.max(np.abs(og[name] - r)) <= 1e-10 * max(1.0, np.max(np.abs(r))), name
+    # the eval-mode model (and p = 0) has no dropout at all
+    l0, _, _ = oracle.step(oracle.eval_cfg(cfg), B, T, pf, x, y)
+    assert abs(l0 - torch_model_loss(named, model, x, y)[0]) <= 1e-12 * abs(l0)
+    assert l0 != loss
 
 
 def test_shorter_sequence_than_block_size(oracle):
