@@ -78,7 +78,7 @@ LABELS = ["gemm.fwd.qkv", "gemm.fwd.proj", "gemm.fwd.fc", "gemm.fwd.fc2", "gemm.
           "gemm.dgrad.head", "gemm.wgrad.head", "gemm.dgrad.fc2", "gemm.wgrad.fc2", "gemm.dgrad.fc",
           "gemm.wgrad.fc", "gemm.dgrad.proj", "gemm.wgrad.proj", "gemm.dgrad.qkv", "gemm.wgrad.qkv",
           "attn.fwd", "attn.bwd.dq", "attn.bwd.dkdv", "ln.fwd", "ln.bwd", "ce", "loss", "colsum",
-          "bias", "embed.fwd", "embed.bwd", "gradnorm", "adamw"]
+          "bias", "embed.fwd", "embed.bwd", "gradnorm", "adamw", "dropout.mask"]
 
 
 # Labels whose launches run with no other work of the step beside them: the
@@ -220,6 +220,8 @@ def main():
     ap.add_argument("--no-breakdown", action="store_true", help="skip the per-kernel-class timing pass")
     ap.add_argument("--roofline-kernel", default=None, help="timing label for the roofline (default: the "
                     "label with the largest time in the breakdown pass)")
+    ap.add_argument("--dropout", type=float, default=0.0, help="training-mode dropout p (the minigpt page's "
+                    "literal model uses 0.1); fresh masks every step")
     ap.add_argument("--generate", action="store_true", help="measure generation instead of the training step "
                     "(prints its own JSON line)")
     ap.add_argument("--gen-batch", type=int, default=12)
@@ -241,7 +243,8 @@ def main():
     w = syn.WORKLOADS[args.workload]
     m = w.model
     cfg = b.make_config(m.vocab, m.block_size, m.n_embd, m.n_head, m.n_layer, m.mlp_hidden, m.bias, b.DTYPE_BF16,
-                        m.ln_eps, gelu_erf=m.gelu_erf, untied_head=m.untied)
+                        m.ln_eps, gelu_erf=m.gelu_erf, untied_head=m.untied,
+                        dropout=args.dropout)
     named = syn.init_params(m)
     g = b.Model(cfg, w.batch, w.seq, b.MODE_TRAIN)
     g.load_named(named)
@@ -258,6 +261,8 @@ def main():
     def step(k):
         nonlocal t
         t += 1
+        if args.dropout > 0:
+            g.set_dropout_seed(k)
         g.forward(xs[k], ys[k])
         g.backward(1.0, True)
         g.adamw_step(w.lr, w.beta1, w.beta2, w.eps, w.weight_decay, t)
@@ -339,7 +344,8 @@ def main():
                                 "micro-batch 12 x 1024, one fwd+bwd+AdamW per step") if not m.untied else
                                ("gpt2_124m_literal: V50257 T1024 C768 H12 L12 F3072, biases, exact erf GELU, "
                                 "untied lm_head; micro-batch 12 x 1024, one fwd+bwd+AdamW per step"),
-                   "global_batch": w.batch, "seq_len": w.seq, "parallelism": "none (1 GPU)"},
+                   "global_batch": w.batch, "seq_len": w.seq, "parallelism": "none (1 GPU)",
+                   "dropout": args.dropout},
         "mfu": round(mfu, 4),
         "flops_per_token": fpt,
         "wall_s": round(wall, 3),
@@ -348,7 +354,7 @@ def main():
         "roofline": roofline,
         "breakdown_ms_per_step": breakdown,
     }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and args.dropout == 0:  # the oracle baseline times the plain step
         out["cpu_baseline"] = cpu_baseline(w, named, args.cpu_seq)
     print(json.dumps(out), flush=True)
 

@@ -25,14 +25,15 @@ EXPORTS = [
     "gpt2_clear_status", "gpt2_arena_tensor", "gpt2_destroy", "gpt2_op_linear_fwd", "gpt2_op_linear_bwd",
     "gpt2_op_layernorm_fwd", "gpt2_op_layernorm_bwd", "gpt2_op_attention_fwd", "gpt2_op_attention_bwd",
     "gpt2_op_cross_entropy", "gpt2_timing_begin", "gpt2_timing_end", "gpt2_char_vocab", "gpt2_char_encode",
-    "gpt2_char_decode", "gpt2_split_point", "gpt2_batch_windows",
+    "gpt2_char_decode", "gpt2_split_point", "gpt2_batch_windows", "gpt2_set_dropout_seed",
 ]
 
 
 class Config(ct.Structure):
     _fields_ = [("vocab", ct.c_int32), ("block_size", ct.c_int32), ("n_embd", ct.c_int32), ("n_head", ct.c_int32),
                 ("n_layer", ct.c_int32), ("mlp_hidden", ct.c_int32), ("bias", ct.c_int32), ("dtype", ct.c_int32),
-                ("ln_eps", ct.c_float), ("gelu_erf", ct.c_int32), ("untied_head", ct.c_int32)]
+                ("ln_eps", ct.c_float), ("gelu_erf", ct.c_int32), ("untied_head", ct.c_int32),
+                ("dropout", ct.c_float)]
 
 
 class TensorDesc(ct.Structure):
@@ -79,6 +80,7 @@ def lib():
             "gpt2_backward": (ct.c_int, [P, f32, i32]),
             "gpt2_adamw_step": (ct.c_int, [P, f32, f32, f32, f32, f32, i32, f32, i32, P]),
             "gpt2_generate": (ct.c_int, [P, P, i32, i32, f32, P, P]),
+            "gpt2_set_dropout_seed": (ct.c_int, [P, ct.c_uint64]),
             "gpt2_char_vocab": (i32, [P, i64, P]),
             "gpt2_char_encode": (ct.c_int, [P, i64, P, i32, P]),
             "gpt2_char_decode": (ct.c_int, [P, i64, P, i32, P]),
@@ -118,9 +120,9 @@ def check(code: int, what: str) -> int:
 
 
 def make_config(vocab, block_size, n_embd, n_head, n_layer, mlp_hidden, bias, dtype, ln_eps=1e-5, gelu_erf=False,
-                untied_head=False) -> Config:
+                untied_head=False, dropout=0.0) -> Config:
     return Config(vocab, block_size, n_embd, n_head, n_layer, mlp_hidden, int(bias), int(dtype), ln_eps,
-                  int(bool(gelu_erf)), int(bool(untied_head)))
+                  int(bool(gelu_erf)), int(bool(untied_head)), float(dropout))
 
 
 def query_sizes(cfg: Config, B: int, T: int, mode: int):
@@ -272,6 +274,10 @@ class Model:
         check(lib().gpt2_adamw_step(self.ctx, lr, beta1, beta2, eps, weight_decay, int(t), clip, decay_mode,
                                     _ptr(self.grad_norm) if want_norm else None), "gpt2_adamw_step")
 
+    def set_dropout_seed(self, seed: int) -> None:
+        """Key of the dropout masks of the following training forwards."""
+        check(lib().gpt2_set_dropout_seed(self.ctx, int(seed)), "gpt2_set_dropout_seed")
+
     def generate(self, prompt, n_new: int, temperature: float, uniforms, out) -> None:
         """prompt: int32 [B, T0] (cuda); uniforms: fp32 [B, n_new] (cuda); out:
         int32 [B, T0 + n_new] (cuda), written on the context's stream."""
@@ -310,7 +316,7 @@ class Model:
                                       ct.byref(cols)), "gpt2_arena_tensor")
         n = int(rows.value) * int(cols.value)
         raw = self.arena[off.value:off.value + n * eb.value]
-        dt = torch.float32 if eb.value == 4 else torch.bfloat16
+        dt = {4: torch.float32, 2: torch.bfloat16, 8: torch.int64}[eb.value]
         return raw.view(dt).view(int(rows.value), int(cols.value))
 
     def close(self) -> None:

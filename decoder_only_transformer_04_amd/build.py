@@ -14,7 +14,7 @@ OBJ = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libgpt2mi.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
-SOURCES = ["layout.cpp", "gemm.hip", "elementwise.hip", "attention_simple.hip", "attention_mfma.hip", "generate.hip",
+SOURCES = ["layout.cpp", "gemm.hip", "elementwise.hip", "attention_simple.hip", "attention_mfma.hip", "generate.hip", "dropout.hip",
            "data.hip", "gpt2.hip"]
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall", "-Wno-unused-function",
          # packed fp32 ALU ops stay off (hipcc's host pass warns that it does not know the feature)

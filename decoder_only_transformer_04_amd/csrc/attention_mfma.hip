@@ -17,6 +17,13 @@
 // every output element is written by exactly one lane, so results are
 // deterministic.
 //
+// Dropout (training mode, DROP): the keep bits of the attention weights are
+// read from a mask written beforehand (one 64-bit word per query row and
+// 64-key tile). The forward weights v_j by P_ij keep_ij and scales O by
+// 1 / (1 - p) at the end, the sum l stays that of P, so lse is unchanged; the
+// backward uses W = P keep / (1 - p) for dV and dP_ij = keep_ij / (1 - p)
+// dO_i . v_j for dS = P (dP - D), where D = dO . O with the dropped O.
+//
 // LDS tiles are [rows][64] bf16 (128 B per row) with the 16-byte chunk index
 // XOR-ed by a bit-reversal of (row / 2) mod 8: conflict-free both for 128-bit
 // row reads (MFMA operands with the contraction index along the row) and for
@@ -29,9 +36,10 @@
 namespace g2 {
 
 hipError_t attention_fwd_simple(int dtype, int B, int Tn, int C, int H, const void* qkv, void* out, float* lse,
-                                hipStream_t s);
+                                hipStream_t s, const uint64_t* dmask, float dscale);
 hipError_t attention_bwd_simple(int dtype, int B, int Tn, int C, int H, const void* qkv, const void* out,
-                                const float* lse, const void* dout, void* dqkv, float* Dbuf, hipStream_t s);
+                                const float* lse, const void* dout, void* dqkv, float* Dbuf, hipStream_t s,
+                                const uint64_t* dmask, float dscale);
 
 namespace {
 
@@ -188,8 +196,10 @@ constexpr float kLazy = 8.0f;
 #endif
 // three workgroups (waves per SIMD) per CU: registers capped at 168. K/V tiles
 // stream into a three-deep LDS ring (48 KB) by DMA, two tiles ahead.
+template <bool DROP>
 __global__ __launch_bounds__(256, G2_ATT_FWD_OCC) void attn_fwd_d64(const bf16_t* qkv, bf16_t* out, float* lse, int T,
-                                                                    int C, int H, float sl2) {
+                                                                    int C, int H, float sl2, const uint64_t* dmask,
+                                                                    int Tw, float dscale) {
     __shared__ __attribute__((aligned(16))) char smem[3][2][kTileBytes];
     int qb, h, b;
     block_coords(T, H, true, qb, h, b);
@@ -215,6 +225,8 @@ __global__ __launch_bounds__(256, G2_ATT_FWD_OCC) void attn_fwd_d64(const bf16_t
     bf16x8 qf[4];
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) qf[kk] = load8(Qg + (int64_t)qi * rs + 16 * kk + 8 * g, qi < T);
+    // this lane's row of keep bits (query qi; rows past T read nothing)
+    const uint64_t* mrow = DROP ? dmask + (((int64_t)b * H + h) * T + min(qi, T - 1)) * Tw : nullptr;
     f32x16 o[2] = {zero16(), zero16()};
     // m is shared by the two half-waves (they hold different keys of the same
     // query); l is kept per half-wave and combined at the end
@@ -231,6 +243,8 @@ __global__ __launch_bounds__(256, G2_ATT_FWD_OCC) void attn_fwd_d64(const bf16_t
         const char* Ks = smem[kt % 3][0];
         const char* Vs = smem[kt % 3][1];
         if (k0 <= q0 + 31) {
+            uint64_t mw = 0;
+            if constexpr (DROP) mw = mrow[kt];
             f32x16 s[2];
 #pragma unroll
             for (int kh = 0; kh < 2; ++kh) {
@@ -271,7 +285,9 @@ __global__ __launch_bounds__(256, G2_ATT_FWD_OCC) void attn_fwd_d64(const bf16_t
                 for (int r = 0; r < 16; ++r) {
                     const float p = fexp2(fmaf(s[kh][r], sl2, -m));
                     l += p;
-                    pk[2 * kh + (r >> 3)][r & 7] = (__bf16)p;
+                    float pv = p;
+                    if constexpr (DROP) pv = ((mw >> (32 * kh + 4 * g + 8 * (r >> 2) + (r & 3))) & 1) ? p : 0.0f;
+                    pk[2 * kh + (r >> 3)][r & 7] = (__bf16)pv;
                 }
 #pragma unroll
             for (int dt = 0; dt < 2; ++dt)
@@ -281,7 +297,7 @@ __global__ __launch_bounds__(256, G2_ATT_FWD_OCC) void attn_fwd_d64(const bf16_t
     }
     l += __shfl_xor(l, 32, 64);
     if (qi < T) {
-        const float inv = 1.0f / l;
+        const float inv = (DROP ? dscale : 1.0f) / l;
         bf16_t* orow = out + ((int64_t)b * T + qi) * C + h * 64;
 #pragma unroll
         for (int dt = 0; dt < 2; ++dt)
@@ -300,9 +316,11 @@ __global__ __launch_bounds__(256, G2_ATT_FWD_OCC) void attn_fwd_d64(const bf16_t
 // ------------------------------------------------------------------ backward: dQ
 // D_i = dO_i . O_i is formed here from the dO rows already in registers and
 // written, with lse in base 2, to Dbuf for the dK/dV kernel that runs next.
+template <bool DROP>
 __global__ __launch_bounds__(256) void attn_bwd_dq_d64(const bf16_t* qkv, const bf16_t* outp, const bf16_t* dout,
                                                        const float* lse, float* Dbuf, bf16_t* dqkv, int T, int C,
-                                                       int H, float sl2, float scale) {
+                                                       int H, float sl2, float scale, const uint64_t* dmask, int Tw,
+                                                       float dscale) {
     __shared__ __attribute__((aligned(16))) char smem[3][2][kTileBytes];
     int qb, h, b;
     block_coords(T, H, true, qb, h, b);
@@ -347,6 +365,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_d64(const bf16_t* qkv, const 
         Dbuf[lb + qi] = Dq;
         L2[lb + qi] = lse2;
     }
+    const uint64_t* mrow = DROP ? dmask + (lb + min(qi, T - 1)) * Tw : nullptr;
     f32x16 dq[2] = {zero16(), zero16()};
     for (int kt = 0; kt < nkt; ++kt) {
         if (kt + 1 < nkt) att_wait_vmcnt<4>();
@@ -357,6 +376,8 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_d64(const bf16_t* qkv, const 
         const char* Ks = smem[kt % 3][0];
         const char* Vs = smem[kt % 3][1];
         if (k0 <= q0 + 31) {
+            uint64_t mw = 0;
+            if constexpr (DROP) mw = mrow[kt];
             f32x16 s[2], dp[2];
 #pragma unroll
             for (int kh = 0; kh < 2; ++kh) {
@@ -377,7 +398,10 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_d64(const bf16_t* qkv, const 
                 for (int r = 0; r < 16; ++r) {
                     float p = fexp2(fmaf(s[kh][r], sl2, -lse2));
                     if (diag && 8 * (r >> 2) + (r & 3) > lim) p = 0.0f;
-                    dsk[2 * kh + (r >> 3)][r & 7] = (__bf16)(p * (dp[kh][r] - Dq));
+                    float dpk = dp[kh][r];
+                    if constexpr (DROP)
+                        dpk = ((mw >> (32 * kh + 4 * g + 8 * (r >> 2) + (r & 3))) & 1) ? dpk * dscale : 0.0f;
+                    dsk[2 * kh + (r >> 3)][r & 7] = (__bf16)(p * (dpk - Dq));
                 }
             }
 #pragma unroll
@@ -402,11 +426,16 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_d64(const bf16_t* qkv, const 
 }
 
 // ------------------------------------------------------------------ backward: dK, dV
+template <bool DROP>
 __global__ __launch_bounds__(256) void attn_bwd_dkdv_d64(const bf16_t* qkv, const bf16_t* dout, const float* lse,
                                                          const float* Dbuf, bf16_t* dqkv, int T, int C, int H,
-                                                         float sl2, float scale) {
+                                                         float sl2, float scale, const uint64_t* dmask, int Tw,
+                                                         float dscale) {
     __shared__ __attribute__((aligned(16))) char smem[2][2][kTileBytes];
     __shared__ float sL[2][64], sD[2][64];
+    // keep bits of the query tile against this workgroup's 128 keys: two words
+    // per query row (keys kb 128 .. + 63 and + 64 .. + 127)
+    __shared__ uint64_t sM[2][64][2];
     int kb, h, b;
     block_coords(T, H, false, kb, h, b);
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 5;
@@ -431,6 +460,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_d64(const bf16_t* qkv, cons
     const int nqt = (T + 63) / 64;
     TileRegs rq, rd;
     float pl = 0.0f, pd = 0.0f;
+    uint64_t pm = 0;
     auto fetch = [&](int qt) {
         tile_load(rq, Qg, rs, qt * 64, T, tid);
         tile_load(rd, dOg, C, qt * 64, T, tid);
@@ -438,6 +468,12 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_d64(const bf16_t* qkv, cons
             const int q = qt * 64 + tid;
             pl = q < T ? L2[lb + q] : INFINITY;  // rows past T get probability 0
             pd = q < T ? Dbuf[lb + q] : 0.0f;
+        }
+        if constexpr (DROP) {
+            if (tid < 128) {
+                const int q = qt * 64 + (tid >> 1), wd = 2 * kb + (tid & 1);
+                pm = (q < T && wd < Tw) ? dmask[(lb + q) * Tw + wd] : 0;
+            }
         }
     };
     auto put = [&](int buf) {
@@ -447,7 +483,11 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_d64(const bf16_t* qkv, cons
             sL[buf][tid] = pl;
             sD[buf][tid] = pd;
         }
+        if constexpr (DROP) {
+            if (tid < 128) sM[buf][tid >> 1][tid & 1] = pm;
+        }
     };
+    const int kbit = kj & 63;  // this lane's key within its mask word (word w / 2 of the pair)
     if (qt0 < nqt) {
         fetch(qt0);
         put(0);
@@ -478,8 +518,14 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_d64(const bf16_t* qkv, cons
                     const int ql = 32 * qh + acc_row(r, g);
                     float p = fexp2(fmaf(s[r], sl2, -sL[buf][ql]));
                     if (diag && 8 * (r >> 2) + (r & 3) < lim) p = 0.0f;
-                    pt[2 * qh + (r >> 3)][r & 7] = (__bf16)p;
-                    dst[2 * qh + (r >> 3)][r & 7] = (__bf16)(p * (dp[r] - sD[buf][ql]));
+                    if constexpr (DROP) {
+                        const bool kp = (sM[buf][ql][w >> 1] >> kbit) & 1;
+                        pt[2 * qh + (r >> 3)][r & 7] = (__bf16)(kp ? p * dscale : 0.0f);
+                        dst[2 * qh + (r >> 3)][r & 7] = (__bf16)(p * ((kp ? dp[r] * dscale : 0.0f) - sD[buf][ql]));
+                    } else {
+                        pt[2 * qh + (r >> 3)][r & 7] = (__bf16)p;
+                        dst[2 * qh + (r >> 3)][r & 7] = (__bf16)(p * (dp[r] - sD[buf][ql]));
+                    }
                 }
             }
 #pragma unroll
@@ -509,36 +555,58 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_d64(const bf16_t* qkv, cons
 
 // ------------------------------------------------------------------ dispatch
 hipError_t attention_fwd(int dtype, int B, int Tn, int C, int H, const void* qkv, void* out, float* lse,
-                         hipStream_t s) {
+                         hipStream_t s, const uint64_t* dmask, float dscale) {
     if (B == 0 || Tn == 0) return hipSuccess;
+    const int Tw = (Tn + 63) / 64;
     if (dtype == GPT2_DTYPE_BF16 && C / H == 64) {
         const float sl2 = kLog2e / 8.0f;  // 1/sqrt(64) in base 2
         const dim3 grid((unsigned)((Tn + 127) / 128 * H * B));
-        hipLaunchKernelGGL(attn_fwd_d64, grid, dim3(256), 0, s, (const bf16_t*)qkv, (bf16_t*)out, lse, Tn, C, H, sl2);
+        if (dmask)
+            hipLaunchKernelGGL(attn_fwd_d64<true>, grid, dim3(256), 0, s, (const bf16_t*)qkv, (bf16_t*)out, lse, Tn, C,
+                               H, sl2, dmask, Tw, dscale);
+        else
+            hipLaunchKernelGGL(attn_fwd_d64<false>, grid, dim3(256), 0, s, (const bf16_t*)qkv, (bf16_t*)out, lse, Tn,
+                               C, H, sl2, nullptr, Tw, 1.0f);
         return hipGetLastError();
     }
-    return attention_fwd_simple(dtype, B, Tn, C, H, qkv, out, lse, s);
+    return attention_fwd_simple(dtype, B, Tn, C, H, qkv, out, lse, s, dmask, dscale);
 }
 
 bool attention_bwd_staged(int dtype, int C, int H) { return dtype == GPT2_DTYPE_BF16 && C / H == 64; }
 
 hipError_t attention_bwd(int dtype, int B, int Tn, int C, int H, const void* qkv, const void* out, const float* lse,
-                         const void* dout, void* dqkv, float* Dbuf, hipStream_t s, int stages) {
+                         const void* dout, void* dqkv, float* Dbuf, hipStream_t s, int stages, const uint64_t* dmask,
+                         float dscale) {
     if (B == 0 || Tn == 0) return hipSuccess;
+    const int Tw = (Tn + 63) / 64;
     if (attention_bwd_staged(dtype, C, H)) {
         const float sl2 = kLog2e / 8.0f;
         const float scale = 0.125f;
         const dim3 grid((unsigned)((Tn + 127) / 128 * H * B));
-        if (stages & ATT_BWD_DQ)
-            hipLaunchKernelGGL(attn_bwd_dq_d64, grid, dim3(256), 0, s, (const bf16_t*)qkv, (const bf16_t*)out,
-                               (const bf16_t*)dout, lse, Dbuf, (bf16_t*)dqkv, Tn, C, H, sl2, scale);
-        if (stages & ATT_BWD_DKDV)
-            hipLaunchKernelGGL(attn_bwd_dkdv_d64, grid, dim3(256), 0, s, (const bf16_t*)qkv, (const bf16_t*)dout,
-                               lse, (const float*)Dbuf, (bf16_t*)dqkv, Tn, C, H, sl2, scale);
+        if (stages & ATT_BWD_DQ) {
+            if (dmask)
+                hipLaunchKernelGGL(attn_bwd_dq_d64<true>, grid, dim3(256), 0, s, (const bf16_t*)qkv, (const bf16_t*)out,
+                                   (const bf16_t*)dout, lse, Dbuf, (bf16_t*)dqkv, Tn, C, H, sl2, scale, dmask, Tw,
+                                   dscale);
+            else
+                hipLaunchKernelGGL(attn_bwd_dq_d64<false>, grid, dim3(256), 0, s, (const bf16_t*)qkv,
+                                   (const bf16_t*)out, (const bf16_t*)dout, lse, Dbuf, (bf16_t*)dqkv, Tn, C, H, sl2,
+                                   scale, nullptr, Tw, 1.0f);
+        }
+        if (stages & ATT_BWD_DKDV) {
+            if (dmask)
+                hipLaunchKernelGGL(attn_bwd_dkdv_d64<true>, grid, dim3(256), 0, s, (const bf16_t*)qkv,
+                                   (const bf16_t*)dout, lse, (const float*)Dbuf, (bf16_t*)dqkv, Tn, C, H, sl2, scale,
+                                   dmask, Tw, dscale);
+            else
+                hipLaunchKernelGGL(attn_bwd_dkdv_d64<false>, grid, dim3(256), 0, s, (const bf16_t*)qkv,
+                                   (const bf16_t*)dout, lse, (const float*)Dbuf, (bf16_t*)dqkv, Tn, C, H, sl2, scale,
+                                   nullptr, Tw, 1.0f);
+        }
         return hipGetLastError();
     }
     if (stages != ATT_BWD_ALL) return hipErrorInvalidValue;
-    return attention_bwd_simple(dtype, B, Tn, C, H, qkv, out, lse, dout, dqkv, Dbuf, s);
+    return attention_bwd_simple(dtype, B, Tn, C, H, qkv, out, lse, dout, dqkv, Dbuf, s, dmask, dscale);
 }
 
 }  // namespace g2

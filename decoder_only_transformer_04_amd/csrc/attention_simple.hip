@@ -7,6 +7,10 @@
 // lse = max + log(sum exp) per row. Backward (P recomputed from lse):
 // D_i = dO_i . O_i, dV_j = sum_i P_ij dO_i, dS_ij = P_ij (dO_i . v_j - D_i),
 // dQ_i = sum_j dS_ij k_j / sqrt(d), dK_j = sum_i dS_ij q_i / sqrt(d).
+// Dropout (dm non-null): the keep bit of (i, j) is bit j % 64 of word
+// ((b H + h) T + i) Tw + j / 64; the forward weights v_j by P_ij keep_ij and
+// scales o by dscale = 1 / (1 - p); the backward uses P keep dscale for dV and
+// keep dscale (dO_i . v_j) in place of dO_i . v_j in dS.
 #include <cmath>
 
 #include "device.h"
@@ -14,7 +18,8 @@
 namespace g2 {
 
 template <class T, int DM>
-__global__ __launch_bounds__(64) void attn_fwd_simple(const T* qkv, T* out, float* lse, int Tn, int C, int H) {
+__global__ __launch_bounds__(64) void attn_fwd_simple(const T* qkv, T* out, float* lse, int Tn, int C, int H,
+                                                      const uint64_t* dm, int Tw, float dscale) {
     __shared__ float Ks[64][DM + 1], Vs[64][DM + 1];
     const int qb = blockIdx.x, h = blockIdx.y, b = blockIdx.z, lane = threadIdx.x;
     const int d = C / H;
@@ -29,8 +34,10 @@ __global__ __launch_bounds__(64) void attn_fwd_simple(const T* qkv, T* out, floa
         o[c] = 0.0f;
     }
     float m = -INFINITY, l = 0.0f;
+    const uint64_t* mrow = dm ? dm + (((int64_t)b * H + h) * Tn + min(i, Tn - 1)) * Tw : nullptr;
     for (int kb = 0; kb <= qb; ++kb) {
         const int j0 = kb * 64;
+        const uint64_t mw = mrow ? mrow[kb] : ~(uint64_t)0;
         {
             const int j = j0 + lane;
 #pragma unroll
@@ -62,15 +69,16 @@ __global__ __launch_bounds__(64) void attn_fwd_simple(const T* qkv, T* out, floa
             for (int r = 0; r < 64; ++r) {
                 const float p = s[r] == -INFINITY ? 0.0f : expf(s[r] - mn);
                 l += p;
+                const float pv = ((mw >> r) & 1) ? p : 0.0f;
 #pragma unroll
-                for (int c = 0; c < DM; ++c) o[c] += p * Vs[r][c];
+                for (int c = 0; c < DM; ++c) o[c] += pv * Vs[r][c];
             }
             m = mn;
         }
         __syncthreads();
     }
     if (i < Tn) {
-        const float inv = 1.0f / l;
+        const float inv = (dm ? dscale : 1.0f) / l;
         T* orow = out + ((int64_t)b * Tn + i) * C + h * d;
 #pragma unroll
         for (int c = 0; c < DM; ++c)
@@ -96,10 +104,12 @@ __global__ void attn_bwd_D(const T* out, const T* dout, float* Dbuf, int B, int 
 
 template <class T, int DM>
 __global__ __launch_bounds__(64) void attn_bwd_dkdv_simple(const T* qkv, const float* lse, const T* dout,
-                                                           const float* Dbuf, T* dqkv, int Tn, int C, int H) {
+                                                           const float* Dbuf, T* dqkv, int Tn, int C, int H,
+                                                           const uint64_t* dm, int Tw, float dscale) {
     __shared__ float Kown[64][DM + 1], Vown[64][DM + 1];
     __shared__ float Qs[64][DM + 1], dOs[64][DM + 1];
     __shared__ float Ls[64], Ds[64];
+    __shared__ uint64_t Ms[64];  // keep words of the query tile for this key block
     const int kb = blockIdx.x, h = blockIdx.y, b = blockIdx.z, lane = threadIdx.x;
     const int d = C / H;
     const float scale = 1.0f / sqrtf((float)d);
@@ -130,6 +140,7 @@ __global__ __launch_bounds__(64) void attn_bwd_dkdv_simple(const T* qkv, const f
             }
             Ls[lane] = i < Tn ? lse[lb + i] : 0.0f;
             Ds[lane] = i < Tn ? Dbuf[lb + i] : 0.0f;
+            Ms[lane] = (dm && i < Tn) ? dm[(lb + i) * Tw + kb] : ~(uint64_t)0;
         }
         __syncthreads();
         if (j < Tn) {
@@ -144,10 +155,12 @@ __global__ __launch_bounds__(64) void attn_bwd_dkdv_simple(const T* qkv, const f
                     dp += dOs[r][c] * Vown[lane][c];
                 }
                 const float p = expf(s * scale - Ls[r]);
-                const float ds = p * (dp - Ds[r]);
+                const bool kp = (Ms[r] >> lane) & 1;
+                const float pv = dm ? (kp ? p * dscale : 0.0f) : p;
+                const float ds = p * ((dm ? (kp ? dp * dscale : 0.0f) : dp) - Ds[r]);
 #pragma unroll
                 for (int c = 0; c < DM; ++c) {
-                    dv[c] += p * dOs[r][c];
+                    dv[c] += pv * dOs[r][c];
                     dk[c] += ds * Qs[r][c] * scale;
                 }
             }
@@ -166,7 +179,8 @@ __global__ __launch_bounds__(64) void attn_bwd_dkdv_simple(const T* qkv, const f
 
 template <class T, int DM>
 __global__ __launch_bounds__(64) void attn_bwd_dq_simple(const T* qkv, const float* lse, const T* dout,
-                                                         const float* Dbuf, T* dqkv, int Tn, int C, int H) {
+                                                         const float* Dbuf, T* dqkv, int Tn, int C, int H,
+                                                         const uint64_t* dm, int Tw, float dscale) {
     __shared__ float Ks[64][DM + 1], Vs[64][DM + 1];
     const int qb = blockIdx.x, h = blockIdx.y, b = blockIdx.z, lane = threadIdx.x;
     const int d = C / H;
@@ -185,7 +199,9 @@ __global__ __launch_bounds__(64) void attn_bwd_dq_simple(const T* qkv, const flo
     }
     const float Li = i < Tn ? lse[lb + i] : 0.0f;
     const float Di = i < Tn ? Dbuf[lb + i] : 0.0f;
+    const uint64_t* mrow = dm ? dm + (lb + min(i, Tn - 1)) * Tw : nullptr;
     for (int kb = 0; kb <= qb; ++kb) {
+        const uint64_t mw = mrow ? mrow[kb] : ~(uint64_t)0;
         __syncthreads();
         {
             const int j = kb * 64 + lane;
@@ -208,7 +224,8 @@ __global__ __launch_bounds__(64) void attn_bwd_dq_simple(const T* qkv, const flo
                     dp += dO[c] * Vs[r][c];
                 }
                 const float p = expf(s * scale - Li);
-                const float ds = p * (dp - Di) * scale;
+                const float dpk = dm ? (((mw >> r) & 1) ? dp * dscale : 0.0f) : dp;
+                const float ds = p * (dpk - Di) * scale;
 #pragma unroll
                 for (int c = 0; c < DM; ++c) dq[c] += ds * Ks[r][c];
             }
@@ -223,50 +240,55 @@ __global__ __launch_bounds__(64) void attn_bwd_dq_simple(const T* qkv, const flo
 }
 
 template <class T, int DM>
-static hipError_t fwd_simple(int B, int Tn, int C, int H, const void* qkv, void* out, float* lse, hipStream_t s) {
+static hipError_t fwd_simple(int B, int Tn, int C, int H, const void* qkv, void* out, float* lse, hipStream_t s,
+                             const uint64_t* dm, float dscale) {
     dim3 grid((Tn + 63) / 64, H, B);
-    hipLaunchKernelGGL((attn_fwd_simple<T, DM>), grid, dim3(64), 0, s, (const T*)qkv, (T*)out, lse, Tn, C, H);
+    hipLaunchKernelGGL((attn_fwd_simple<T, DM>), grid, dim3(64), 0, s, (const T*)qkv, (T*)out, lse, Tn, C, H, dm,
+                       (Tn + 63) / 64, dscale);
     return hipGetLastError();
 }
 
 template <class T, int DM>
 static hipError_t bwd_simple(int B, int Tn, int C, int H, const void* qkv, const void* out, const float* lse,
-                             const void* dout, void* dqkv, float* Dbuf, hipStream_t s) {
+                             const void* dout, void* dqkv, float* Dbuf, hipStream_t s, const uint64_t* dm,
+                             float dscale) {
+    const int Tw = (Tn + 63) / 64;
     const int64_t n = (int64_t)B * H * Tn;
     hipLaunchKernelGGL((attn_bwd_D<T>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, (const T*)out,
                        (const T*)dout, Dbuf, B, Tn, C, H);
     dim3 grid((Tn + 63) / 64, H, B);
     hipLaunchKernelGGL((attn_bwd_dkdv_simple<T, DM>), grid, dim3(64), 0, s, (const T*)qkv, lse, (const T*)dout,
-                       (const float*)Dbuf, (T*)dqkv, Tn, C, H);
+                       (const float*)Dbuf, (T*)dqkv, Tn, C, H, dm, Tw, dscale);
     hipLaunchKernelGGL((attn_bwd_dq_simple<T, DM>), grid, dim3(64), 0, s, (const T*)qkv, lse, (const T*)dout,
-                       (const float*)Dbuf, (T*)dqkv, Tn, C, H);
+                       (const float*)Dbuf, (T*)dqkv, Tn, C, H, dm, Tw, dscale);
     return hipGetLastError();
 }
 
 hipError_t attention_fwd_simple(int dtype, int B, int Tn, int C, int H, const void* qkv, void* out, float* lse,
-                                hipStream_t s) {
+                                hipStream_t s, const uint64_t* dm, float dscale) {
     const int d = C / H;
     if (dtype == GPT2_DTYPE_BF16) {
-        if (d <= 32) return fwd_simple<bf16_t, 32>(B, Tn, C, H, qkv, out, lse, s);
-        if (d <= 64) return fwd_simple<bf16_t, 64>(B, Tn, C, H, qkv, out, lse, s);
-        return fwd_simple<bf16_t, 128>(B, Tn, C, H, qkv, out, lse, s);
+        if (d <= 32) return fwd_simple<bf16_t, 32>(B, Tn, C, H, qkv, out, lse, s, dm, dscale);
+        if (d <= 64) return fwd_simple<bf16_t, 64>(B, Tn, C, H, qkv, out, lse, s, dm, dscale);
+        return fwd_simple<bf16_t, 128>(B, Tn, C, H, qkv, out, lse, s, dm, dscale);
     }
-    if (d <= 32) return fwd_simple<float, 32>(B, Tn, C, H, qkv, out, lse, s);
-    if (d <= 64) return fwd_simple<float, 64>(B, Tn, C, H, qkv, out, lse, s);
-    return fwd_simple<float, 128>(B, Tn, C, H, qkv, out, lse, s);
+    if (d <= 32) return fwd_simple<float, 32>(B, Tn, C, H, qkv, out, lse, s, dm, dscale);
+    if (d <= 64) return fwd_simple<float, 64>(B, Tn, C, H, qkv, out, lse, s, dm, dscale);
+    return fwd_simple<float, 128>(B, Tn, C, H, qkv, out, lse, s, dm, dscale);
 }
 
 hipError_t attention_bwd_simple(int dtype, int B, int Tn, int C, int H, const void* qkv, const void* out,
-                                const float* lse, const void* dout, void* dqkv, float* Dbuf, hipStream_t s) {
+                                const float* lse, const void* dout, void* dqkv, float* Dbuf, hipStream_t s,
+                                const uint64_t* dm, float dscale) {
     const int d = C / H;
     if (dtype == GPT2_DTYPE_BF16) {
-        if (d <= 32) return bwd_simple<bf16_t, 32>(B, Tn, C, H, qkv, out, lse, dout, dqkv, Dbuf, s);
-        if (d <= 64) return bwd_simple<bf16_t, 64>(B, Tn, C, H, qkv, out, lse, dout, dqkv, Dbuf, s);
-        return bwd_simple<bf16_t, 128>(B, Tn, C, H, qkv, out, lse, dout, dqkv, Dbuf, s);
+        if (d <= 32) return bwd_simple<bf16_t, 32>(B, Tn, C, H, qkv, out, lse, dout, dqkv, Dbuf, s, dm, dscale);
+        if (d <= 64) return bwd_simple<bf16_t, 64>(B, Tn, C, H, qkv, out, lse, dout, dqkv, Dbuf, s, dm, dscale);
+        return bwd_simple<bf16_t, 128>(B, Tn, C, H, qkv, out, lse, dout, dqkv, Dbuf, s, dm, dscale);
     }
-    if (d <= 32) return bwd_simple<float, 32>(B, Tn, C, H, qkv, out, lse, dout, dqkv, Dbuf, s);
-    if (d <= 64) return bwd_simple<float, 64>(B, Tn, C, H, qkv, out, lse, dout, dqkv, Dbuf, s);
-    return bwd_simple<float, 128>(B, Tn, C, H, qkv, out, lse, dout, dqkv, Dbuf, s);
+    if (d <= 32) return bwd_simple<float, 32>(B, Tn, C, H, qkv, out, lse, dout, dqkv, Dbuf, s, dm, dscale);
+    if (d <= 64) return bwd_simple<float, 64>(B, Tn, C, H, qkv, out, lse, dout, dqkv, Dbuf, s, dm, dscale);
+    return bwd_simple<float, 128>(B, Tn, C, H, qkv, out, lse, dout, dqkv, Dbuf, s, dm, dscale);
 }
 
 }  // namespace g2

@@ -69,6 +69,10 @@ struct ArenaPlan {
     // weight gradient reading one has a whole sub-layer to finish before the
     // next write to it
     Region dres, dres_act, dres_act2, dtmp, dF, dqkv, datt, attD;
+    // training-mode dropout keep masks (all layers; empty without dropout)
+    Region dm_attn, dm_proj, dm_fc2;
+    int64_t dm_attn_words = 0, dm_res_words = 0;  // 64-bit words per layer
+    int dm_tw = 0;                                // words per attention row
     // parameter-gradient partials, one buffer per producer so that all of them
     // are reduced by one launch at the end of the backward: LayerNorm backward
     // calls in issue order (ln_f, then ln2 and ln1 of each layer from the top),
@@ -125,6 +129,10 @@ struct GemmArgs {
     // EPI_GELU_BWD only (nullable): column sums of the output over each 64-row
     // block, written to colsum_part[(m / 64) * N + n] (the bias gradient's partials)
     float* colsum_part;
+    // EPI_RESID only (nullable): dropout of the branch, C = R + keep(m N + n) *
+    // dscale * (acc + bias), keep bits LSB-first in bytes (see dropout_masks_res)
+    const uint8_t* dmask;
+    float dscale;
 };
 
 #ifdef __HIPCC__
@@ -138,9 +146,12 @@ hipError_t layernorm_fwd(int dtype, const float* x, const float* g, const float*
                          float* mean, float* rstd, int64_t rows, int C, hipStream_t s);
 // with_res: the partial rows also carry the column sums of the updated dres
 // (layout per partial row: dg[C], db[C], dres[C]; else dg[C], db[C])
+// dmask (nullable): the activation copy and the dres column sums are of the
+// dropped residual gradient keep(row C + c) * dscale * dres (the gradient of the
+// dropout branch that feeds dres); dres itself is never masked
 hipError_t layernorm_bwd(int dtype, const float* dy, const float* x, const float* mean, const float* rstd,
                          const float* g, float* dres, void* dres_act, float* part, int part_rows, int64_t rows, int C,
-                         int add, int with_res, hipStream_t s);
+                         int add, int with_res, hipStream_t s, const uint8_t* dmask = nullptr, float dscale = 1.0f);
 int ln_bwd_partial_rows(int64_t rows);  // partial rows layernorm_bwd writes
 hipError_t colsum_finish2(const float* part, int part_rows, int ld, float* out_a, int na, float* out_b, int nb,
                           int accumulate, hipStream_t s);
@@ -164,8 +175,11 @@ int bias_partial_rows(int64_t rows, int N);  // partial rows bias_partials write
 hipError_t bias_partials(int dtype, const void* dY, int64_t rows, int N, float* part, int part_rows, hipStream_t s);
 hipError_t bias_grad(int dtype, const void* dY, int64_t rows, int N, float* part, int part_rows, float* db,
                      int accumulate, hipStream_t s);
+// dmask (nullable): dropout of the attention weights, keep bit of query i, key j
+// of (b, h) at bit j % 64 of word ((b H + h) T + i) Tw + j / 64, Tw = ceil(T / 64);
+// the weights P_ij * keep * dscale multiply v_j (lse stays that of P)
 hipError_t attention_fwd(int dtype, int B, int T, int C, int H, const void* qkv, void* out, float* lse,
-                         hipStream_t s);
+                         hipStream_t s, const uint64_t* dmask = nullptr, float dscale = 1.0f);
 // attention backward runs as two launches on the MFMA path: dQ (which also forms
 // D = rowsum(dO*O) and writes it with lse in base 2 to Dbuf) and then dK/dV;
 // `stages` selects which of them to enqueue (the scalar path takes both only).
@@ -174,7 +188,22 @@ enum { ATT_BWD_DQ = 2, ATT_BWD_DKDV = 4, ATT_BWD_ALL = 6 };
 bool attention_bwd_staged(int dtype, int C, int H);
 hipError_t attention_bwd(int dtype, int B, int T, int C, int H, const void* qkv, const void* out,
                          const float* lse, const void* dout, void* dqkv, float* Dbuf, hipStream_t s,
-                         int stages = ATT_BWD_ALL);
+                         int stages = ATT_BWD_ALL, const uint64_t* dmask = nullptr, float dscale = 1.0f);
+
+// --------------------------------------------------------------- dropout
+// Keep masks from Philox4x32-10 (Salmon et al., SC 2011) under key `seed`:
+// element e of site `site`, layer l takes 16-bit half e % 8 (low half of word 0
+// first) of the generator at counter (e / 8 low, e / 8 high, site, l) and is
+// kept when that half is >= thr (round(p 65536)). Bits are written LSB-first,
+// 64 per word, one block of words_per_layer words per layer.
+enum { DROP_ATTN = 0, DROP_PROJ = 1, DROP_FC2 = 2 };
+// attention site: e = (bh T + i) T + j, stored at bit j % 64 of word (bh T + i) Tw + j / 64;
+// words wholly above the diagonal (64 (j / 64) > i) are written as zero
+hipError_t dropout_masks_attn(uint64_t* bits, int L, int64_t words_per_layer, int BH, int T, int Tw, uint64_t seed,
+                              uint32_t thr, hipStream_t s);
+// residual sites: e = m C + c over n_elem elements, stored at bit e % 64 of word e / 64
+hipError_t dropout_masks_res(uint64_t* bits, int L, int64_t words_per_layer, int64_t n_elem, int site,
+                             uint64_t seed, uint32_t thr, hipStream_t s);
 hipError_t cross_entropy(int dtype, void* logits, int64_t rows, int V, int ld, const int32_t* targets,
                          float* loss_rows, int32_t* argmax, int write_grad, uint32_t* status, hipStream_t s);
 hipError_t mean_loss(const float* loss_rows, int64_t rows, float* out, uint32_t* status, hipStream_t s);

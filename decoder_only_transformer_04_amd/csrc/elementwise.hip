@@ -403,12 +403,14 @@ hipError_t layernorm_fwd(int dtype, const float* x, const float* g, const float*
 // dx = rstd (g dy - mean(g dy) - xhat mean(g dy xhat)); dres (+)= dx; the act copy
 // of dres is refreshed; per-block partial sums of dy*xhat (dg) and dy (db) go to
 // part[block][0..C) and part[block][C..2C). A block covers 16 rows (4 per wave).
+// With dmask the act copy and the dres column sums are of keep * dscale * dres
+// (the gradient reaching the dropped branch that fed dres).
 int ln_bwd_partial_rows(int64_t rows) { return (int)((rows + 15) / 16); }
 
 template <int NJ4, class T>
 __global__ __launch_bounds__(256) void ln_bwd_v4(const float* dy, const float* x, const float* mean, const float* rstd,
                                                  const float* g, float* dres, T* dres_act, float* part, int64_t rows,
-                                                 int C, int add, int with_res) {
+                                                 int C, int add, int with_res, const uint8_t* dmask, float dscale) {
     __shared__ float red[4][256 * NJ4];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int C4 = C / 4;
@@ -464,6 +466,15 @@ __global__ __launch_bounds__(256) void ln_bwd_v4(const float* dy, const float* x
                                        rs * (gg[j].w * d[j].w - a - xh[j].w * bb));
                 o.x += old[j].x; o.y += old[j].y; o.z += old[j].z; o.w += old[j].w;
                 dp[c4] = o;
+                if (dmask) {
+                    // four elements from a multiple of 4 (C % 4 == 0): a nibble of keep bits
+                    const int64_t e = row * C + 4 * c4;
+                    const uint32_t kb = (uint32_t)dmask[e >> 3] >> (e & 7);
+                    o.x = (kb & 1) ? o.x * dscale : 0.0f;
+                    o.y = (kb & 2) ? o.y * dscale : 0.0f;
+                    o.z = (kb & 4) ? o.z * dscale : 0.0f;
+                    o.w = (kb & 8) ? o.w * dscale : 0.0f;
+                }
                 if (dres_act) st4<T>(dres_act + row * C + 4 * c4, o);
                 pr[j].x += o.x; pr[j].y += o.y; pr[j].z += o.z; pr[j].w += o.w;
             }
@@ -488,7 +499,8 @@ __global__ __launch_bounds__(256) void ln_bwd_v4(const float* dy, const float* x
 template <int NJ, class T>
 __global__ __launch_bounds__(256) void ln_bwd_kernel(const float* dy, const float* x, const float* mean,
                                                      const float* rstd, const float* g, float* dres, T* dres_act,
-                                                     float* part, int64_t rows, int C, int add, int with_res) {
+                                                     float* part, int64_t rows, int C, int add, int with_res,
+                                                     const uint8_t* dmask, float dscale) {
     __shared__ float red[4][64 * NJ];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     float pg[NJ], pb[NJ], pr[NJ], gg[NJ];
@@ -524,8 +536,12 @@ __global__ __launch_bounds__(256) void ln_bwd_kernel(const float* dy, const floa
             const int c = lane + 64 * j;
             if (c < C) {
                 const float dx = rs * (gg[j] * d[j] - a - xh[j] * bb);
-                const float o = add ? dres[row * C + c] + dx : dx;
+                float o = add ? dres[row * C + c] + dx : dx;
                 dres[row * C + c] = o;
+                if (dmask) {
+                    const int64_t e = row * C + c;
+                    o = ((dmask[e >> 3] >> (e & 7)) & 1) ? o * dscale : 0.0f;
+                }
                 if (dres_act) Act<T>::st(dres_act, row * C + c, o);
                 pr[j] += o;
             }
@@ -547,13 +563,13 @@ __global__ __launch_bounds__(256) void ln_bwd_kernel(const float* dy, const floa
 template <class T>
 static hipError_t ln_bwd_dispatch(const float* dy, const float* x, const float* mean, const float* rstd,
                                   const float* g, float* dres, T* dres_act, float* part, int64_t rows, int C, int add,
-                                  int with_res, hipStream_t s) {
+                                  int with_res, hipStream_t s, const uint8_t* dmask, float dscale) {
     dim3 grid(nblk(rows, 16)), blk(256);
     if (C % 4 == 0) {
         const int nj4 = (C / 4 + 63) / 64;
 #define G2_LNB4(N)                                                                                              \
     hipLaunchKernelGGL((ln_bwd_v4<N, T>), grid, blk, 0, s, dy, x, mean, rstd, g, dres, dres_act, part, rows, C, \
-                       add, with_res)
+                       add, with_res, dmask, dscale)
         if (nj4 <= 1) G2_LNB4(1);
         else if (nj4 <= 2) G2_LNB4(2);
         else if (nj4 <= 3) G2_LNB4(3);
@@ -567,7 +583,7 @@ static hipError_t ln_bwd_dispatch(const float* dy, const float* x, const float* 
     const int nj = (C + 63) / 64;
 #define G2_LNB(N)                                                                                                  \
     hipLaunchKernelGGL((ln_bwd_kernel<N, T>), grid, blk, 0, s, dy, x, mean, rstd, g, dres, dres_act, part, rows, C, \
-                       add, with_res)
+                       add, with_res, dmask, dscale)
     if (nj <= 2) G2_LNB(2);
     else if (nj <= 4) G2_LNB(4);
     else if (nj <= 6) G2_LNB(6);
@@ -581,12 +597,14 @@ static hipError_t ln_bwd_dispatch(const float* dy, const float* x, const float* 
 
 hipError_t layernorm_bwd(int dtype, const float* dy, const float* x, const float* mean, const float* rstd,
                          const float* g, float* dres, void* dres_act, float* part, int part_rows, int64_t rows, int C,
-                         int add, int with_res, hipStream_t s) {
+                         int add, int with_res, hipStream_t s, const uint8_t* dmask, float dscale) {
     if (rows == 0) return hipSuccess;
     if (part_rows < ln_bwd_partial_rows(rows)) return hipErrorInvalidValue;
     if (dtype == GPT2_DTYPE_BF16)
-        return ln_bwd_dispatch<bf16_t>(dy, x, mean, rstd, g, dres, (bf16_t*)dres_act, part, rows, C, add, with_res, s);
-    return ln_bwd_dispatch<float>(dy, x, mean, rstd, g, dres, (float*)dres_act, part, rows, C, add, with_res, s);
+        return ln_bwd_dispatch<bf16_t>(dy, x, mean, rstd, g, dres, (bf16_t*)dres_act, part, rows, C, add, with_res, s,
+                                       dmask, dscale);
+    return ln_bwd_dispatch<float>(dy, x, mean, rstd, g, dres, (float*)dres_act, part, rows, C, add, with_res, s, dmask,
+                                  dscale);
 }
 
 // Column sums of partial rows into up to three outputs: out_a[c] (+)= sum_p

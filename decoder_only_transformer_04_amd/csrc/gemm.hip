@@ -50,6 +50,8 @@ struct GP {
     const float* ln_g;  // skinny products: A is fp32 and the operand is its LayerNorm (nullable)
     const float* ln_b;
     float ln_eps;
+    const uint8_t* dmask;  // EPI_RESID: dropout keep bits of the branch (nullable)
+    float dscale;
 };
 
 // ------------------------------------------------------------------ epilogue
@@ -66,7 +68,12 @@ __device__ __forceinline__ void epi_apply(const GP& p, int64_t m, int n, float v
         Act<T>::st((T*)p.C2, m * p.ldc2 + n, g);
     } else if constexpr (EPI == EPI_RESID) {
         float r = ((const float*)p.R)[m * p.ldr + n];
-        ((float*)p.C)[m * p.ldc + n] = r + v + bias;
+        float y = v + bias;
+        if (p.dmask) {
+            const int64_t e = m * p.N + n;
+            y = ((p.dmask[e >> 3] >> (e & 7)) & 1) ? y * p.dscale : 0.0f;
+        }
+        ((float*)p.C)[m * p.ldc + n] = r + y;
     } else if constexpr (EPI == EPI_F32) {
         float* c = (float*)p.C + (int64_t)blockIdx.z * p.c_split_stride + m * p.ldc + n;
         float o = p.alpha * v;
@@ -130,8 +137,15 @@ __device__ __forceinline__ void epi_apply8(const GP& p, int64_t m, int n, const 
     } else if constexpr (EPI == EPI_RESID) {
         float r[8];
         ld8f((const float*)p.R + m * p.ldr + n, r);
+        if (p.dmask) {
+            // eight consecutive elements from a multiple of 8 (N % 8 == 0): one byte of keep bits
+            const uint32_t kb = p.dmask[(m * p.N + n) >> 3];
 #pragma unroll
-        for (int k = 0; k < 8; ++k) o[k] = r[k] + v[k] + bv[k];
+            for (int k = 0; k < 8; ++k) o[k] = r[k] + (((kb >> k) & 1) ? (v[k] + bv[k]) * p.dscale : 0.0f);
+        } else {
+#pragma unroll
+            for (int k = 0; k < 8; ++k) o[k] = r[k] + v[k] + bv[k];
+        }
         st8f((float*)p.C + m * p.ldc + n, o);
     } else if constexpr (EPI == EPI_F32) {
         float* c = (float*)p.C + (int64_t)blockIdx.z * p.c_split_stride + m * p.ldc + n;
@@ -1071,6 +1085,8 @@ hipError_t gemm(int dtype, const GemmArgs& a, hipStream_t s) {
     p.ln_g = a.ln_g;
     p.ln_b = a.ln_b;
     p.ln_eps = a.ln_eps;
+    p.dmask = a.epi == EPI_RESID ? a.dmask : nullptr;
+    p.dscale = a.dscale;
     if (a.M <= 0 || a.N <= 0) return hipSuccess;
     if (a.K <= 0) {
         // empty contraction: the product is zero

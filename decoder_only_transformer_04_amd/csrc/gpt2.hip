@@ -45,6 +45,7 @@ struct gpt2_ctx {
     bool cjob_batched = false;
     // optional per-launch timing (gpt2_timing_begin/end)
     bool timing = false;
+    uint64_t drop_seed = 0;  // key of the dropout masks (gpt2_set_dropout_seed)
     std::string timing_prefix;
     std::vector<hipEvent_t> ev_pool;
     size_t ev_used = 0;
@@ -202,6 +203,19 @@ const void* wptr(gpt2_ctx* x, int64_t off) {
 const float* pf(gpt2_ctx* x, int64_t off) { return off < 0 ? nullptr : x->bufs.params + off; }
 float* gf(gpt2_ctx* x, int64_t off) { return off < 0 ? nullptr : x->bufs.grads + off; }
 
+// training-mode dropout: masks in the arena, keep threshold and scale from p
+bool dropping(const gpt2_ctx* x) { return x->ap.mode == GPT2_MODE_TRAIN && x->cfg.dropout > 0.0f; }
+float drop_scale(const gpt2_ctx* x) { return (float)(1.0 / (1.0 - (double)x->cfg.dropout)); }
+uint32_t drop_threshold(const gpt2_ctx* x) {
+    return (uint32_t)std::min(std::floor((double)x->cfg.dropout * 65536.0 + 0.5), 65536.0);
+}
+const uint64_t* dm_attn(gpt2_ctx* x, int l) {
+    return dropping(x) ? at<uint64_t>(x, x->ap.dm_attn) + (int64_t)l * x->ap.dm_attn_words : nullptr;
+}
+const uint8_t* dm_res(gpt2_ctx* x, const Region& r, int l) {
+    return dropping(x) ? (const uint8_t*)(at<uint64_t>(x, r) + (int64_t)l * x->ap.dm_res_words) : nullptr;
+}
+
 GemmArgs gemm_args() {
     GemmArgs a;
     std::memset(&a, 0, sizeof(a));
@@ -211,7 +225,7 @@ GemmArgs gemm_args() {
 
 // Y[M,N] = X[M,K] W[N,K]^T with an epilogue, on stream s
 hipError_t linear_fwd_on(gpt2_ctx* x, hipStream_t s, int epi, int64_t M, int N, int K, const void* X, const void* W,
-                         const float* bias, void* Y, void* Y2, const void* R) {
+                         const float* bias, void* Y, void* Y2, const void* R, const uint8_t* dmask = nullptr) {
     GemmArgs a = gemm_args();
     a.M = M; a.N = N; a.K = K;
     a.A = X; a.lda = K; a.a_kc = true;
@@ -221,11 +235,13 @@ hipError_t linear_fwd_on(gpt2_ctx* x, hipStream_t s, int epi, int64_t M, int N, 
     a.C2 = Y2; a.ldc2 = N;
     a.R = R; a.ldr = N;
     a.gelu_erf = x->cfg.gelu_erf;
+    a.dmask = dmask;
+    a.dscale = drop_scale(x);
     return gemm(x->cfg.dtype, a, s);
 }
 hipError_t linear_fwd(gpt2_ctx* x, int epi, int64_t M, int N, int K, const void* X, const void* W, const float* bias,
-                      void* Y, void* Y2, const void* R) {
-    return linear_fwd_on(x, x->stream, epi, M, N, K, X, W, bias, Y, Y2, R);
+                      void* Y, void* Y2, const void* R, const uint8_t* dmask = nullptr) {
+    return linear_fwd_on(x, x->stream, epi, M, N, K, X, W, bias, Y, Y2, R, dmask);
 }
 // Y = LayerNorm(X; g, b) W^T with an epilogue, X fp32, for a few rows (the
 // skinny product forms the LayerNorm while staging X)
@@ -442,6 +458,18 @@ int gpt2_forward(gpt2_ctx* x, const int32_t* d_idx, const int32_t* d_targets, fl
         G2_TRY(hipMemcpyAsync(at<int32_t>(x, x->idx_save), d_idx, (size_t)M * 4, hipMemcpyDeviceToDevice, s));
         x->have_idx = true;
     }
+    const bool drop = dropping(x);
+    const float dsc = drop_scale(x);
+    if (drop) {
+        // every layer's keep masks for this step, read again by the backward
+        const uint32_t thr = drop_threshold(x);
+        G2_T("dropout.mask", dropout_masks_attn(at<uint64_t>(x, ap.dm_attn), c.n_layer, ap.dm_attn_words, ap.B * H, T,
+                                                ap.dm_tw, x->drop_seed, thr, s));
+        G2_T("dropout.mask", dropout_masks_res(at<uint64_t>(x, ap.dm_proj), c.n_layer, ap.dm_res_words,
+                                               (int64_t)M * C, DROP_PROJ, x->drop_seed, thr, s));
+        G2_T("dropout.mask", dropout_masks_res(at<uint64_t>(x, ap.dm_fc2), c.n_layer, ap.dm_res_words,
+                                               (int64_t)M * C, DROP_FC2, x->drop_seed, thr, s));
+    }
     G2_T("embed.fwd", encoder_fwd(dt, d_idx, pf(x, x->pl.wte), nullptr, pf(x, x->pl.wpe), nullptr, at<float>(x, ap.x[0]), M, T, C,
                        c.vocab, status, s));
     for (int l = 0; l < c.n_layer; ++l) {
@@ -455,15 +483,15 @@ int gpt2_forward(gpt2_ctx* x, const int32_t* d_idx, const int32_t* d_targets, fl
         G2_T("gemm.fwd.qkv", linear_fwd(x, EPI_STORE, M, 3 * C, C, at<char>(x, ap.ln1[sl]), wptr(x, w.w_qkv), pf(x, w.b_qkv),
                           at<char>(x, ap.qkv[sl]), nullptr, nullptr));
         G2_T("attn.fwd", attention_fwd(dt, ap.B, T, C, H, at<char>(x, ap.qkv[sl]), at<char>(x, ap.att[sl]),
-                             at<float>(x, ap.lse[sl]), s));
+                             at<float>(x, ap.lse[sl]), s, dm_attn(x, l), dsc));
         G2_T("gemm.fwd.proj", linear_fwd(x, EPI_RESID, M, C, C, at<char>(x, ap.att[sl]), wptr(x, w.w_proj), pf(x, w.b_proj), xmid,
-                          nullptr, xin));
+                          nullptr, xin, dm_res(x, ap.dm_proj, l)));
         G2_T("ln.fwd", layernorm_fwd(dt, xmid, pf(x, w.ln2_g), pf(x, w.ln2_b), c.ln_eps, at<char>(x, ap.ln2[sl]),
                              at<float>(x, ap.m2[sl]), at<float>(x, ap.r2[sl]), M, C, s));
         G2_T("gemm.fwd.fc", linear_fwd(x, EPI_GELU, M, F, C, at<char>(x, ap.ln2[sl]), wptr(x, w.w_fc), pf(x, w.b_fc),
                           at<char>(x, ap.fch[sl]), at<char>(x, ap.fcg[sl]), nullptr));
         G2_T("gemm.fwd.fc2", linear_fwd(x, EPI_RESID, M, C, F, at<char>(x, ap.fcg[sl]), wptr(x, w.w_fc2), pf(x, w.b_fc2), xout,
-                          nullptr, xmid));
+                          nullptr, xmid, dm_res(x, ap.dm_fc2, l)));
     }
     G2_T("ln.fwd", layernorm_fwd(dt, at<float>(x, ap.xL), pf(x, x->pl.lnf_g), pf(x, x->pl.lnf_b), c.ln_eps,
                          at<char>(x, ap.xf), at<float>(x, ap.mf), at<float>(x, ap.rf), M, C, s));
@@ -500,9 +528,14 @@ int gpt2_backward(gpt2_ctx* x, float loss_scale, int32_t zero_grads) {
     const float alpha = loss_scale / (float)M;  // d(mean loss)/dlogits = (softmax - onehot) / (B*T)
     float* dres = at<float>(x, ap.dres);
     // LayerNorm-f and LN1 backward write the activation copy of the residual
-    // gradient to dres_a, LN2 backward to dres_b (fp32: both are dres itself)
-    void* dres_a = bf ? (void*)at<char>(x, ap.dres_act) : (void*)dres;
-    void* dres_b = bf ? (void*)at<char>(x, ap.dres_act2) : (void*)dres;
+    // gradient to dres_a, LN2 backward to dres_b (fp32: both are dres itself).
+    // With dropout the copies are of the dropped gradient (the one reaching the
+    // fc2 or projection output), so fp32 writes them too.
+    const bool drop = dropping(x);
+    const float dsc = drop_scale(x);
+    const bool copy = bf || drop;
+    void* dres_a = copy ? (void*)at<char>(x, ap.dres_act) : (void*)dres;
+    void* dres_b = copy ? (void*)at<char>(x, ap.dres_act2) : (void*)dres;
     float* dtmp = at<float>(x, ap.dtmp);
     // every LayerNorm backward and bias leaves its column-sum partials in a buffer
     // of its own; run_colsum_jobs reduces them all at the end
@@ -546,8 +579,8 @@ int gpt2_backward(gpt2_ctx* x, float loss_scale, int32_t zero_grads) {
     const int Ltop = c.n_layer - 1;
     float* b_fc2_top = gf(x, pl.layer[Ltop].b_fc2);
     G2_T("ln.bwd", layernorm_bwd(dt, dtmp, at<float>(x, ap.xL), at<float>(x, ap.mf), at<float>(x, ap.rf), pf(x, pl.lnf_g),
-                         dres, bf ? dres_a : nullptr, at<float>(x, ap.ln_part[0]), ap.ln_part_rows, M, C, 0,
-                         b_fc2_top != nullptr, s));
+                         dres, copy ? dres_a : nullptr, at<float>(x, ap.ln_part[0]), ap.ln_part_rows, M, C, 0,
+                         b_fc2_top != nullptr, s, dm_res(x, ap.dm_fc2, Ltop), dsc));
     for (int l = c.n_layer - 1; l >= 0; --l) {
         const LayerW& w = pl.layer[l];
         const int k = c.n_layer - 1 - l;
@@ -575,8 +608,8 @@ int gpt2_backward(gpt2_ctx* x, float loss_scale, int32_t zero_grads) {
         float* b_proj = gf(x, w.b_proj);
         if (above) G2_TRY(join(slot(l + 1, W_PROJ)));  // dres_b is read by the projection weight gradient above
         G2_T("ln.bwd", layernorm_bwd(dt, dtmp, at<float>(x, ap.xmid[l]), at<float>(x, ap.m2[l]), at<float>(x, ap.r2[l]),
-                             pf(x, w.ln2_g), dres, bf ? dres_b : nullptr, at<float>(x, ap.ln_part[1 + 2 * k]),
-                             ap.ln_part_rows, M, C, 1, b_proj != nullptr, s));
+                             pf(x, w.ln2_g), dres, copy ? dres_b : nullptr, at<float>(x, ap.ln_part[1 + 2 * k]),
+                             ap.ln_part_rows, M, C, 1, b_proj != nullptr, s, dm_res(x, ap.dm_proj, l), dsc));
         // x_mid = x_in + proj(attn(ln1(x_in)))
         G2_TRY(fork(slot(l, W_PROJ)));
         G2_TS("gemm.wgrad.proj", ws, linear_wgrad(dt, ws, M, C, C, dres_b, C, at<char>(x, ap.att[l]), gf(x, w.w_proj), acc, 1.0f,
@@ -592,12 +625,15 @@ int gpt2_backward(gpt2_ctx* x, float loss_scale, int32_t zero_grads) {
             char* dqkv = at<char>(x, ap.dqkv);
             float* attD = at<float>(x, ap.attD);
             if (above) G2_TRY(join(slot(l + 1, W_QKV)));  // dqkv is read by the qkv weight gradient above
+            const uint64_t* dma = dm_attn(x, l);
             if (attention_bwd_staged(dt, C, H)) {
-                G2_T("attn.bwd.dq", attention_bwd(dt, ap.B, T, C, H, qkv_l, att_l, lse_l, datt, dqkv, attD, s, ATT_BWD_DQ));
+                G2_T("attn.bwd.dq",
+                     attention_bwd(dt, ap.B, T, C, H, qkv_l, att_l, lse_l, datt, dqkv, attD, s, ATT_BWD_DQ, dma, dsc));
                 G2_T("attn.bwd.dkdv",
-                     attention_bwd(dt, ap.B, T, C, H, qkv_l, att_l, lse_l, datt, dqkv, attD, s, ATT_BWD_DKDV));
+                     attention_bwd(dt, ap.B, T, C, H, qkv_l, att_l, lse_l, datt, dqkv, attD, s, ATT_BWD_DKDV, dma, dsc));
             } else {
-                G2_T("attn.bwd", attention_bwd(dt, ap.B, T, C, H, qkv_l, att_l, lse_l, datt, dqkv, attD, s));
+                G2_T("attn.bwd",
+                     attention_bwd(dt, ap.B, T, C, H, qkv_l, att_l, lse_l, datt, dqkv, attD, s, ATT_BWD_ALL, dma, dsc));
             }
         }
         G2_TRY(fork(slot(l, W_QKV)));
@@ -611,8 +647,9 @@ int gpt2_backward(gpt2_ctx* x, float loss_scale, int32_t zero_grads) {
         float* b_fc2_below = l > 0 ? gf(x, pl.layer[l - 1].b_fc2) : nullptr;
         G2_TRY(join(slot(l, W_FC2)));  // dres_a is read by this layer's fc2 weight gradient
         G2_T("ln.bwd", layernorm_bwd(dt, dtmp, at<float>(x, ap.x[l]), at<float>(x, ap.m1[l]), at<float>(x, ap.r1[l]),
-                             pf(x, w.ln1_g), dres, bf ? dres_a : nullptr, at<float>(x, ap.ln_part[2 + 2 * k]),
-                             ap.ln_part_rows, M, C, 1, b_fc2_below != nullptr, s));
+                             pf(x, w.ln1_g), dres, copy ? dres_a : nullptr, at<float>(x, ap.ln_part[2 + 2 * k]),
+                             ap.ln_part_rows, M, C, 1, b_fc2_below != nullptr, s,
+                             l > 0 ? dm_res(x, ap.dm_fc2, l - 1) : nullptr, dsc));
     }
     // the embedding backward adds into dwte after the head's weight gradient;
     // untied, nothing else writes dwte, so an overwriting pass clears it first
@@ -802,6 +839,13 @@ int gpt2_generate(gpt2_ctx* x, const int32_t* d_prompt, int32_t T0, int32_t n_ne
     return GPT2_OK;
 }
 
+int gpt2_set_dropout_seed(gpt2_ctx* x, uint64_t seed) {
+    if (!x) return GPT2_EINVAL;
+    if (!dropping(x)) return GPT2_ESTATE;
+    x->drop_seed = seed;
+    return GPT2_OK;
+}
+
 int gpt2_sync_status(gpt2_ctx* x, uint32_t* bits) {
     if (!x) return GPT2_EINVAL;
     uint32_t v = 0;
@@ -869,6 +913,16 @@ int gpt2_arena_tensor(const gpt2_ctx* cx, const char* name, int32_t layer, size_
     if (n == "loss_rows") { *byte_offset = ap.loss_rows.off; *elem_bytes = 4; *rows = ap.M; *cols = 1; return GPT2_OK; }
     if (n == "logits") {
         *byte_offset = ap.logits.off; *elem_bytes = ab; *rows = ap.M; *cols = cx->pl.vocab_pad;
+        return GPT2_OK;
+    }
+    // dropout keep bits of the last TRAIN forward (64-bit words)
+    if (n == "drop_attn" || n == "drop_proj" || n == "drop_fc2") {
+        if (!dropping(cx) || layer < 0 || layer >= cx->cfg.n_layer) return GPT2_EINVAL;
+        const bool att = n == "drop_attn";
+        const int64_t words = att ? ap.dm_attn_words : ap.dm_res_words;
+        const Region& r = att ? ap.dm_attn : n == "drop_proj" ? ap.dm_proj : ap.dm_fc2;
+        *byte_offset = r.off + (size_t)layer * words * 8; *elem_bytes = 8;
+        *rows = att ? words / ap.dm_tw : words; *cols = att ? ap.dm_tw : 1;
         return GPT2_OK;
     }
     return GPT2_EINVAL;

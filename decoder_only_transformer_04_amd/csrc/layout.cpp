@@ -20,6 +20,7 @@ int validate_config(const gpt2_config* c) {
     if (c->dtype != GPT2_DTYPE_F32 && c->dtype != GPT2_DTYPE_BF16) return GPT2_EINVAL;
     if (!(c->ln_eps > 0.0f) || !std::isfinite(c->ln_eps)) return GPT2_EINVAL;
     if ((c->gelu_erf != 0 && c->gelu_erf != 1) || (c->untied_head != 0 && c->untied_head != 1)) return GPT2_EINVAL;
+    if (!(c->dropout >= 0.0f && c->dropout < 1.0f)) return GPT2_EINVAL;
     const int d = c->n_embd / c->n_head;
     if (d > 128) return GPT2_EINVAL;
     if (c->dtype == GPT2_DTYPE_BF16) {
@@ -156,6 +157,14 @@ ArenaPlan make_arena_plan(const gpt2_config& c, const ParamLayout& pl, int B, in
         a.enc_segstart = take(Vp * 4);
         a.enc_order = take(M * 4);
         a.enc_segtok = take(M * 4);
+        if (c.dropout > 0.0f) {
+            a.dm_tw = (T + 63) / 64;
+            a.dm_attn_words = (int64_t)B * H * T * a.dm_tw;
+            a.dm_res_words = (int64_t)((M * C + 63) / 64);
+            a.dm_attn = take((size_t)c.n_layer * a.dm_attn_words * 8);
+            a.dm_proj = take((size_t)c.n_layer * a.dm_res_words * 8);
+            a.dm_fc2 = take((size_t)c.n_layer * a.dm_res_words * 8);
+        }
     }
     a.total = off;
     return a;

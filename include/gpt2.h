@@ -83,6 +83,15 @@ typedef struct gpt2_config {
      *                (0: the head reuses wte). Other values are GPT2_EINVAL. */
     int32_t gelu_erf;
     int32_t untied_head;
+    /* Training-mode dropout probability p in [0, 1) (minigpt's cfg.dropout; 0:
+     * none, the GPT-2 readings). With p > 0 a GPT2_MODE_TRAIN forward drops, as
+     * minigpt.py's block does in model.train(): every head's attention weights
+     * after the softmax, the attention projection's output and the FeedForward's
+     * output, each element kept with probability 1 - round(65536 p) / 65536 and
+     * scaled by 1 / (1 - p); the backward uses the same masks. The masks are
+     * Philox4x32-10 draws under the key gpt2_set_dropout_seed sets (the element
+     * numbering is documented there). EVAL and GENERATE contexts never drop. */
+    float dropout;
 } gpt2_config;
 
 /* One named parameter tensor in the flat buffers. */
@@ -142,6 +151,16 @@ int gpt2_init(gpt2_ctx** out, const gpt2_config* cfg, const gpt2_buffers* bufs, 
 /* Re-derive the low-precision weight copies after the caller rewrote params
  * (loading a checkpoint, re-synchronising with another implementation). */
 int gpt2_refresh_weights(gpt2_ctx* ctx);
+
+/* Key of the dropout masks of the following TRAIN forwards (default 0); change
+ * it every step for fresh masks. Element e of site s (0: attention weights, e =
+ * ((b H + h) T + i) T + j for query i, key j of head h in sequence b; 1: the
+ * projection output and 2: the FeedForward output, e = m C + c for row m = b T +
+ * t) in layer l is kept when 16-bit half e % 8 (low half of word 0 first) of
+ * Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC 2011) at counter (e / 8 low and
+ * high words, s, l) under key (seed low, seed high) is >= round(65536 p).
+ * GPT2_ESTATE unless the context is a TRAIN context with p > 0. */
+int gpt2_set_dropout_seed(gpt2_ctx* ctx, uint64_t seed);
 
 /* Forward pass over d_idx [B*T] int32 (row-major [B][T]). With d_targets [B*T]
  * it also writes the mean cross-entropy over all B*T positions to *d_loss (one
@@ -233,7 +252,13 @@ int gpt2_timing_end(gpt2_ctx* ctx, float* total_ms, int32_t* launches);
  * "logits", "loss_rows"}; layer ignored for the last three. *elem_bytes receives
  * 2 or 4. In TRAIN mode "logits" holds the logits gradient after a forward with
  * targets. "fcg" is the GELU output of the MLP's first layer and "fch" the GELU
- * derivative at its pre-activation (the factor the backward applies). */
+ * derivative at its pre-activation (the factor the backward applies). With
+ * dropout, "drop_attn" (rows B H T, cols ceil(T / 64)), "drop_proj" and
+ * "drop_fc2" (ceil(B T C / 64) rows, 1 col) are the layer's keep bits of the last
+ * TRAIN forward as 8-byte words, bit k of word w the element numbered as in
+ * gpt2_set_dropout_seed (attention: key 64 w' + k of row (b H + h) T + i, w' the
+ * column; residual sites: element 64 w + k); attention bits past the diagonal
+ * are zero. */
 int gpt2_arena_tensor(const gpt2_ctx* ctx, const char* name, int32_t layer, size_t* byte_offset,
                       int32_t* elem_bytes, int64_t* rows, int64_t* cols);
 

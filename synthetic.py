@@ -37,6 +37,7 @@ class Model:
     ln_eps: float = 1e-5
     gelu_erf: bool = False  # exact erf GELU (nn.GELU() default) instead of the tanh form
     untied: bool = False    # separate lm_head [V, C] instead of the head tied to wte
+    dropout: float = 0.0    # training-mode dropout probability (the minigpt page's literal model: 0.1)
 
 
 @dataclasses.dataclass(frozen=True)

@@ -48,15 +48,16 @@ def cosine(a, r) -> float:
     return float(a @ r / (na * nr))
 
 
-def ocfg(o, m: syn.Model):
+def ocfg(o, m: syn.Model, seed: int = 0):
+    # the dropout probability as the GPU's fp32 config holds it
     return o.make_cfg(m.vocab, m.block_size, m.n_embd, m.n_head, m.n_layer, m.mlp_hidden, m.bias, m.ln_eps,
-                      gelu_erf=m.gelu_erf, untied=m.untied)
+                      gelu_erf=m.gelu_erf, untied=m.untied, dropout=float(np.float32(m.dropout)), seed=seed)
 
 
 def gcfg(b, m: syn.Model, dtype: str):
     return b.make_config(m.vocab, m.block_size, m.n_embd, m.n_head, m.n_layer, m.mlp_hidden, m.bias,
                          b.DTYPE_F32 if dtype == "f32" else b.DTYPE_BF16, m.ln_eps, gelu_erf=m.gelu_erf,
-                         untied_head=m.untied)
+                         untied_head=m.untied, dropout=m.dropout)
 
 
 def gpu_model(b, m: syn.Model, dtype: str, B: int, T: int, named: dict, mode=None):
@@ -77,8 +78,8 @@ def gpu_named_params(g) -> dict:
     return {k: np.array(v) for k, v in g.named(flat).items()}
 
 
-def oracle_grads(o, m: syn.Model, named: dict, x, y, dtype=np.float64, loss_scale=1.0):
-    cfg = ocfg(o, m)
+def oracle_grads(o, m: syn.Model, named: dict, x, y, dtype=np.float64, loss_scale=1.0, seed=0):
+    cfg = ocfg(o, m, seed)
     p = o.pack(cfg, named, dtype)
     g = np.zeros_like(p)
     B, T = x.shape

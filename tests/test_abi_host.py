@@ -108,8 +108,28 @@ def test_invalid_configs_rejected(b):
         for k, v in kw.items():
             setattr(c, k, v)
         assert b.lib().gpt2_query_sizes(ct.byref(c), 1, 64, 0, None, None) == b.GPT2_EINVAL
+    # dropout: a probability in [0, 1)
+    for p in (-0.1, 1.0, float("nan")):
+        c = b.make_config(65, 64, 128, 4, 4, 512, 0, b.DTYPE_F32, dropout=p)
+        assert b.lib().gpt2_query_sizes(ct.byref(c), 1, 64, 0, None, None) == b.GPT2_EINVAL
     # shorter sequences than block_size are valid
     assert b.lib().gpt2_query_sizes(ct.byref(ok), 3, 37, 0, None, None) == 0
+
+
+def test_dropout_masks_only_in_training_arena(b):
+    """The keep masks (attention: B H T ceil(T / 64) words; each residual site:
+    ceil(B T C / 64) words, per layer) are planned for TRAIN contexts only."""
+    m = syn.WORKLOADS["gpt2_124m"].model
+    plain = cfg_of(b, m, "bf16")
+    drop = cfg_of(b, m, "bf16")
+    drop.dropout = 0.1
+    B, T = 12, 1024
+    _, tr0 = b.query_sizes(plain, B, T, b.MODE_TRAIN)
+    _, tr1 = b.query_sizes(drop, B, T, b.MODE_TRAIN)
+    words = B * m.n_head * T * (T // 64) + 2 * (B * T * m.n_embd // 64)
+    assert tr1 - tr0 == m.n_layer * words * 8
+    for mode in (b.MODE_EVAL,):
+        assert b.query_sizes(plain, B, T, mode)[1] == b.query_sizes(drop, B, T, mode)[1]
 
 
 def test_init_rejects_null_and_small_arena(b):

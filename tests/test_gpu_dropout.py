@@ -1,0 +1,220 @@
+"""Training-mode dropout of the HIP step against the oracle (GPU required).
+
+The keep masks are bit-exact against the oracle's Philox4x32-10 draws (they are
+integer work). Given the same masks the step is the plain step with a
+different elementwise pattern, so the tolerances are the step's own: fp32 loss
+relative error <= 1e-5 and per-tensor gradient max|g - r| / max|r| <= 1e-3; bf16
+loss absolute error <= 2e-2 and per-tensor gradient cosine >= 0.999 (double).
+"""
+import dataclasses
+
+import numpy as np
+import pytest
+
+import synthetic as syn
+from gpu_helpers import cosine, gpu_model, gpu_named_grads, gpu_named_params, max_rel, oracle_grads, say
+
+pytestmark = pytest.mark.gpu
+
+P = 0.1
+SEED = 0x0123456789ABCDEF  # both key words non-zero
+
+
+@pytest.fixture(scope="module")
+def b():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    from decoder_only_transformer_04_amd import binding
+    binding.lib()
+    return binding
+
+
+def with_dropout(m: syn.Model, p=P) -> syn.Model:
+    return dataclasses.replace(m, dropout=p)
+
+
+def dev_tokens(x):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.int32).reshape(-1)).cuda()
+
+
+def step(g, x, y, seed):
+    import torch
+    g.set_dropout_seed(seed)
+    g.forward(dev_tokens(x), dev_tokens(y))
+    g.backward(1.0, True)
+    torch.cuda.synchronize()
+    return float(g.loss.item())
+
+
+def pack_words(flags: np.ndarray) -> np.ndarray:
+    """uint64 words of 0/1 flags along the last axis (padded to 64), bit k = flag k."""
+    n = flags.shape[-1]
+    w = (n + 63) // 64
+    pad = np.zeros(flags.shape[:-1] + (w * 64,), dtype=np.uint8)
+    pad[..., :n] = flags
+    return np.packbits(pad, axis=-1, bitorder="little").view("<u8")
+
+
+def oracle_attn_words(oracle, p, seed, layer, rows, T):
+    """Words of the attention keep bits for the given rows r = (b H + h) T + i."""
+    out = []
+    for r in rows:
+        i = r % T
+        k = oracle.dropout_keep(p, seed, oracle.DROP_ATTN, layer, T, e0=r * T)
+        k[i + 1:] = 0  # bits past the diagonal are stored as zero
+        out.append(pack_words(k))
+    return np.stack(out)
+
+
+def gpu_words(g, name, layer):
+    return g.arena_tensor(name, layer).cpu().numpy().view(np.uint64)
+
+
+def test_masks_bit_exact_ragged(b, oracle):
+    """T = 50 (not a multiple of 8 or 64): every layer's three masks equal the
+    oracle's keep flags bit for bit."""
+    m = with_dropout(syn.WORKLOADS["tiny_f32"].model)
+    B, T = 3, 50
+    say(f"dropout masks tiny_f32 B={B} T={T}")
+    named = syn.init_params(m)
+    x, y = syn.batch(syn.WORKLOADS["tiny_f32"], B=B, T=T)
+    g = gpu_model(b, m, "f32", B, T, named)
+    step(g, x, y, SEED)
+    p32 = float(np.float32(P))
+    BH = B * m.n_head
+    for layer in range(m.n_layer):
+        ga = gpu_words(g, "drop_attn", layer)
+        assert ga.shape == (BH * T, 1)
+        keep = oracle.dropout_keep(p32, SEED, oracle.DROP_ATTN, layer, BH * T * T).reshape(BH * T, T)
+        keep = keep * np.tril(np.ones((T, T), np.uint8))[np.arange(BH * T) % T]
+        np.testing.assert_array_equal(ga, pack_words(keep))
+        for name, site in (("drop_proj", oracle.DROP_PROJ), ("drop_fc2", oracle.DROP_FC2)):
+            k = oracle.dropout_keep(p32, SEED, site, layer, B * T * m.n_embd)
+            np.testing.assert_array_equal(gpu_words(g, name, layer).ravel(), pack_words(k[None, :]).ravel())
+    assert g.sync_status() == 0
+
+
+@pytest.mark.parametrize("T", [64, 50])
+def test_dropout_f32_step_matches_oracle(b, oracle, T):
+    """fp32 (scalar attention kernels, head size 32): loss and every gradient."""
+    m = with_dropout(syn.WORKLOADS["tiny_f32"].model)
+    B = 2
+    say(f"dropout tiny_f32 B={B} T={T}")
+    named = syn.init_params(m)
+    x, y = syn.batch(syn.WORKLOADS["tiny_f32"], B=B, T=T)
+    g = gpu_model(b, m, "f32", B, T, named)
+    loss = step(g, x, y, SEED)
+    rloss, rg = oracle_grads(oracle, m, named, x, y, seed=SEED)
+    assert abs(loss - rloss) <= 1e-5 * abs(rloss), (loss, rloss)
+    gg = gpu_named_grads(g)
+    for k, r in rg.items():
+        assert max_rel(gg[k], r) <= 1e-3, (k, max_rel(gg[k], r))
+    # without dropout the same inputs give a different loss
+    l0, _ = oracle_grads(oracle, with_dropout(m, 0.0), named, x[:1], y[:1])
+    assert l0 != oracle_grads(oracle, m, named, x[:1], y[:1], seed=SEED)[0]
+
+
+def test_dropout_bf16_literal_steps(b, oracle):
+    """The minigpt page's literal model (erf GELU, own lm_head, dropout 0.1) at
+    the char-level size, bf16 with the MFMA attention kernels (head size 64):
+    three AdamW steps with a fresh seed each; at every step the oracle, run at
+    the GPU's current parameters with the same seed, gives the loss and the
+    gradients."""
+    w = syn.WORKLOADS["char_bf16_literal"]
+    m = with_dropout(w.model)
+    B, T = 4, w.seq
+    named = syn.init_params(m)
+    g = gpu_model(b, m, "bf16", B, T, named)
+    worst = []
+    for s in range(3):
+        say(f"dropout char_bf16_literal step {s}")
+        x, y = syn.batch(w, step=s, B=B, T=T)
+        gpn = gpu_named_params(g)
+        loss = step(g, x, y, 1000 + s)
+        rloss, rg = oracle_grads(oracle, m, gpn, x, y, dtype=np.float32, seed=1000 + s)
+        assert abs(loss - rloss) <= 2e-2, (s, loss, rloss)
+        gg = gpu_named_grads(g)
+        cs = {k: cosine(gg[k], r) for k, r in rg.items()}
+        k = min(cs, key=cs.get)
+        assert cs[k] >= 0.999, (s, k, cs[k])
+        worst.append((k, round(cs[k], 6)))
+        g.adamw_step(w.lr, w.beta1, w.beta2, w.eps, w.weight_decay, s + 1)
+    assert g.sync_status() == 0
+    say("worst cosines", worst)
+
+
+def test_dropout_gpt2_124m_slice_bf16(b, oracle):
+    """The 124M shape (12 layers, V = 50257, biases) with dropout on one
+    128-token sequence: loss and every gradient tensor."""
+    m = with_dropout(syn.GPT2_124M)
+    say("dropout gpt2_124m B=1 T=128 bf16")
+    named = syn.init_params(m)
+    x, y = syn.batch(syn.WORKLOADS["gpt2_124m"], B=1, T=128)
+    g = gpu_model(b, m, "bf16", 1, 128, named)
+    loss = step(g, x, y, SEED)
+    rloss, rg = oracle_grads(oracle, m, named, x, y, dtype=np.float32, seed=SEED)
+    assert abs(loss - rloss) <= 2e-2, (loss, rloss)
+    gg = gpu_named_grads(g)
+    for k, r in rg.items():
+        assert cosine(gg[k], r) >= 0.999, (k, cosine(gg[k], r))
+
+
+def test_dropout_full_size_masks_sampled(b, oracle):
+    """At the benchmark's size (124M, 12 x 1024): sampled attention rows and
+    residual words of the first and last layer equal the oracle's, and the
+    step runs clean."""
+    m = with_dropout(syn.GPT2_124M)
+    B, T = 12, 1024
+    say("dropout gpt2_124m 12 x 1024 sampled masks")
+    w = syn.WORKLOADS["gpt2_124m"]
+    g = gpu_model(b, m, "bf16", B, T, syn.init_params(m))
+    x, y = syn.batch(w, B=B, T=T)
+    loss = step(g, x, y, SEED)
+    assert np.isfinite(loss)
+    p32 = float(np.float32(P))
+    rng = np.random.default_rng(3)
+    BH = B * m.n_head
+    rows = np.concatenate([[0, T - 1, BH * T - 1], rng.integers(0, BH * T, 13)])
+    res_words = rng.integers(0, (B * T * m.n_embd) // 64, 16)
+    for layer in (0, m.n_layer - 1):
+        ga = gpu_words(g, "drop_attn", layer)
+        np.testing.assert_array_equal(ga[rows], oracle_attn_words(oracle, p32, SEED, layer, rows, T))
+        for name, site in (("drop_proj", oracle.DROP_PROJ), ("drop_fc2", oracle.DROP_FC2)):
+            gr = gpu_words(g, name, layer).ravel()
+            for wd in res_words:
+                k = oracle.dropout_keep(p32, SEED, site, layer, 64, e0=int(wd) * 64)
+                assert gr[wd] == pack_words(k[None, :])[0, 0], (name, layer, wd)
+    assert g.sync_status() == 0
+
+
+def test_dropout_eval_seed_and_determinism(b):
+    """EVAL contexts never drop (same logits as the p = 0 model) and refuse a
+    seed; a TRAIN step is bit-identical for the same seed and differs for
+    another."""
+    import torch
+    base = syn.WORKLOADS["char_bf16"].model
+    m = with_dropout(base)
+    B, T = 2, 256
+    named = syn.init_params(m)
+    x, y = syn.batch(syn.WORKLOADS["char_bf16"], B=B, T=T)
+    outs, ctxs = [], []
+    for mm in (m, base):
+        e = gpu_model(b, mm, "bf16", B, T, named, mode=b.MODE_EVAL)
+        e.forward(dev_tokens(x), dev_tokens(y))
+        torch.cuda.synchronize()
+        outs.append(e.arena_tensor("logits").float().cpu())
+        ctxs.append(e)
+    assert torch.equal(outs[0], outs[1])
+    with pytest.raises(b.GPT2Error):
+        ctxs[0].set_dropout_seed(1)             # the dropout model in eval mode
+    g = gpu_model(b, m, "bf16", B, T, named)
+    l1 = step(g, x, y, 5)
+    g1 = g.grads.clone()
+    l2 = step(g, x, y, 5)
+    assert l1 == l2 and torch.equal(g1, g.grads)
+    l3 = step(g, x, y, 6)
+    assert l3 != l1
+    plain = gpu_model(b, base, "bf16", B, T, named)
+    with pytest.raises(b.GPT2Error):
+        plain.set_dropout_seed(1)               # no dropout configured
