@@ -113,6 +113,20 @@ __device__ __forceinline__ void att_wait_vmcnt() {
     static_assert(N >= 0 && N < 64, "vmcnt range");
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
+// keep words of one 64-key tile for the 32 query rows of wave w, streamed into
+// LDS like the K/V tiles (one 4-byte global_load_lds per wave: lane l fetches
+// half l % 2 of row l / 2's word), so they ride in the same vmcnt-ordered
+// stream as the tiles. dst: the ring slot's 128 words; rows past T read row T - 1.
+__device__ __forceinline__ void mask_dma(uint64_t* dst, const uint64_t* rows, int Tw, int kt, int r0, int T, int w,
+                                         int lane) {
+    const int row = min(r0 + 32 * w + (lane >> 1), T - 1);
+    const uint32_t* src = (const uint32_t*)(rows + (int64_t)row * Tw + kt) + (lane & 1);
+#if defined(__HIP_DEVICE_COMPILE__)
+    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
+                                     (G2_LDS void*)(dst + 32 * w), 4, 0, 0);
+#endif
+}
+
 // workgroup barrier ordering LDS only (a __syncthreads() would also drain the
 // DMA loads still in flight for later tiles)
 __device__ __forceinline__ void att_lds_barrier() {
@@ -196,11 +210,13 @@ constexpr float kLazy = 8.0f;
 #endif
 // three workgroups (waves per SIMD) per CU: registers capped at 168. K/V tiles
 // stream into a three-deep LDS ring (48 KB) by DMA, two tiles ahead.
+// (with dropout: two per CU, the keep bits' registers do not fit in 168)
 template <bool DROP>
-__global__ __launch_bounds__(256, G2_ATT_FWD_OCC) void attn_fwd_d64(const bf16_t* qkv, bf16_t* out, float* lse, int T,
+__global__ __launch_bounds__(256, DROP ? 2 : G2_ATT_FWD_OCC) void attn_fwd_d64(const bf16_t* qkv, bf16_t* out, float* lse, int T,
                                                                     int C, int H, float sl2, const uint64_t* dmask,
                                                                     int Tw, float dscale) {
     __shared__ __attribute__((aligned(16))) char smem[3][2][kTileBytes];
+    __shared__ __attribute__((aligned(16))) uint64_t smask[DROP ? 3 : 1][128];  // keep words per query row
     int qb, h, b;
     block_coords(T, H, true, qb, h, b);
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 5;
@@ -213,38 +229,38 @@ __global__ __launch_bounds__(256, G2_ATT_FWD_OCC) void attn_fwd_d64(const bf16_t
     const int qi = q0 + (lane & 31);
     const int kend = min(T, qb * 128 + 128);
     const int nkt = (kend + 63) / 64;
+    const uint64_t* mrows = DROP ? dmask + ((int64_t)b * H + h) * T * Tw : nullptr;
     TileDma dma;
     dma.init(w, lane);
     auto issue = [&](int kt) {
         char* buf = smem[kt % 3][0];
         dma.issue(buf, Kg, rs, kt * 64, T, w);
         dma.issue(buf + kTileBytes, Vg, rs, kt * 64, T, w);
+        if constexpr (DROP) mask_dma(smask[kt % 3], mrows, Tw, kt, qb * 128, T, w, lane);
     };
     issue(0);
     if (nkt > 1) issue(1);
     bf16x8 qf[4];
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) qf[kk] = load8(Qg + (int64_t)qi * rs + 16 * kk + 8 * g, qi < T);
-    // this lane's row of keep bits (query qi; rows past T read nothing)
-    const uint64_t* mrow = DROP ? dmask + (((int64_t)b * H + h) * T + min(qi, T - 1)) * Tw : nullptr;
     f32x16 o[2] = {zero16(), zero16()};
     // m is shared by the two half-waves (they hold different keys of the same
     // query); l is kept per half-wave and combined at the end
     float m = -INFINITY, l = 0.0f;
     for (int kt = 0; kt < nkt; ++kt) {
-        // tile kt has landed once at most the next tile's 4 loads are pending
-        // (the Q loads above were issued after tiles 0 and 1 and are waited for
-        // by the compiler before their first use)
-        if (kt + 1 < nkt) att_wait_vmcnt<4>();
+        // tile kt has landed once at most the next tile's 4 loads (5 with the
+        // keep words) are pending (the Q loads above were issued after tiles 0
+        // and 1 and are waited for by the compiler before their first use)
+        if (kt + 1 < nkt) att_wait_vmcnt<DROP ? 5 : 4>();
         else att_wait_vmcnt<0>();
         att_lds_barrier();  // every wave's share of tile kt is in LDS; tile kt-1's slot is free
+        uint64_t mw = 0;
+        if constexpr (DROP) mw = smask[kt % 3][32 * w + (lane & 31)];
         if (kt + 2 < nkt) issue(kt + 2);
         const int k0 = kt * 64;
         const char* Ks = smem[kt % 3][0];
         const char* Vs = smem[kt % 3][1];
         if (k0 <= q0 + 31) {
-            uint64_t mw = 0;
-            if constexpr (DROP) mw = mrow[kt];
             f32x16 s[2];
 #pragma unroll
             for (int kh = 0; kh < 2; ++kh) {
@@ -322,6 +338,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_d64(const bf16_t* qkv, const 
                                                        int H, float sl2, float scale, const uint64_t* dmask, int Tw,
                                                        float dscale) {
     __shared__ __attribute__((aligned(16))) char smem[3][2][kTileBytes];
+    __shared__ __attribute__((aligned(16))) uint64_t smask[DROP ? 3 : 1][128];  // keep words per query row
     int qb, h, b;
     block_coords(T, H, true, qb, h, b);
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 5;
@@ -336,13 +353,15 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_d64(const bf16_t* qkv, const 
     const bool qok = qi < T;
     const int kend = min(T, qb * 128 + 128);
     const int nkt = (kend + 63) / 64;
-    // K/V tiles stream into a three-deep LDS ring by DMA, two tiles ahead
+    const uint64_t* mrows = DROP ? dmask + ((int64_t)b * H + h) * T * Tw : nullptr;
+    // K/V tiles (and the keep words) stream into a three-deep LDS ring by DMA, two tiles ahead
     TileDma dma;
     dma.init(w, lane);
     auto issue = [&](int kt) {
         char* buf = smem[kt % 3][0];
         dma.issue(buf, Kg, rs, kt * 64, T, w);
         dma.issue(buf + kTileBytes, Vg, rs, kt * 64, T, w);
+        if constexpr (DROP) mask_dma(smask[kt % 3], mrows, Tw, kt, qb * 128, T, w, lane);
     };
     issue(0);
     if (nkt > 1) issue(1);
@@ -365,19 +384,18 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_d64(const bf16_t* qkv, const 
         Dbuf[lb + qi] = Dq;
         L2[lb + qi] = lse2;
     }
-    const uint64_t* mrow = DROP ? dmask + (lb + min(qi, T - 1)) * Tw : nullptr;
     f32x16 dq[2] = {zero16(), zero16()};
     for (int kt = 0; kt < nkt; ++kt) {
-        if (kt + 1 < nkt) att_wait_vmcnt<4>();
+        if (kt + 1 < nkt) att_wait_vmcnt<DROP ? 5 : 4>();
         else att_wait_vmcnt<0>();
         att_lds_barrier();  // every wave's share of tile kt is in LDS; tile kt-1's slot is free
+        uint64_t mw = 0;
+        if constexpr (DROP) mw = smask[kt % 3][32 * w + (lane & 31)];
         if (kt + 2 < nkt) issue(kt + 2);
         const int k0 = kt * 64;
         const char* Ks = smem[kt % 3][0];
         const char* Vs = smem[kt % 3][1];
         if (k0 <= q0 + 31) {
-            uint64_t mw = 0;
-            if constexpr (DROP) mw = mrow[kt];
             f32x16 s[2], dp[2];
 #pragma unroll
             for (int kh = 0; kh < 2; ++kh) {

@@ -195,14 +195,15 @@ hipError_t attention_bwd(int dtype, int B, int T, int C, int H, const void* qkv,
 // element e of site `site`, layer l takes 16-bit half e % 8 (low half of word 0
 // first) of the generator at counter (e / 8 low, e / 8 high, site, l) and is
 // kept when that half is >= thr (round(p 65536)). Bits are written LSB-first,
-// 64 per word, one block of words_per_layer words per layer.
+// 64 per word, one block of words_per_layer words per layer, for layers
+// layer0 .. layer0 + L - 1 (bits points at layer0's block).
 enum { DROP_ATTN = 0, DROP_PROJ = 1, DROP_FC2 = 2 };
 // attention site: e = (bh T + i) T + j, stored at bit j % 64 of word (bh T + i) Tw + j / 64;
 // words wholly above the diagonal (64 (j / 64) > i) are written as zero
-hipError_t dropout_masks_attn(uint64_t* bits, int L, int64_t words_per_layer, int BH, int T, int Tw, uint64_t seed,
-                              uint32_t thr, hipStream_t s);
+hipError_t dropout_masks_attn(uint64_t* bits, int layer0, int L, int64_t words_per_layer, int BH, int T, int Tw,
+                              uint64_t seed, uint32_t thr, hipStream_t s);
 // residual sites: e = m C + c over n_elem elements, stored at bit e % 64 of word e / 64
-hipError_t dropout_masks_res(uint64_t* bits, int L, int64_t words_per_layer, int64_t n_elem, int site,
+hipError_t dropout_masks_res(uint64_t* bits, int layer0, int L, int64_t words_per_layer, int64_t n_elem, int site,
                              uint64_t seed, uint32_t thr, hipStream_t s);
 hipError_t cross_entropy(int dtype, void* logits, int64_t rows, int V, int ld, const int32_t* targets,
                          float* loss_rows, int32_t* argmax, int write_grad, uint32_t* status, hipStream_t s);

@@ -23,14 +23,15 @@ __device__ __forceinline__ void philox4x32_10(uint32_t c0, uint32_t c1, uint32_t
                                               uint32_t k1, uint32_t (&r)[4]) {
 #pragma unroll
     for (int i = 0; i < 10; ++i) {
-        const uint32_t lo0 = 0xD2511F53u * c0, hi0 = __umulhi(0xD2511F53u, c0);
-        const uint32_t lo1 = 0xCD9E8D57u * c2, hi1 = __umulhi(0xCD9E8D57u, c2);
-        const uint32_t n0 = hi1 ^ c1 ^ k0;
-        const uint32_t n2 = hi0 ^ c3 ^ k1;
+        // one 32 x 32 -> 64-bit product per multiplication (v_mad_u64_u32)
+        const uint64_t p0 = (uint64_t)0xD2511F53u * c0;
+        const uint64_t p1 = (uint64_t)0xCD9E8D57u * c2;
+        const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0;
+        const uint32_t n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
         c0 = n0;
-        c1 = lo1;
+        c1 = (uint32_t)p1;
         c2 = n2;
-        c3 = lo0;
+        c3 = (uint32_t)p0;
         k0 += 0x9E3779B9u;
         k1 += 0xBB67AE85u;
     }
@@ -63,10 +64,10 @@ __device__ __forceinline__ uint64_t keep_bits(uint64_t e_lo, uint64_t e_hi, uint
 }
 
 __global__ __launch_bounds__(256) void drop_attn_kernel(uint64_t* bits, int64_t words, int T, int Tw, uint32_t k0,
-                                                        uint32_t k1, uint32_t thr) {
+                                                        uint32_t k1, uint32_t thr, int layer0) {
     const int64_t w = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (w >= words) return;
-    const int layer = blockIdx.y;
+    const int layer = layer0 + (int)blockIdx.y;
     const int64_t row = w / Tw;  // (b H + h) T + i
     const int kw = (int)(w - row * Tw);
     const int i = (int)(row % T);
@@ -77,38 +78,38 @@ __global__ __launch_bounds__(256) void drop_attn_kernel(uint64_t* bits, int64_t 
         const int jend = min(64 * kw + 64, i + 1);
         out = keep_bits(e0, (uint64_t)row * T + jend, DROP_ATTN, (uint32_t)layer, k0, k1, thr);
     }
-    bits[(int64_t)layer * words + w] = out;
+    bits[(int64_t)blockIdx.y * words + w] = out;
 }
 
 __global__ __launch_bounds__(256) void drop_res_kernel(uint64_t* bits, int64_t words, int64_t n_elem, int site,
-                                                       uint32_t k0, uint32_t k1, uint32_t thr) {
+                                                       uint32_t k0, uint32_t k1, uint32_t thr, int layer0) {
     const int64_t w = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (w >= words) return;
-    const int layer = blockIdx.y;
+    const int layer = layer0 + (int)blockIdx.y;
     const uint64_t e0 = (uint64_t)w * 64;
     const uint64_t e1 = min(e0 + 64, (uint64_t)n_elem);
-    bits[(int64_t)layer * words + w] = keep_bits(e0, e1, (uint32_t)site, (uint32_t)layer, k0, k1, thr);
+    bits[(int64_t)blockIdx.y * words + w] = keep_bits(e0, e1, (uint32_t)site, (uint32_t)layer, k0, k1, thr);
 }
 
 }  // namespace
 
-hipError_t dropout_masks_attn(uint64_t* bits, int L, int64_t words_per_layer, int BH, int T, int Tw, uint64_t seed,
-                              uint32_t thr, hipStream_t s) {
+hipError_t dropout_masks_attn(uint64_t* bits, int layer0, int L, int64_t words_per_layer, int BH, int T, int Tw,
+                              uint64_t seed, uint32_t thr, hipStream_t s) {
     if (L <= 0 || words_per_layer <= 0) return hipSuccess;
     if (words_per_layer != (int64_t)BH * T * Tw || Tw != (T + 63) / 64) return hipErrorInvalidValue;
     const dim3 grid((unsigned)((words_per_layer + 255) / 256), (unsigned)L);
     hipLaunchKernelGGL(drop_attn_kernel, grid, dim3(256), 0, s, bits, words_per_layer, T, Tw, (uint32_t)seed,
-                       (uint32_t)(seed >> 32), thr);
+                       (uint32_t)(seed >> 32), thr, layer0);
     return hipGetLastError();
 }
 
-hipError_t dropout_masks_res(uint64_t* bits, int L, int64_t words_per_layer, int64_t n_elem, int site,
+hipError_t dropout_masks_res(uint64_t* bits, int layer0, int L, int64_t words_per_layer, int64_t n_elem, int site,
                              uint64_t seed, uint32_t thr, hipStream_t s) {
     if (L <= 0 || words_per_layer <= 0) return hipSuccess;
     if (words_per_layer != (n_elem + 63) / 64) return hipErrorInvalidValue;
     const dim3 grid((unsigned)((words_per_layer + 255) / 256), (unsigned)L);
     hipLaunchKernelGGL(drop_res_kernel, grid, dim3(256), 0, s, bits, words_per_layer, n_elem, site, (uint32_t)seed,
-                       (uint32_t)(seed >> 32), thr);
+                       (uint32_t)(seed >> 32), thr, layer0);
     return hipGetLastError();
 }
 

@@ -46,6 +46,11 @@ struct gpt2_ctx {
     // optional per-launch timing (gpt2_timing_begin/end)
     bool timing = false;
     uint64_t drop_seed = 0;  // key of the dropout masks (gpt2_set_dropout_seed)
+    // with a second stream the forward generates layer l's masks there and
+    // waits for dev[l] just before layer l first reads them; dfork orders that
+    // generation after the previous backward's last read of the masks
+    std::vector<hipEvent_t> dev;
+    hipEvent_t dfork = nullptr;
     std::string timing_prefix;
     std::vector<hipEvent_t> ev_pool;
     size_t ev_used = 0;
@@ -401,6 +406,14 @@ int gpt2_init(gpt2_ctx** out, const gpt2_config* cfg, const gpt2_buffers* bufs, 
             ok = hipEventCreateWithFlags(&e, hipEventDisableTiming) == hipSuccess;
             if (ok) x->wev.push_back(e);
         }
+        if (ok && x->cfg.dropout > 0.0f) {
+            ok = hipEventCreateWithFlags(&x->dfork, hipEventDisableTiming) == hipSuccess;
+            for (int i = 0; ok && i < x->cfg.n_layer; ++i) {
+                hipEvent_t e = nullptr;
+                ok = hipEventCreateWithFlags(&e, hipEventDisableTiming) == hipSuccess;
+                if (ok) x->dev.push_back(e);
+            }
+        }
         if (!ok) {
             gpt2_destroy(x);
             return GPT2_EHIP;
@@ -437,6 +450,8 @@ void gpt2_destroy(gpt2_ctx* x) {
     if (x->gstream) (void)hipStreamDestroy(x->gstream);
     for (hipEvent_t e : x->ev_pool) (void)hipEventDestroy(e);
     for (hipEvent_t e : x->wev) (void)hipEventDestroy(e);
+    for (hipEvent_t e : x->dev) (void)hipEventDestroy(e);
+    if (x->dfork) (void)hipEventDestroy(x->dfork);
     if (x->wstream) (void)hipStreamDestroy(x->wstream);
     delete x;
 }
@@ -460,15 +475,27 @@ int gpt2_forward(gpt2_ctx* x, const int32_t* d_idx, const int32_t* d_targets, fl
     }
     const bool drop = dropping(x);
     const float dsc = drop_scale(x);
+    // every layer's keep masks for this step (read again by the backward): on
+    // the second stream layer by layer, beside the forward's products, else
+    // here all at once
+    const bool dside = drop && !x->dev.empty();
     if (drop) {
-        // every layer's keep masks for this step, read again by the backward
         const uint32_t thr = drop_threshold(x);
-        G2_T("dropout.mask", dropout_masks_attn(at<uint64_t>(x, ap.dm_attn), c.n_layer, ap.dm_attn_words, ap.B * H, T,
-                                                ap.dm_tw, x->drop_seed, thr, s));
-        G2_T("dropout.mask", dropout_masks_res(at<uint64_t>(x, ap.dm_proj), c.n_layer, ap.dm_res_words,
-                                               (int64_t)M * C, DROP_PROJ, x->drop_seed, thr, s));
-        G2_T("dropout.mask", dropout_masks_res(at<uint64_t>(x, ap.dm_fc2), c.n_layer, ap.dm_res_words,
-                                               (int64_t)M * C, DROP_FC2, x->drop_seed, thr, s));
+        const int nl = dside ? 1 : c.n_layer;
+        hipStream_t ms = dside ? x->wstream : s;
+        if (dside) {
+            G2_TRY(hipEventRecord(x->dfork, s));
+            G2_TRY(hipStreamWaitEvent(ms, x->dfork, 0));
+        }
+        for (int l = 0; l < c.n_layer; l += nl) {
+            G2_TS("dropout.mask", ms, dropout_masks_attn(at<uint64_t>(x, ap.dm_attn) + (int64_t)l * ap.dm_attn_words, l, nl,
+                                                         ap.dm_attn_words, ap.B * H, T, ap.dm_tw, x->drop_seed, thr, ms));
+            G2_TS("dropout.mask", ms, dropout_masks_res(at<uint64_t>(x, ap.dm_proj) + (int64_t)l * ap.dm_res_words, l, nl,
+                                                        ap.dm_res_words, (int64_t)M * C, DROP_PROJ, x->drop_seed, thr, ms));
+            G2_TS("dropout.mask", ms, dropout_masks_res(at<uint64_t>(x, ap.dm_fc2) + (int64_t)l * ap.dm_res_words, l, nl,
+                                                        ap.dm_res_words, (int64_t)M * C, DROP_FC2, x->drop_seed, thr, ms));
+            if (dside) G2_TRY(hipEventRecord(x->dev[l], ms));
+        }
     }
     G2_T("embed.fwd", encoder_fwd(dt, d_idx, pf(x, x->pl.wte), nullptr, pf(x, x->pl.wpe), nullptr, at<float>(x, ap.x[0]), M, T, C,
                        c.vocab, status, s));
@@ -482,6 +509,7 @@ int gpt2_forward(gpt2_ctx* x, const int32_t* d_idx, const int32_t* d_targets, fl
                              at<float>(x, ap.m1[sl]), at<float>(x, ap.r1[sl]), M, C, s));
         G2_T("gemm.fwd.qkv", linear_fwd(x, EPI_STORE, M, 3 * C, C, at<char>(x, ap.ln1[sl]), wptr(x, w.w_qkv), pf(x, w.b_qkv),
                           at<char>(x, ap.qkv[sl]), nullptr, nullptr));
+        if (dside) G2_TRY(hipStreamWaitEvent(s, x->dev[l], 0));  // this layer's masks
         G2_T("attn.fwd", attention_fwd(dt, ap.B, T, C, H, at<char>(x, ap.qkv[sl]), at<char>(x, ap.att[sl]),
                              at<float>(x, ap.lse[sl]), s, dm_attn(x, l), dsc));
         G2_T("gemm.fwd.proj", linear_fwd(x, EPI_RESID, M, C, C, at<char>(x, ap.att[sl]), wptr(x, w.w_proj), pf(x, w.b_proj), xmid,
