@@ -218,3 +218,46 @@ def test_dropout_eval_seed_and_determinism(b):
     plain = gpu_model(b, base, "bf16", B, T, named)
     with pytest.raises(b.GPT2Error):
         plain.set_dropout_seed(1)               # no dropout configured
+
+
+def test_dropout_accumulation_two_seeds(b, oracle):
+    """Gradient accumulation with dropout: two micro-batches at scale 1/2, each
+    with its own seed, the second added to the first (zero_grads = 0), equal
+    the mean of the oracle's gradients under those two seeds."""
+    m = with_dropout(syn.WORKLOADS["tiny_f32"].model)
+    B, T = 2, 64
+    say("dropout accumulation tiny_f32")
+    named = syn.init_params(m)
+    w = syn.WORKLOADS["tiny_f32"]
+    xs = [syn.batch(w, step=k, B=B, T=T) for k in (0, 1)]
+    g = gpu_model(b, m, "f32", B, T, named)
+    for k, (x, y) in enumerate(xs):
+        g.set_dropout_seed(77 + k)
+        g.forward(dev_tokens(x), dev_tokens(y))
+        g.backward(0.5, k == 0)
+    ref = None
+    for k, (x, y) in enumerate(xs):
+        _, rg = oracle_grads(oracle, m, named, x, y, loss_scale=0.5, seed=77 + k)
+        ref = rg if ref is None else {n: ref[n] + rg[n] for n in ref}
+    gg = gpu_named_grads(g)
+    for n, r in ref.items():
+        assert max_rel(gg[n], r) <= 1e-3, (n, max_rel(gg[n], r))
+
+
+@pytest.mark.parametrize("p", [0.5])
+def test_dropout_bf16_scalar_attention_and_large_p(b, oracle, p):
+    """bf16 with head size 32 (the scalar attention kernels, which take bf16
+    operands too) at p = 0.5: loss and every gradient at the bf16 tolerances."""
+    m = syn.Model(65, 64, 128, 4, 2, 512, True, dropout=p)
+    B, T = 3, 64
+    say(f"dropout bf16 head size 32 p={p}")
+    named = syn.init_params(m)
+    x, y = syn.batch(syn.WORKLOADS["tiny_f32"], B=B, T=T)
+    g = gpu_model(b, m, "bf16", B, T, named)
+    loss = step(g, x, y, SEED)
+    rloss, rg = oracle_grads(oracle, m, named, x, y, dtype=np.float32, seed=SEED)
+    assert abs(loss - rloss) <= 2e-2, (loss, rloss)
+    gg = gpu_named_grads(g)
+    for k, r in rg.items():
+        assert cosine(gg[k], r) >= 0.999, (k, cosine(gg[k], r))
+    assert g.sync_status() == 0
