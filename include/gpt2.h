@@ -241,7 +241,8 @@ int gpt2_clear_status(gpt2_ctx* ctx);
  * fc,fc2,head}", "attn.fwd", "ce", "loss", "gemm.dgrad.{head,fc2,fc,proj,qkv}",
  * "gemm.wgrad.{head,fc2,fc,proj,qkv}", "ln.bwd", "colsum", "bias",
  * "attn.bwd.{dq,dkdv}" (bf16, head size 64; "attn.bwd" otherwise), "embed.bwd",
- * "gradnorm", "adamw". A prefix also times the labels that extend it by a
+ * "gradnorm", "adamw", "dropout.mask" (with dropout; on the second stream when
+ * there is one, so its events overlap the forward's). A prefix also times the labels that extend it by a
  * '.'-separated part ("attn.bwd" covers both backward launches); an empty
  * prefix times every launch. */
 int gpt2_timing_begin(gpt2_ctx* ctx, const char* prefix);
