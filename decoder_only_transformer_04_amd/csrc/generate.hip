@@ -45,6 +45,16 @@ __global__ void gen_embed_kernel(const int32_t* seq, int64_t seq_ld, const int32
 
 constexpr int kAttThreads = 256;
 
+// one 16-byte piece of an activation row as floats (8 bf16 or 4 fp32)
+__device__ __forceinline__ void load16f(const bf16_t* p, float (&o)[8]) { unpack8f(*(const uint4*)p, o); }
+__device__ __forceinline__ void load16f(const float* p, float (&o)[4]) {
+    const float4 v = *(const float4*)p;
+    o[0] = v.x;
+    o[1] = v.y;
+    o[2] = v.z;
+    o[3] = v.w;
+}
+
 // One workgroup per (sequence b, head h); d = C / H <= 128, pos < Tc <= kGenMaxCache.
 // Scores go to LDS (one float per cached position), then max, exponentials and
 // their sum; the output sums p_j v_j with each thread owning one dimension of
@@ -72,37 +82,51 @@ __global__ __launch_bounds__(kAttThreads) void gen_attn_kernel(const T* qkv, T* 
         vb[(int64_t)pos * C + c] = row[2 * C + h * d + c];
     }
     __syncthreads();  // the appended k and v are visible to the whole workgroup
-    // scores of the positions j <= pos (causal: the new query sees the window so far)
+    // scores of the positions j <= pos (causal: the new query sees the window so far);
+    // a key row is read as 16-byte pieces when the head's columns allow it
+    constexpr int E = 16 / sizeof(T);
+    const bool vec = d % E == 0 && ((h * d) % E) == 0 && C % E == 0;
     float mx = -FLT_MAX;
     for (int j = tid; j <= pos; j += kAttThreads) {
         const T* kr = kb + (int64_t)j * C;
         float s = 0.0f;
-        for (int c = 0; c < d; ++c) s = fmaf(q[c], Act<T>::ld(kr, c), s);
+        if (vec) {
+            for (int c0 = 0; c0 < d; c0 += E) {
+                float kv[E];
+                load16f(kr + c0, kv);
+#pragma unroll
+                for (int e = 0; e < E; ++e) s = fmaf(q[c0 + e], kv[e], s);
+            }
+        } else {
+            for (int c = 0; c < d; ++c) s = fmaf(q[c], Act<T>::ld(kr, c), s);
+        }
         s *= scale;
         sc[j] = s;
         mx = fmaxf(mx, s);
     }
-    red[tid] = mx;
+    // block maximum and sum: a wave reduction, then the four wave results
+    constexpr int NWV = kAttThreads / 64;
+    const int lane = tid & 63, wv = tid >> 6;
+    mx = wave_max(mx);
+    if (lane == 0) red[wv] = mx;
     __syncthreads();
-    for (int w = kAttThreads / 2; w > 0; w >>= 1) {
-        if (tid < w) red[tid] = fmaxf(red[tid], red[tid + w]);
-        __syncthreads();
-    }
     mx = red[0];
-    __syncthreads();
+#pragma unroll
+    for (int k = 1; k < NWV; ++k) mx = fmaxf(mx, red[k]);
     float sum = 0.0f;
     for (int j = tid; j <= pos; j += kAttThreads) {
         const float e = __expf(sc[j] - mx);
         sc[j] = e;
         sum += e;
     }
-    red[tid] = sum;
+    sum = wave_sum(sum);
+    __syncthreads();  // every wave has read the maxima before they are overwritten
+    if (lane == 0) red[wv] = sum;
     __syncthreads();
-    for (int w = kAttThreads / 2; w > 0; w >>= 1) {
-        if (tid < w) red[tid] += red[tid + w];
-        __syncthreads();
-    }
-    const float inv = 1.0f / red[0];
+    float tot = red[0];
+#pragma unroll
+    for (int k = 1; k < NWV; ++k) tot += red[k];
+    const float inv = 1.0f / tot;
     // out[c] = sum_j p_j v_j[c]: slice `sl` of the positions (j = sl, sl + ns, ...)
     const int ns = kAttThreads / d;  // d <= 128, so ns >= 2
     const int c = tid % d, sl = tid / d;
