@@ -144,6 +144,7 @@ def test_init_rejects_null_and_small_arena(b):
     assert b.lib().gpt2_init(ct.byref(ctx), ct.byref(cfg), ct.byref(bufs), 4, 64, 0, None) == b.GPT2_EINVAL
     assert b.lib().gpt2_forward(None, None, None, None, None) == b.GPT2_EINVAL
     assert b.lib().gpt2_backward(None, 1.0, 1) == b.GPT2_EINVAL
+    assert b.lib().gpt2_set_dropout_seed(None, 1) == b.GPT2_EINVAL
 
 
 def test_strerror(b):
